@@ -1,0 +1,373 @@
+"""Seeded step generator.
+
+A step is a list of requests, each with a context already in the cache
+(``prior`` tokens), ``n`` tokens scheduled this step, and a block table.  The
+flat metadata follows the definitions in "Model execution", section
+"Flattening a step": query_start_loc are cumulative token counts, seq_lens are
+prior + n, and each new token's slot is ``table[pos // 16] * 16 + pos % 16``.
+
+Values are N(0,1) draws from a seeded ``torch.Generator`` on the device the
+step is built on, rounded once to the step's dtype.  Prior-context K/V are
+written straight into the pools; slots of the new tokens, the tail of each
+last block and all unreferenced blocks are filled with ``fill`` (NaN for
+correctness runs, so that a value that should never be read shows up).
+
+Draw order (fixed): numpy ``default_rng(seed)`` for shapes and placement
+(config-specific, see ``config_step``), then torch draws in the order query,
+key, value, K pool, V pool.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field, replace
+
+import numpy as np
+import torch
+
+BLOCK = 16
+
+CONFIG_NAMES = {
+    1: "tiny mixed step, fp32 (Hq 4 / Hkv 2, d 64; prefill 37 + decodes at 5, 17, 64)",
+    2: "long-context single decode, bf16 (1 x 32768, Hq 32 / Hkv 8, d 128)",
+    3: "large-batch decode, bf16 (256 x U[512, 8192], Hq 32 / Hkv 8, d 128)",
+    4: "long prefill, bf16 (4 x 8192 new tokens, Hq 32 / Hkv 8, d 128)",
+    5: "mixed chunked-prefill step, bf16 (2 x 2048 chunks + 4096 decodes, 25% shared 1024-token prefix)",
+}
+
+
+@dataclass
+class Request:
+    prior: int              # tokens already in the cache
+    n: int                  # tokens scheduled this step
+    table: list             # physical block ids covering prior + n tokens
+
+
+@dataclass
+class StepInputs:
+    name: str
+    dtype: str                      # "bf16" or "f32"
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    scale: float
+    num_blocks: int
+    query_start_loc: np.ndarray     # int32 [B+1]
+    seq_lens: np.ndarray            # int32 [B]
+    block_tables: np.ndarray        # int32 [B, stride], -1 past the context
+    slot_mapping: np.ndarray        # int64 [Nt]
+    query: torch.Tensor = None      # [Nt, Hq, d]
+    key: torch.Tensor = None        # [Nt, Hkv, d]
+    value: torch.Tensor = None      # [Nt, Hkv, d]
+    k_pool: torch.Tensor = None     # [NB, Hkv, 16, d] before the write
+    v_pool: torch.Tensor = None     # [NB, Hkv, d, 16] before the write
+    info: dict = field(default_factory=dict)
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.seq_lens.shape[0])
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.slot_mapping.shape[0])
+
+    @property
+    def q_lens(self) -> np.ndarray:
+        return np.diff(self.query_start_loc.astype(np.int64))
+
+    @property
+    def max_query_len(self) -> int:
+        return int(self.q_lens.max()) if self.num_seqs else 0
+
+    @property
+    def max_seq_len(self) -> int:
+        return int(self.seq_lens.max()) if self.num_seqs else 0
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+
+def raw_numpy(t: torch.Tensor) -> np.ndarray:
+    """Host numpy view of a tensor: bf16 as its uint16 bit pattern."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def unique_block_count(step: StepInputs) -> int:
+    """Number of distinct physical blocks the step's requests reference."""
+    ids = []
+    for b in range(step.num_seqs):
+        nb = -(-int(step.seq_lens[b]) // step.block_size)
+        ids.append(step.block_tables[b, :nb])
+    if not ids:
+        return 0
+    return int(np.unique(np.concatenate(ids)).size)
+
+
+def build_step(name, requests, *, dtype, num_q_heads, num_kv_heads, head_dim,
+               num_blocks, seed, device="cpu", fill="nan", stride=None,
+               scale=None, pad_tokens=0, order=None, info=None,
+               with_values=True) -> StepInputs:
+    """Flatten ``requests`` (in ``order`` if given) and draw the step's values."""
+    if order is not None:
+        requests = [requests[i] for i in order]
+    B = len(requests)
+    counts = [r.n for r in requests]
+    qsl = np.zeros(B + 1, dtype=np.int32)
+    qsl[1:] = np.cumsum(counts, dtype=np.int64)
+    seq_lens = np.array([r.prior + r.n for r in requests], dtype=np.int32)
+    need = [-(-(r.prior + r.n) // BLOCK) for r in requests]
+    if stride is None:
+        stride = max(need) if need else 1
+    tables = np.full((B, max(stride, 1)), -1, dtype=np.int32)
+    for b, r in enumerate(requests):
+        assert len(r.table) >= need[b]
+        tables[b, : need[b]] = r.table[: need[b]]
+    nt = int(qsl[-1]) + pad_tokens
+    slots = np.full(nt, -1, dtype=np.int64)
+    t = 0
+    for r in requests:
+        tab = np.asarray(r.table, dtype=np.int64)
+        pos = np.arange(r.prior, r.prior + r.n, dtype=np.int64)
+        slots[t: t + r.n] = tab[pos // BLOCK] * BLOCK + pos % BLOCK
+        t += r.n
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    step = StepInputs(name=name, dtype=dtype, num_q_heads=num_q_heads,
+                      num_kv_heads=num_kv_heads, head_dim=head_dim,
+                      block_size=BLOCK, scale=float(scale), num_blocks=num_blocks,
+                      query_start_loc=qsl, seq_lens=seq_lens, block_tables=tables,
+                      slot_mapping=slots, info=dict(info or {}))
+    if with_values:
+        _draw_values(step, requests, seed, device, fill)
+    return step
+
+
+def _prior_slot_mask(step: StepInputs, requests, device) -> torch.Tensor:
+    """Boolean [num_blocks * 16]: True where a prior-context token lives."""
+    chunks = []
+    for r in requests:
+        if r.prior == 0:
+            continue
+        tab = torch.as_tensor(np.asarray(r.table, dtype=np.int64))
+        pos = torch.arange(r.prior, dtype=torch.int64)
+        chunks.append(tab[pos // BLOCK] * BLOCK + pos % BLOCK)
+    mask = torch.zeros(step.num_blocks * BLOCK, dtype=torch.bool, device=device)
+    if chunks:
+        mask[torch.cat(chunks).to(device)] = True
+    return mask
+
+
+def _draw_values(step: StepInputs, requests, seed, device, fill) -> None:
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    dt = step.torch_dtype
+    Nt, Hq, Hkv, d = step.num_tokens, step.num_q_heads, step.num_kv_heads, step.head_dim
+    NB = step.num_blocks
+
+    def randn(*shape):
+        # draw in fp32 and round once (RNE) to the step dtype
+        if dt == torch.float32:
+            return torch.randn(*shape, generator=g, device=device, dtype=torch.float32)
+        out = torch.empty(*shape, device=device, dtype=dt)
+        flat = out.view(-1)
+        chunk = 1 << 28
+        for s in range(0, flat.numel(), chunk):
+            e = min(s + chunk, flat.numel())
+            flat[s:e] = torch.randn(e - s, generator=g, device=device,
+                                    dtype=torch.float32).to(dt)
+        return out
+
+    step.query = randn(Nt, Hq, d)
+    step.key = randn(Nt, Hkv, d)
+    step.value = randn(Nt, Hkv, d)
+    step.k_pool = randn(NB, Hkv, BLOCK, d)
+    step.v_pool = randn(NB, Hkv, d, BLOCK)
+    live = _prior_slot_mask(step, requests, device).view(NB, BLOCK)
+    dead = ~live
+    fv = float("nan") if fill == "nan" else 0.0
+    step.k_pool.masked_fill_(dead.view(NB, 1, BLOCK, 1), fv)
+    step.v_pool.masked_fill_(dead.view(NB, 1, 1, BLOCK), fv)
+    # padded tokens (slot < 0) carry poison too: they must never be read
+    pad = torch.as_tensor(step.slot_mapping < 0).to(device)
+    if bool(pad.any()):
+        step.query[pad] = fv
+        step.key[pad] = fv
+        step.value[pad] = fv
+
+
+# ----------------------------------------------------------------------------
+# the five workloads
+# ----------------------------------------------------------------------------
+
+def _assign_tables(rng_perm, need_list, shared=None):
+    """Hand out physical blocks from a permutation, request by request."""
+    tables, k = [], 0
+    for i, nb in enumerate(need_list):
+        if shared is not None and shared[i] is not None:
+            pre = list(shared[i])
+            rest = nb - len(pre)
+            tables.append(pre + list(rng_perm[k: k + rest]))
+            k += rest
+        else:
+            tables.append(list(rng_perm[k: k + nb]))
+            k += nb
+    return tables, k
+
+
+def config_step(cfg: int, *, device="cpu", fill="nan", variant=None,
+                scale_down=None, with_values=True) -> StepInputs:
+    """Build workload ``cfg`` (1..5) with seed = cfg.
+
+    ``variant="alt"`` for config 1 reads the decode contexts as prior tokens
+    (seq_lens 6, 18, 65) instead of totals (5, 17, 64).  ``scale_down`` gives
+    smaller versions of configs 3-5 with the same structure, for tests the CPU
+    oracle finishes in seconds: a dict of overrides (see below).
+    """
+    seed = cfg
+    rng = np.random.default_rng(seed)
+    sd = dict(scale_down or {})
+    if cfg == 1:
+        dec = [6, 18, 65] if variant == "alt" else [5, 17, 64]
+        shapes = [(0, 37)] + [(s - 1, 1) for s in dec]
+        need = [-(-(p + n) // BLOCK) for p, n in shapes]
+        perm = rng.permutation(32)
+        tables, _ = _assign_tables(perm, need)
+        reqs = [Request(p, n, t) for (p, n), t in zip(shapes, tables)]
+        return build_step(f"config1{'-alt' if variant == 'alt' else ''}", reqs,
+                          dtype="f32", num_q_heads=4, num_kv_heads=2, head_dim=64,
+                          num_blocks=32, seed=seed, device=device, fill=fill,
+                          scale=1.0 / math.sqrt(64), with_values=with_values)
+    if cfg == 2:
+        ctx = sd.get("context", 32768)
+        pool = sd.get("pool_blocks", 4096)
+        need = -(-ctx // BLOCK)
+        table = list(rng.permutation(pool)[:need])
+        reqs = [Request(ctx - 1, 1, table)]
+        return build_step("config2", reqs, dtype="bf16", num_q_heads=32,
+                          num_kv_heads=8, head_dim=128, num_blocks=pool, seed=seed,
+                          device=device, fill=fill, stride=need,
+                          with_values=with_values)
+    if cfg == 3:
+        B = sd.get("batch", 256)
+        lo, hi = sd.get("lo", 512), sd.get("hi", 8192)
+        ctx = rng.integers(lo, hi + 1, size=B)
+        need = [-(-int(c) // BLOCK) for c in ctx]
+        total = int(sum(need))
+        pool = 2 * total
+        perm = rng.permutation(pool)
+        tables, _ = _assign_tables(perm, need)
+        reqs = [Request(int(c) - 1, 1, t) for c, t in zip(ctx, tables)]
+        return build_step("config3", reqs, dtype="bf16", num_q_heads=32,
+                          num_kv_heads=8, head_dim=128, num_blocks=pool, seed=seed,
+                          device=device, fill=fill, stride=-(-hi // BLOCK),
+                          with_values=with_values)
+    if cfg == 4:
+        B = sd.get("batch", 4)
+        n = sd.get("new", 8192)
+        pool = sd.get("pool_blocks", 4096)
+        need = [-(-n // BLOCK)] * B
+        perm = rng.permutation(pool)
+        tables, _ = _assign_tables(perm, need)
+        reqs = [Request(0, n, t) for t in tables]
+        return build_step("config4", reqs, dtype="bf16", num_q_heads=32,
+                          num_kv_heads=8, head_dim=128, num_blocks=pool, seed=seed,
+                          device=device, fill=fill, stride=need[0],
+                          with_values=with_values)
+    if cfg == 5:
+        chunk = sd.get("chunk", 2048)
+        priors = sd.get("priors", (4096, 16384))
+        ndec = sd.get("decodes", 4096)
+        lo, hi = sd.get("lo", 128), sd.get("hi", 16384)
+        prefix = sd.get("prefix", 1024)
+        nshare = sd.get("sharers", ndec // 4)
+        stride = sd.get("stride", 1152)
+        # contexts: log-uniform on [lo, hi], floored and clipped
+        u = rng.uniform(math.log(lo), math.log(hi + 1), size=ndec)
+        ctx = np.clip(np.floor(np.exp(u)).astype(np.int64), lo, hi)
+        eligible = np.nonzero(ctx >= prefix + 1)[0]
+        sharers = set(rng.choice(eligible, size=min(nshare, eligible.size),
+                                 replace=False).tolist())
+        shapes = [(p, chunk) for p in priors] + [(int(c) - 1, 1) for c in ctx]
+        need = [-(-(p + n) // BLOCK) for p, n in shapes]
+        pre_blocks = prefix // BLOCK
+        unique = pre_blocks + sum(
+            need[i] - (pre_blocks if (i - len(priors)) in sharers else 0)
+            for i in range(len(shapes)))
+        pool = int(math.ceil(1.25 * unique))
+        perm = rng.permutation(pool)
+        shared_ids = list(perm[:pre_blocks])
+        shared = [None] * len(priors) + [
+            shared_ids if j in sharers else None for j in range(ndec)]
+        tables, _ = _assign_tables(perm[pre_blocks:], need, shared)
+        reqs = [Request(p, n, t) for (p, n), t in zip(shapes, tables)]
+        order = rng.permutation(len(reqs))
+        info = {"shared_blocks": shared_ids, "num_sharers": len(sharers),
+                "unique_blocks": unique}
+        return build_step("config5", reqs, dtype="bf16", num_q_heads=32,
+                          num_kv_heads=8, head_dim=128, num_blocks=pool, seed=seed,
+                          device=device, fill=fill, stride=stride, order=order,
+                          info=info, with_values=with_values)
+    raise ValueError(f"no config {cfg}")
+
+
+def extract_requests(step: StepInputs, req_ids, device="cpu") -> tuple:
+    """A small step holding only the requests ``req_ids`` of ``step``.
+
+    The referenced blocks are copied into a compact pool (renumbered in order
+    of first use) and the metadata is rebuilt for those requests' rows only.
+    Returns (small_step, token_index) where ``token_index[k]`` is the flat row
+    of ``step`` that row k of the small step came from.  Values are the same
+    bits as in ``step`` (pre-write pools, queries and new K/V).
+    """
+    req_ids = list(req_ids)
+    qsl = step.query_start_loc.astype(np.int64)
+    blocks, remap = [], {}
+    tables, rows = [], []
+    for b in req_ids:
+        nb = -(-int(step.seq_lens[b]) // step.block_size)
+        tab = []
+        for pb in step.block_tables[b, :nb]:
+            pb = int(pb)
+            if pb not in remap:
+                remap[pb] = len(blocks)
+                blocks.append(pb)
+            tab.append(remap[pb])
+        tables.append(tab)
+        rows.extend(range(int(qsl[b]), int(qsl[b + 1])))
+    B = len(req_ids)
+    stride = max(len(t) for t in tables) if tables else 1
+    bt = np.full((B, stride), -1, dtype=np.int32)
+    for i, t in enumerate(tables):
+        bt[i, : len(t)] = t
+    q_lens = [int(qsl[b + 1] - qsl[b]) for b in req_ids]
+    new_qsl = np.zeros(B + 1, dtype=np.int32)
+    new_qsl[1:] = np.cumsum(q_lens)
+    seq_lens = step.seq_lens[req_ids].astype(np.int32)
+    # rebuild slots from the renumbered tables (positions are unchanged)
+    slots = np.empty(len(rows), dtype=np.int64)
+    k = 0
+    for i, b in enumerate(req_ids):
+        ctx = int(step.seq_lens[b]) - q_lens[i]
+        for j in range(q_lens[i]):
+            p = ctx + j
+            slots[k] = bt[i, p // BLOCK] * BLOCK + p % BLOCK
+            k += 1
+    idx_blocks = torch.as_tensor(np.asarray(blocks, dtype=np.int64))
+    idx_rows = torch.as_tensor(np.asarray(rows, dtype=np.int64))
+    src_dev = step.k_pool.device
+    small = replace(
+        step, name=step.name + "-extract", num_blocks=len(blocks),
+        query_start_loc=new_qsl, seq_lens=seq_lens, block_tables=bt,
+        slot_mapping=slots,
+        query=step.query[idx_rows.to(src_dev)].to(device),
+        key=step.key[idx_rows.to(src_dev)].to(device),
+        value=step.value[idx_rows.to(src_dev)].to(device),
+        k_pool=step.k_pool[idx_blocks.to(src_dev)].to(device),
+        v_pool=step.v_pool[idx_blocks.to(src_dev)].to(device),
+        info=dict(step.info))
+    return small, np.asarray(rows, dtype=np.int64)
