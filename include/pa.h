@@ -1,0 +1,219 @@
+/*
+ * pa.h -- C ABI of the paged-attention library for one flat engine step
+ * (MI355X / gfx950).
+ *
+ * What a step is ("Model execution", section "Flattening a step"): all tokens
+ * scheduled in the step are concatenated into one flat batch.  Attention gets
+ * per-request offsets (query_start_loc), total context lengths (seq_lens) and
+ * block tables; the KV write gets a slot mapping, slot = block_id * block_size
+ * + offset.  The arithmetic is exact attention computed FlashAttention-style
+ * ("Inside the engine: kernels, CUDA graphs and the life of a request",
+ * sections "Never materialise the T x T matrix", "Prefill has a full grid;
+ * decode at batch 1 has almost none" and "Attention over a block table, not
+ * a contiguous tensor").
+ *
+ * Conventions common to every entry point
+ * ---------------------------------------
+ * - Every tensor argument is a DEVICE pointer owned by the caller.  The
+ *   library allocates and frees no device memory and keeps no per-call state.
+ * - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *   stream) and never synchronises or reads device memory on the host: grid
+ *   sizes come only from the host scalars passed in.
+ * - Scalars and pointers are validated on the host before anything is
+ *   enqueued; a non-OK status means nothing was launched.  A launch failure
+ *   is reported as PA_ERR_HIP.  No call aborts or throws.
+ * - Data-dependent faults are NOT checked on the fast path (that would need a
+ *   device-to-host read): block ids outside [0, num_blocks), duplicate slots,
+ *   seq_len < q_len, a non-monotone query_start_loc, or q_len / seq_len above
+ *   the max_query_len / max_seq_len passed in give undefined results.
+ * - Identical inputs and num_splits give bitwise-identical outputs (no atomics
+ *   in any reduction; reduction order depends only on logical positions).
+ *
+ * Layouts (row-major, innermost last; d = head_dim, bs = block_size = 16):
+ *   query        [num_tokens][num_q_heads][d]
+ *   key, value   [num_tokens][num_kv_heads][d]           (the step's new tokens)
+ *   key_cache    [num_blocks][num_kv_heads][bs][d]        (token-major block)
+ *   value_cache  [num_blocks][num_kv_heads][d][bs]        (dim-major block)
+ *   out          [num_tokens][num_q_heads][d]
+ *   lse          [num_tokens][num_q_heads]   float32, natural log
+ *   query_start_loc [num_seqs + 1] int32, seq_lens [num_seqs] int32,
+ *   block_tables [num_seqs][block_table_stride] int32,
+ *   slot_mapping [num_tokens] int64.
+ * The value block is stored dim-major so that the P*V product reads 8
+ * consecutive keys of one dimension as a single matrix-core operand.
+ *
+ * Grouped-query attention: query head h reads KV head h / (num_q_heads /
+ * num_kv_heads).  Causality with prior context: row i of request b sits at
+ * position p = seq_lens[b] - q_len_b + i and attends to positions 0..p.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,        /* a required pointer is NULL                        */
+  PA_ERR_INVALID = 2,     /* a scalar is out of range or inconsistent          */
+  PA_ERR_UNSUPPORTED = 3, /* valid, but outside what the kernels implement      */
+  PA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required        */
+  PA_ERR_HIP = 5          /* the HIP runtime reported an error on launch       */
+} pa_status;
+
+typedef enum pa_dtype {
+  PA_F32 = 0,             /* float32 activations and cache                     */
+  PA_BF16 = 1             /* bfloat16 activations and cache (fp32 accumulate)  */
+} pa_dtype;
+
+#define PA_BLOCK_SIZE 16
+#define PA_MAX_SPLITS 256
+
+/*
+ * pa_kv_write -- scatter the step's new K and V into the paged cache.
+ * ("Model execution", section "Flattening a step": the KV write uses the
+ * slot mapping, slot = block_id * block_size + offset.)
+ *
+ * For every t < num_tokens with s = slot_mapping[t] >= 0, and every KV head h:
+ *   key_cache  [s / bs][h][s % bs][:] = key  [t][h][:]
+ *   value_cache[s / bs][h][:][s % bs] = value[t][h][:]
+ * A negative slot marks a padded token: nothing is written for it.  The copy
+ * is bit-exact (cache dtype = input dtype, nothing converts) and no other
+ * cache entry changes.  Slots must be distinct and < num_blocks * bs
+ * (unchecked).
+ *
+ * Supported: head_dim in {64, 128}, block_size == 16, num_kv_heads >= 1.
+ * num_tokens == 0 is a no-op (pointers may then be NULL).
+ */
+pa_status pa_kv_write(const void* key, const void* value,
+                      void* key_cache, void* value_cache,
+                      const int64_t* slot_mapping,
+                      int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, int64_t num_blocks,
+                      pa_dtype dtype, void* stream);
+
+/*
+ * pa_attention_fwd -- causal attention of every scheduled row of the flat
+ * batch through the block tables ("Inside the engine ...", sections "Never
+ * materialise the T x T matrix" and "Attention over a block table, not a
+ * contiguous tensor"; metadata as in "Model execution", "Flattening a step").
+ *
+ * For request b, q_len_b = query_start_loc[b+1] - query_start_loc[b] rows at
+ * flat indices query_start_loc[b] ..; row i has position
+ * p = seq_lens[b] - q_len_b + i and, for every query head h,
+ *   out[t][h] = softmax(scale * q[t][h] . K[0..p]) V[0..p]
+ *   lse[t][h] = ln sum_j exp(scale * q[t][h] . K[j])          (if lse != NULL)
+ * where K[j], V[j] are read from block block_tables[b][j / 16], offset j % 16,
+ * KV head h / (num_q_heads / num_kv_heads).  Rows at or after
+ * query_start_loc[num_seqs] are not written.  The cache must already hold the
+ * step's new tokens (call pa_kv_write first on the same stream).
+ *
+ * Execution: rows of requests with few new tokens (decode) run a
+ * bandwidth-bound kernel; with num_splits > 1 their key range is cut into
+ * num_splits block ranges whose partial results are merged by a second
+ * reduction (the split-KV method of "Prefill has a full grid; decode at batch
+ * 1 has almost none").  Rows of requests with many new tokens run the tiled
+ * matrix-core kernel.  num_splits: 0 = pa_choose_num_splits() for these
+ * scalars, 1 = no split, 2..PA_MAX_SPLITS = forced.  The result does not
+ * depend on num_splits beyond rounding.
+ *
+ * max_query_len / max_seq_len: host-known upper bounds of q_len_b / seq_lens
+ * (they size the grids).  block_table_stride >= ceil(max_seq_len / 16); table
+ * entries past a request's last block are never read.
+ *
+ * workspace: device scratch of at least pa_attention_workspace_size(num_seqs,
+ * num_tokens, num_q_heads, head_dim, S) bytes, S the split count in use
+ * (resolve num_splits = 0 with pa_choose_num_splits first).  It may be NULL
+ * when that size is 0.  Its contents on entry do not matter.
+ *
+ * Supported: dtype PA_BF16 or PA_F32, head_dim in {64, 128}, block_size 16,
+ * num_q_heads % num_kv_heads == 0 with group size in {1, 2, 4, 8, 16}.
+ */
+pa_status pa_attention_fwd(const void* query,
+                           const void* key_cache, const void* value_cache,
+                           const int32_t* query_start_loc,
+                           const int32_t* seq_lens,
+                           const int32_t* block_tables,
+                           int32_t num_seqs, int32_t num_tokens,
+                           int32_t max_query_len, int32_t max_seq_len,
+                           int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size,
+                           int32_t block_table_stride, int64_t num_blocks,
+                           float scale, int32_t num_splits,
+                           void* out, float* lse,
+                           void* workspace, size_t workspace_bytes,
+                           pa_dtype dtype, void* stream);
+
+/*
+ * pa_split_combine -- merge split-KV partials ("Prefill has a full grid;
+ * decode at batch 1 has almost none": the partials are combined in a second
+ * reduction kernel).
+ *
+ * partial_out [num_splits][num_tokens][num_q_heads][head_dim] float32 holds
+ * each split's normalised output o_s, partial_lse [num_splits][num_tokens]
+ * [num_q_heads] float32 its natural-log sum-exp (-inf for a split that saw no
+ * key; its o_s is ignored).  With M = max_s lse_s:
+ *   lse = M + ln sum_s exp(lse_s - M),   out = sum_s exp(lse_s - lse) o_s
+ * written as `dtype` (bf16 rounds to nearest even once).  An entry whose
+ * splits are all -inf gets out = NaN and lse = -inf.  lse may be NULL.
+ * Supported: 1 <= num_splits <= PA_MAX_SPLITS, head_dim in {64, 128}.
+ */
+pa_status pa_split_combine(const float* partial_out, const float* partial_lse,
+                           int32_t num_splits, int32_t num_tokens,
+                           int32_t num_q_heads, int32_t head_dim,
+                           void* out, float* lse, pa_dtype dtype, void* stream);
+
+/*
+ * pa_attention_workspace_size -- bytes of workspace pa_attention_fwd needs for
+ * this batch shape at `num_splits` splits (num_splits >= 1; the split
+ * partials, plus a small work list for the matrix-core kernel).
+ */
+size_t pa_attention_workspace_size(int32_t num_seqs, int32_t num_tokens,
+                                   int32_t num_q_heads, int32_t head_dim,
+                                   int32_t num_splits);
+
+/*
+ * pa_choose_num_splits -- the split / no-split crossover ("Prefill has a full
+ * grid; decode at batch 1 has almost none": the split pays at low batch and
+ * is disabled once the query rows fill the grid).  Returns 1 when any request
+ * may have more new tokens than the decode kernel packs (max_query_len above
+ * 16 / group size) or when num_seqs * num_kv_heads work units already fill
+ * the device; otherwise enough splits to give every compute unit work,
+ * bounded by PA_MAX_SPLITS and by the number of 16-token blocks.  num_cus <= 0
+ * means "ask the current device".  Performance only: results do not depend on
+ * it.
+ */
+int32_t pa_choose_num_splits(int32_t num_seqs, int32_t max_query_len,
+                             int32_t max_seq_len, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t num_cus);
+
+/* pa_status_string -- static text for a status code (never NULL). */
+const char* pa_status_string(pa_status status);
+
+/* pa_version -- library version, major * 10000 + minor * 100 + patch. */
+int32_t pa_version(void);
+
+/*
+ * Kernel tracing (measurement aid).  pa_trace_begin(capacity) makes every
+ * later launch inside this library record a pair of HIP events around itself
+ * on its stream, for up to `capacity` launches; it creates the events (host
+ * call, may allocate).  pa_trace_end() stops recording.  After the caller has
+ * synchronised the streams, pa_trace_read() fills kernel_ids[i] and
+ * milliseconds[i] for the recorded launches (at most `capacity` entries) and
+ * returns their number (-1 on error).  pa_kernel_name() names a kernel id.
+ * Tracing is process-wide and not thread-safe against concurrent launches.
+ */
+pa_status   pa_trace_begin(int32_t capacity);
+pa_status   pa_trace_end(void);
+int32_t     pa_trace_read(int32_t* kernel_ids, float* milliseconds, int32_t capacity);
+const char* pa_kernel_name(int32_t kernel_id);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

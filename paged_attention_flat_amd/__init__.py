@@ -1,0 +1,188 @@
+"""Paged attention for one flat engine step on MI355X (gfx950).
+
+Thin Python binding over libpa.so (include/pa.h).  PyTorch is used only for
+device memory and the current stream; every step of the computation runs in
+the library's HIP kernels.  The cache layouts are
+
+    key_cache   [num_blocks, num_kv_heads, 16, head_dim]
+    value_cache [num_blocks, num_kv_heads, head_dim, 16]
+
+and the flat-batch metadata follows "Model execution", section "Flattening a
+step" (query_start_loc, seq_lens, block tables, slot_mapping).
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import LIB, PA_BF16, PA_F32, PA_BLOCK_SIZE, PA_MAX_SPLITS  # noqa: F401
+
+__all__ = [
+    "PaError", "kv_write", "attention", "split_combine", "workspace_size",
+    "choose_num_splits", "alloc_cache", "trace_begin", "trace_end", "trace_read",
+    "kernel_name", "version",
+]
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = LIB.pa_status_string(status).decode()
+        super().__init__(f"{where}: {msg} (status {status})")
+        self.status = status
+
+
+def _check(status: int, where: str) -> None:
+    if status != _lib.PA_OK:
+        raise PaError(status, where)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    if t.dtype == torch.float32:
+        return PA_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def version() -> int:
+    return int(LIB.pa_version())
+
+
+def alloc_cache(num_blocks: int, num_kv_heads: int, head_dim: int, dtype, device="cuda"):
+    """Allocate an (uninitialised) K and V cache pair in the library's layout."""
+    k = torch.empty(num_blocks, num_kv_heads, PA_BLOCK_SIZE, head_dim, dtype=dtype,
+                    device=device)
+    v = torch.empty(num_blocks, num_kv_heads, head_dim, PA_BLOCK_SIZE, dtype=dtype,
+                    device=device)
+    return k, v
+
+
+def kv_write(key, value, key_cache, value_cache, slot_mapping, stream=None) -> None:
+    """Write the step's new K/V rows ([Nt, Hkv, d]) at their slots."""
+    nt, hkv, d = key.shape
+    if value.shape != key.shape or value.dtype != key.dtype:
+        raise ValueError("key and value must match")
+    if key_cache.dtype != key.dtype or value_cache.dtype != key.dtype:
+        raise ValueError("cache dtype must equal the K/V dtype")
+    nb = key_cache.shape[0]
+    if tuple(key_cache.shape) != (nb, hkv, PA_BLOCK_SIZE, d) or \
+            tuple(value_cache.shape) != (nb, hkv, d, PA_BLOCK_SIZE):
+        raise ValueError("cache shapes must be [NB, Hkv, 16, d] and [NB, Hkv, d, 16]")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (nt,):
+        raise ValueError("slot_mapping must be int64 [num_tokens]")
+    st = LIB.pa_kv_write(_dev(key, "key"), _dev(value, "value"), _dev(key_cache, "key_cache"),
+                         _dev(value_cache, "value_cache"), _dev(slot_mapping, "slot_mapping"),
+                         nt, hkv, d, PA_BLOCK_SIZE, nb, _dtype_code(key), _stream(stream))
+    _check(st, "pa_kv_write")
+
+
+def workspace_size(num_seqs: int, num_tokens: int, num_q_heads: int, head_dim: int,
+                   num_splits: int) -> int:
+    return int(LIB.pa_attention_workspace_size(num_seqs, num_tokens, num_q_heads, head_dim,
+                                               max(1, num_splits)))
+
+
+def choose_num_splits(num_seqs: int, max_query_len: int, max_seq_len: int, num_q_heads: int,
+                      num_kv_heads: int, num_cus: int = 0) -> int:
+    return int(LIB.pa_choose_num_splits(num_seqs, max_query_len, max_seq_len, num_q_heads,
+                                        num_kv_heads, num_cus))
+
+
+def attention(query, key_cache, value_cache, query_start_loc, seq_lens, block_tables,
+              max_query_len: int, max_seq_len: int, scale: float, num_splits: int = 0,
+              out=None, lse=None, want_lse: bool = True, workspace=None, stream=None):
+    """Causal paged attention for every scheduled row.  Returns (out, lse)."""
+    nt, hq, d = query.shape
+    nb, hkv = key_cache.shape[0], key_cache.shape[1]
+    if tuple(key_cache.shape) != (nb, hkv, PA_BLOCK_SIZE, d) or \
+            tuple(value_cache.shape) != (nb, hkv, d, PA_BLOCK_SIZE):
+        raise ValueError("cache shapes must be [NB, Hkv, 16, d] and [NB, Hkv, d, 16]")
+    if key_cache.dtype != query.dtype or value_cache.dtype != query.dtype:
+        raise ValueError("cache dtype must equal the query dtype")
+    for name, t in (("query_start_loc", query_start_loc), ("seq_lens", seq_lens),
+                    ("block_tables", block_tables)):
+        if t.dtype != torch.int32:
+            raise ValueError(f"{name} must be int32")
+    ns = seq_lens.shape[0]
+    if query_start_loc.shape != (ns + 1,) or block_tables.dim() != 2 or \
+            block_tables.shape[0] != ns:
+        raise ValueError("metadata shapes disagree")
+    splits = num_splits
+    if splits == 0:
+        splits = choose_num_splits(ns, max_query_len, max_seq_len, hq, hkv)
+    if out is None:
+        out = torch.empty_like(query)
+    if lse is None and want_lse:
+        lse = torch.empty(nt, hq, dtype=torch.float32, device=query.device)
+    need = workspace_size(ns, nt, hq, d, splits)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+    st = LIB.pa_attention_fwd(
+        _dev(query, "query"), _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+        _dev(query_start_loc, "query_start_loc"), _dev(seq_lens, "seq_lens"),
+        _dev(block_tables, "block_tables"), ns, nt, int(max_query_len), int(max_seq_len),
+        hq, hkv, d, PA_BLOCK_SIZE, block_tables.shape[1], nb, float(scale), splits,
+        _dev(out, "out"), None if lse is None else _dev(lse, "lse"),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _dtype_code(query), _stream(stream))
+    _check(st, "pa_attention_fwd")
+    return out, lse
+
+
+def split_combine(partial_out, partial_lse, out=None, lse=None, dtype=torch.bfloat16,
+                  stream=None):
+    """Merge [S, Nt, Hq, d] fp32 partials and their [S, Nt, Hq] lse."""
+    s, nt, hq, d = partial_out.shape
+    if partial_out.dtype != torch.float32 or partial_lse.dtype != torch.float32 or \
+            tuple(partial_lse.shape) != (s, nt, hq):
+        raise ValueError("partials must be float32 [S, Nt, Hq, d] and [S, Nt, Hq]")
+    if out is None:
+        out = torch.empty(nt, hq, d, dtype=dtype, device=partial_out.device)
+    if lse is None:
+        lse = torch.empty(nt, hq, dtype=torch.float32, device=partial_out.device)
+    st = LIB.pa_split_combine(_dev(partial_out, "partial_out"), _dev(partial_lse, "partial_lse"),
+                              s, nt, hq, d, _dev(out, "out"), _dev(lse, "lse"),
+                              _dtype_code(out), _stream(stream))
+    _check(st, "pa_split_combine")
+    return out, lse
+
+
+def trace_begin(capacity: int = 4096) -> None:
+    _check(LIB.pa_trace_begin(capacity), "pa_trace_begin")
+
+
+def trace_end() -> None:
+    _check(LIB.pa_trace_end(), "pa_trace_end")
+
+
+def kernel_name(kid: int) -> str:
+    return LIB.pa_kernel_name(kid).decode()
+
+
+def trace_read(capacity: int = 1 << 16):
+    """[(kernel_name, milliseconds)] of the launches recorded since
+    trace_begin.  Synchronise the device first."""
+    ids = (ctypes.c_int32 * capacity)()
+    ms = (ctypes.c_float * capacity)()
+    n = LIB.pa_trace_read(ids, ms, capacity)
+    if n < 0:
+        raise PaError(_lib.PA_ERR_INVALID, "pa_trace_read")
+    return [(kernel_name(ids[i]), float(ms[i])) for i in range(n)]

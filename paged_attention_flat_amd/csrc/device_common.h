@@ -1,0 +1,54 @@
+// Device-side helpers for the gfx950 kernels: vector types for the matrix
+// cores, bf16 packing, wave reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// fp32 -> bf16 round-to-nearest-even (NaN stays NaN), as raw bits.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  __bf16 h = static_cast<__bf16>(f);
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h));
+}
+
+// Pack two floats into one dword of two bf16 (lo in the low half).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint2 lo, uint2 hi) {
+  uint4 v = make_uint4(lo.x, lo.y, hi.x, hi.y);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Cross-lane exchange inside a wave64 (ds_bpermute based).
+__device__ __forceinline__ float shfl_xor(float v, int mask) {
+  return __shfl_xor(v, mask, 64);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) {
+  return __builtin_amdgcn_exp2f(x);
+}
+
+__device__ __forceinline__ float fast_log2(float x) {
+  return __builtin_amdgcn_logf(x);
+}
+
+}  // namespace pa

@@ -1,0 +1,78 @@
+// KV write: scatter the step's new K and V rows into the paged cache through
+// slot_mapping ("Model execution", section "Flattening a step": the KV write
+// puts each new token's K and V at slot block_id * block_size + offset).
+//
+// One work-group handles 16 consecutive flat tokens of one KV head.  The K
+// row of a token is a contiguous run in the token-major K block, copied in
+// 16-byte pieces.  The V block is dim-major, so the 16 V rows are first staged
+// in LDS and then written column by column: lanes that differ in the token
+// index write neighbouring offsets of one dimension, which coalesce when the
+// tokens fill consecutive slots of a block (the usual case for a prefill
+// chunk).  The copy is a bit copy; the element type only fixes the width.
+#include "device_common.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+constexpr int kTok = 16;
+
+template <typename E>
+__global__ __launch_bounds__(256) void kv_write_kernel(
+    const E* __restrict__ key, const E* __restrict__ value, E* __restrict__ kc,
+    E* __restrict__ vc, const int64_t* __restrict__ slots, int32_t nt,
+    int32_t hkv, int32_t d) {
+  constexpr int kPad = 16 / sizeof(E);  // keeps LDS rows 16-byte aligned
+  __shared__ __align__(16) E vrow[kTok][128 + kPad];
+  __shared__ int64_t sslot[kTok];
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * kTok;
+  const int h = blockIdx.y;
+  if (tid < kTok) sslot[tid] = (t0 + tid < nt) ? slots[t0 + tid] : -1;
+  __syncthreads();
+
+  const int cpr = d * (int)sizeof(E) / 16;  // 16-byte pieces per row
+  for (int c = tid; c < kTok * cpr; c += 256) {
+    const int ti = c / cpr, part = c - ti * cpr;
+    const int64_t s = sslot[ti];
+    if (s < 0) continue;
+    const size_t src = ((size_t)(t0 + ti) * hkv + h) * d;
+    const uint4 kv = reinterpret_cast<const uint4*>(key + src)[part];
+    const uint4 vv = reinterpret_cast<const uint4*>(value + src)[part];
+    const size_t blk = (size_t)(s >> 4), off = (size_t)(s & 15);
+    E* kdst = kc + ((blk * hkv + h) * kTok + off) * d;
+    reinterpret_cast<uint4*>(kdst)[part] = kv;
+    reinterpret_cast<uint4*>(&vrow[ti][0])[part] = vv;
+  }
+  __syncthreads();
+
+  for (int e = tid; e < kTok * d; e += 256) {
+    const int ti = e & (kTok - 1), c = e >> 4;
+    const int64_t s = sslot[ti];
+    if (s < 0) continue;
+    const size_t blk = (size_t)(s >> 4), off = (size_t)(s & 15);
+    vc[((blk * hkv + h) * d + c) * kTok + off] = vrow[ti][c];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_kv_write(const void* key, const void* value, void* kc, void* vc,
+                           const int64_t* slots, int32_t nt, int32_t hkv,
+                           int32_t d, int32_t esize, hipStream_t stream) {
+  dim3 grid((nt + kTok - 1) / kTok, hkv);
+  trace_before(K_KV_WRITE, stream);
+  if (esize == 2) {
+    hipLaunchKernelGGL(kv_write_kernel<uint16_t>, grid, dim3(256), 0, stream,
+                       (const uint16_t*)key, (const uint16_t*)value, (uint16_t*)kc,
+                       (uint16_t*)vc, slots, nt, hkv, d);
+  } else {
+    hipLaunchKernelGGL(kv_write_kernel<uint32_t>, grid, dim3(256), 0, stream,
+                       (const uint32_t*)key, (const uint32_t*)value, (uint32_t*)kc,
+                       (uint32_t*)vc, slots, nt, hkv, d);
+  }
+  trace_after(stream);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,329 @@
+// Host side of the C ABI declared in include/pa.h: argument validation, the
+// launch plan of one flat step, the split / no-split crossover and the
+// optional kernel tracing.  No entry point synchronises or reads device
+// memory; grids are sized from host scalars only.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <mutex>
+#include <vector>
+
+#include "../../include/pa.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+// ---- tracing ----------------------------------------------------------------
+struct TraceState {
+  std::mutex mu;
+  bool active = false;
+  int32_t capacity = 0;
+  int32_t used = 0;
+  std::vector<hipEvent_t> start, stop;
+  std::vector<int32_t> ids;
+};
+
+TraceState& trace() {
+  static TraceState* s = new TraceState();  // never destroyed: safe at exit
+  return *s;
+}
+
+thread_local int32_t g_pending = -1;
+
+void destroy_events(TraceState& t) {
+  for (auto e : t.start) hipEventDestroy(e);
+  for (auto e : t.stop) hipEventDestroy(e);
+  t.start.clear();
+  t.stop.clear();
+  t.ids.clear();
+  t.capacity = 0;
+  t.used = 0;
+}
+
+int32_t device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return 256;
+  return cus;
+}
+
+bool is_pow2_group(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t plan_capacity(int32_t num_seqs, int32_t num_tokens) {
+  // items <= sum over prefill requests of ceil(q_len / TQ) <= num_tokens / TQ
+  // + (number of such requests); TQ >= 8 and at most min(num_seqs,
+  // num_tokens / 2) requests qualify (they have >= 2 tokens)
+  const size_t by_tokens = (size_t)num_tokens / 8 + 1;
+  const size_t reqs = std::min<size_t>((size_t)num_seqs, (size_t)num_tokens / 2 + 1);
+  return by_tokens + reqs;
+}
+
+size_t workspace_bytes_for(int32_t num_seqs, int32_t num_tokens, int32_t hq, int32_t d,
+                           int32_t splits) {
+  size_t bytes = 256 + (1 + 2 * plan_capacity(num_seqs, num_tokens)) * sizeof(int32_t);
+  bytes = (bytes + 255) & ~size_t(255);
+  if (splits > 1) {
+    const size_t rows = (size_t)splits * num_tokens * hq;
+    bytes += rows * d * sizeof(float);
+    bytes = (bytes + 255) & ~size_t(255);
+    bytes += rows * sizeof(float);
+  }
+  return bytes;
+}
+
+}  // namespace
+
+void trace_before(int32_t kernel_id, hipStream_t stream) {
+  TraceState& t = trace();
+  std::lock_guard<std::mutex> lk(t.mu);
+  g_pending = -1;
+  if (!t.active || t.used >= t.capacity) return;
+  g_pending = t.used++;
+  t.ids[g_pending] = kernel_id;
+  hipEventRecord(t.start[g_pending], stream);
+}
+
+void trace_after(hipStream_t stream) {
+  if (g_pending < 0) return;
+  TraceState& t = trace();
+  std::lock_guard<std::mutex> lk(t.mu);
+  hipEventRecord(t.stop[g_pending], stream);
+  g_pending = -1;
+}
+
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" {
+
+const char* pa_status_string(pa_status s) {
+  switch (s) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "a required pointer is NULL";
+    case PA_ERR_INVALID: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int32_t pa_version(void) { return 100; }  // 0.1.0
+
+const char* pa_kernel_name(int32_t id) {
+  switch (id) {
+    case K_KV_WRITE: return "kv_write";
+    case K_DECODE: return "decode";
+    case K_DECODE_SPLIT: return "decode_split_partial";
+    case K_COMBINE: return "split_combine";
+    case K_PLAN: return "prefill_plan";
+    case K_PREFILL: return "prefill_mfma";
+    case K_F32_ATTN: return "attn_f32";
+    case K_F32_ATTN_SPLIT: return "attn_f32_split_partial";
+  }
+  return "unknown";
+}
+
+pa_status pa_trace_begin(int32_t capacity) {
+  if (capacity <= 0 || capacity > (1 << 20)) return PA_ERR_INVALID;
+  TraceState& t = trace();
+  std::lock_guard<std::mutex> lk(t.mu);
+  destroy_events(t);
+  t.start.resize(capacity);
+  t.stop.resize(capacity);
+  t.ids.assign(capacity, -1);
+  for (int32_t i = 0; i < capacity; ++i) {
+    if (hipEventCreate(&t.start[i]) != hipSuccess || hipEventCreate(&t.stop[i]) != hipSuccess) {
+      t.start.resize(i);
+      t.stop.resize(i);
+      destroy_events(t);
+      return PA_ERR_HIP;
+    }
+  }
+  t.capacity = capacity;
+  t.used = 0;
+  t.active = true;
+  return PA_OK;
+}
+
+pa_status pa_trace_end(void) {
+  TraceState& t = trace();
+  std::lock_guard<std::mutex> lk(t.mu);
+  t.active = false;
+  return PA_OK;
+}
+
+int32_t pa_trace_read(int32_t* kernel_ids, float* ms, int32_t capacity) {
+  if (kernel_ids == nullptr || ms == nullptr || capacity < 0) return -1;
+  TraceState& t = trace();
+  std::lock_guard<std::mutex> lk(t.mu);
+  const int32_t n = std::min(capacity, t.used);
+  for (int32_t i = 0; i < n; ++i) {
+    float v = -1.f;
+    if (hipEventElapsedTime(&v, t.start[i], t.stop[i]) != hipSuccess) v = -1.f;
+    kernel_ids[i] = t.ids[i];
+    ms[i] = v;
+  }
+  return n;
+}
+
+size_t pa_attention_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                   int32_t head_dim, int32_t num_splits) {
+  if (num_seqs < 0 || num_tokens < 0 || num_q_heads <= 0 || head_dim <= 0 || num_splits < 1)
+    return 0;
+  return workspace_bytes_for(num_seqs, num_tokens, num_q_heads, head_dim, num_splits);
+}
+
+int32_t pa_choose_num_splits(int32_t num_seqs, int32_t max_query_len, int32_t max_seq_len,
+                             int32_t num_q_heads, int32_t num_kv_heads, int32_t num_cus) {
+  if (num_seqs <= 0 || num_kv_heads <= 0 || num_q_heads <= 0 || max_seq_len <= 0) return 1;
+  const int32_t group = num_q_heads / num_kv_heads;
+  if (group <= 0 || group > 16) return 1;
+  if (max_query_len > decode_max_q(group)) return 1;  // prefill rows present
+  if (num_cus <= 0) num_cus = device_cu_count();
+  const int64_t units = (int64_t)num_seqs * num_kv_heads;
+  if (units >= num_cus) return 1;
+  const int64_t want = (2 * (int64_t)num_cus + units - 1) / units;
+  const int64_t blocks = (max_seq_len + PA_BLOCK_SIZE - 1) / PA_BLOCK_SIZE;
+  const int64_t by_blocks = std::max<int64_t>(1, blocks / 8);  // >= 8 blocks per split
+  int64_t s = std::min<int64_t>(want, by_blocks);
+  s = std::min<int64_t>(s, PA_MAX_SPLITS);
+  return (int32_t)std::max<int64_t>(1, s);
+}
+
+pa_status pa_kv_write(const void* key, const void* value, void* key_cache, void* value_cache,
+                      const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t block_size, int64_t num_blocks, pa_dtype dtype,
+                      void* stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_INVALID;
+  if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_INVALID;
+  if (block_size != PA_BLOCK_SIZE) return PA_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping) return PA_ERR_NULL;
+  if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) || !aligned16(value_cache))
+    return PA_ERR_INVALID;
+  const int32_t esize = dtype == PA_BF16 ? 2 : 4;
+  hipError_t e = launch_kv_write(key, value, key_cache, value_cache, slot_mapping, num_tokens,
+                                 num_kv_heads, head_dim, esize, (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status pa_split_combine(const float* partial_out, const float* partial_lse,
+                           int32_t num_splits, int32_t num_tokens, int32_t num_q_heads,
+                           int32_t head_dim, void* out, float* lse, pa_dtype dtype,
+                           void* stream) {
+  if (num_splits < 1 || num_splits > PA_MAX_SPLITS || num_tokens < 0 || num_q_heads <= 0)
+    return PA_ERR_INVALID;
+  if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_INVALID;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (!partial_out || !partial_lse || !out) return PA_ERR_NULL;
+  if (!aligned16(partial_out) || !aligned16(out)) return PA_ERR_INVALID;
+  hipError_t e = launch_combine(partial_out, partial_lse, num_splits, num_tokens, num_q_heads,
+                                head_dim, out, lse, dtype == PA_BF16, nullptr, 0, 0,
+                                (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status pa_attention_fwd(const void* query, const void* key_cache, const void* value_cache,
+                           const int32_t* query_start_loc, const int32_t* seq_lens,
+                           const int32_t* block_tables, int32_t num_seqs, int32_t num_tokens,
+                           int32_t max_query_len, int32_t max_seq_len, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int32_t block_table_stride, int64_t num_blocks, float scale,
+                           int32_t num_splits, void* out, float* lse, void* workspace,
+                           size_t workspace_bytes, pa_dtype dtype, void* stream) {
+  if (num_seqs < 0 || num_tokens < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      num_blocks <= 0 || num_splits < 0 || num_splits > PA_MAX_SPLITS || !std::isfinite(scale))
+    return PA_ERR_INVALID;
+  if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_INVALID;
+  if (num_q_heads % num_kv_heads != 0) return PA_ERR_INVALID;
+  const int32_t group = num_q_heads / num_kv_heads;
+  if (!is_pow2_group(group)) return PA_ERR_UNSUPPORTED;
+  if (block_size != PA_BLOCK_SIZE) return PA_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || num_tokens == 0) return PA_OK;
+  if (max_query_len < 1 || max_query_len > num_tokens || max_seq_len < max_query_len)
+    return PA_ERR_INVALID;
+  if ((int64_t)block_table_stride * PA_BLOCK_SIZE < (int64_t)max_seq_len) return PA_ERR_INVALID;
+  if (!query || !key_cache || !value_cache || !query_start_loc || !seq_lens || !block_tables ||
+      !out)
+    return PA_ERR_NULL;
+  if (!aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache) || !aligned16(out))
+    return PA_ERR_INVALID;
+
+  const int32_t splits =
+      num_splits == 0 ? pa_choose_num_splits(num_seqs, max_query_len, max_seq_len, num_q_heads,
+                                             num_kv_heads, 0)
+                      : num_splits;
+  const size_t need = workspace_bytes_for(num_seqs, num_tokens, num_q_heads, head_dim, splits);
+  if (workspace == nullptr || workspace_bytes < need) return PA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return PA_ERR_INVALID;
+
+  AttnArgs a;
+  a.q = query;
+  a.kc = key_cache;
+  a.vc = value_cache;
+  a.qsl = query_start_loc;
+  a.seq_lens = seq_lens;
+  a.tables = block_tables;
+  a.num_seqs = num_seqs;
+  a.num_tokens = num_tokens;
+  a.max_query_len = max_query_len;
+  a.max_seq_len = max_seq_len;
+  a.hq = num_q_heads;
+  a.hkv = num_kv_heads;
+  a.d = head_dim;
+  a.table_stride = block_table_stride;
+  a.scale = scale;
+  a.splits = splits;
+  a.out = out;
+  a.lse = lse;
+  char* ws = static_cast<char*>(workspace);
+  a.plan = reinterpret_cast<int32_t*>(ws + 256);
+  {
+    // tighter bound for this group size (the workspace holds the loosest one)
+    const int64_t tq = prefill_tile_tokens(group), dq = decode_max_q(group);
+    const int64_t cap = num_tokens / tq + 1 +
+                        std::min<int64_t>(num_seqs, num_tokens / (dq + 1) + 1);
+    a.plan_cap = (int32_t)std::min<int64_t>(cap, (int64_t)plan_capacity(num_seqs, num_tokens));
+  }
+  size_t off = 256 + (1 + 2 * plan_capacity(num_seqs, num_tokens)) * sizeof(int32_t);
+  off = (off + 255) & ~size_t(255);
+  a.part_out = nullptr;
+  a.part_lse = nullptr;
+  if (splits > 1) {
+    const size_t rows = (size_t)splits * num_tokens * num_q_heads;
+    a.part_out = reinterpret_cast<float*>(ws + off);
+    off += rows * head_dim * sizeof(float);
+    off = (off + 255) & ~size_t(255);
+    a.part_lse = reinterpret_cast<float*>(ws + off);
+  }
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (dtype == PA_F32) {
+    e = launch_attn_f32(a, s);
+    if (e == hipSuccess && splits > 1)
+      e = launch_combine(a.part_out, a.part_lse, splits, num_tokens, num_q_heads, head_dim, out,
+                         lse, 0, query_start_loc, num_seqs, 1 << 30, s);
+  } else {
+    const int32_t dq = decode_max_q(group);
+    if (max_query_len > dq) e = launch_prefill_bf16(a, s);
+    if (e == hipSuccess) e = launch_decode_bf16(a, s);
+    if (e == hipSuccess && splits > 1)
+      e = launch_combine(a.part_out, a.part_lse, splits, num_tokens, num_q_heads, head_dim, out,
+                         lse, 1, query_start_loc, num_seqs, dq, s);
+  }
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // extern "C"

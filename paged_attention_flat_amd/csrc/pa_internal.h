@@ -1,0 +1,64 @@
+// Internal declarations shared by the host API and the kernel translation
+// units of the paged-attention library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+// ---- kernel ids for tracing -------------------------------------------------
+enum KernelId : int32_t {
+  K_KV_WRITE = 0,
+  K_DECODE = 1,
+  K_DECODE_SPLIT = 2,
+  K_COMBINE = 3,
+  K_PLAN = 4,
+  K_PREFILL = 5,
+  K_F32_ATTN = 6,
+  K_F32_ATTN_SPLIT = 7,
+  K_COUNT = 8
+};
+
+// Tracing hooks (pa_api.cpp).  trace_before/after bracket one launch.
+void trace_before(int32_t kernel_id, hipStream_t stream);
+void trace_after(hipStream_t stream);
+
+// ---- launchers (each enqueues on `stream` and returns hipGetLastError) ------
+hipError_t launch_kv_write(const void* key, const void* value, void* kc, void* vc,
+                           const int64_t* slots, int32_t nt, int32_t hkv,
+                           int32_t d, int32_t esize, hipStream_t stream);
+
+struct AttnArgs {
+  const void* q;
+  const void* kc;
+  const void* vc;
+  const int32_t* qsl;
+  const int32_t* seq_lens;
+  const int32_t* tables;
+  int32_t num_seqs, num_tokens, max_query_len, max_seq_len;
+  int32_t hq, hkv, d, table_stride;
+  float scale;
+  int32_t splits;
+  void* out;
+  float* lse;
+  float* part_out;      // [splits][nt][hq][d] when splits > 1
+  float* part_lse;      // [splits][nt][hq]
+  int32_t* plan;        // work list of the matrix-core kernel
+  int32_t plan_cap;     // capacity of the work list (items)
+};
+
+// Largest number of new tokens per request that the decode kernel packs.
+inline int32_t decode_max_q(int32_t group) { return 16 / group; }
+// Query tokens per work-group of the prefill kernel.
+inline int32_t prefill_tile_tokens(int32_t group) { return 128 / group; }
+
+hipError_t launch_decode_bf16(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_combine(const float* po, const float* pl, int32_t splits,
+                          int32_t nt, int32_t hq, int32_t d, void* out, float* lse,
+                          int32_t out_bf16, const int32_t* qsl, int32_t num_seqs,
+                          int32_t decode_max_q, hipStream_t stream);
+
+}  // namespace pa

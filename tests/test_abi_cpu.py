@@ -1,0 +1,117 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every entry point declared in include/pa.h, and rejects bad arguments before
+anything is launched."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "pa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from paged_attention_flat_amd import _lib
+    return _lib.LIB
+
+
+def test_header_declares_the_boundary():
+    names = header_functions()
+    for required in ("pa_kv_write", "pa_attention_fwd", "pa_split_combine"):
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from paged_attention_flat_amd import _lib
+    for name in header_functions():
+        assert hasattr(lib, name), name
+        assert name in _lib.PROTOTYPES, f"{name} has no Python prototype"
+
+
+def test_status_strings(lib):
+    for s in range(6):
+        assert lib.pa_status_string(s)
+    assert lib.pa_status_string(99) == b"unknown status"
+    assert lib.pa_version() >= 100
+
+
+def test_kv_write_validation(lib):
+    P = ctypes.c_void_p(16)  # never dereferenced: every call below fails validation
+    assert lib.pa_kv_write(P, P, P, P, P, 4, 0, 128, 16, 8, 1, None) == 2   # no KV heads
+    assert lib.pa_kv_write(P, P, P, P, P, 4, 2, 96, 16, 8, 1, None) == 3    # head_dim
+    assert lib.pa_kv_write(P, P, P, P, P, 4, 2, 128, 32, 8, 1, None) == 3   # block size
+    assert lib.pa_kv_write(P, P, P, P, P, 4, 2, 128, 16, 8, 7, None) == 2   # dtype
+    assert lib.pa_kv_write(None, P, P, P, P, 4, 2, 128, 16, 8, 1, None) == 1
+    assert lib.pa_kv_write(None, None, None, None, None, 0, 2, 128, 16, 8, 1, None) == 0
+    assert lib.pa_kv_write(ctypes.c_void_p(18), P, P, P, P, 4, 2, 128, 16, 8, 1, None) == 2
+
+
+def _fwd(lib, **kw):
+    P = ctypes.c_void_p(256)
+    a = dict(q=P, kc=P, vc=P, qsl=P, sl=P, bt=P, ns=2, nt=3, mq=2, ms=40, hq=8, hkv=2, d=128,
+             bs=16, stride=3, nb=10, scale=0.1, splits=1, out=P, lse=None, ws=P,
+             wsb=1 << 20, dtype=1)
+    a.update(kw)
+    return lib.pa_attention_fwd(a["q"], a["kc"], a["vc"], a["qsl"], a["sl"], a["bt"], a["ns"],
+                                a["nt"], a["mq"], a["ms"], a["hq"], a["hkv"], a["d"], a["bs"],
+                                a["stride"], a["nb"], a["scale"], a["splits"], a["out"],
+                                a["lse"], a["ws"], a["wsb"], a["dtype"], None)
+
+
+def test_attention_validation(lib):
+    assert _fwd(lib, hq=6, hkv=4) == 2                # Hq % Hkv != 0
+    assert _fwd(lib, hq=6, hkv=2) == 3                # group 3 not implemented
+    assert _fwd(lib, hq=64, hkv=2) == 3               # group 32 not implemented
+    assert _fwd(lib, d=80) == 3
+    assert _fwd(lib, bs=8) == 3
+    assert _fwd(lib, splits=-1) == 2
+    assert _fwd(lib, splits=257) == 2
+    assert _fwd(lib, scale=float("nan")) == 2
+    assert _fwd(lib, dtype=5) == 2
+    assert _fwd(lib, mq=4) == 2                       # max_query_len > num_tokens
+    assert _fwd(lib, ms=1) == 2                       # max_seq_len < max_query_len
+    assert _fwd(lib, stride=2) == 2                   # table narrower than max_seq_len
+    assert _fwd(lib, qsl=None) == 1
+    assert _fwd(lib, out=None) == 1
+    assert _fwd(lib, ws=None) == 4
+    assert _fwd(lib, wsb=16) == 4
+    need = lib.pa_attention_workspace_size(2, 3, 8, 128, 4)
+    assert _fwd(lib, splits=4, wsb=need - 1) == 4
+    assert _fwd(lib, ns=0) == 0 and _fwd(lib, nt=0) == 0
+
+
+def test_split_combine_validation(lib):
+    P = ctypes.c_void_p(256)
+    assert lib.pa_split_combine(P, P, 0, 4, 8, 128, P, None, 1, None) == 2
+    assert lib.pa_split_combine(P, P, 300, 4, 8, 128, P, None, 1, None) == 2
+    assert lib.pa_split_combine(P, P, 4, 4, 8, 100, P, None, 1, None) == 3
+    assert lib.pa_split_combine(None, P, 4, 4, 8, 128, P, None, 1, None) == 1
+    assert lib.pa_split_combine(None, None, 4, 0, 8, 128, None, None, 1, None) == 0
+
+
+def test_workspace_size_grows_with_splits(lib):
+    one = lib.pa_attention_workspace_size(1, 1, 32, 128, 1)
+    many = lib.pa_attention_workspace_size(1, 1, 32, 128, 64)
+    assert many - one >= 64 * 32 * 129 * 4
+    assert lib.pa_attention_workspace_size(1, 1, 32, 128, 0) == 0
+
+
+def test_split_heuristic_crossover(lib):
+    f = lib.pa_choose_num_splits
+    assert f(1, 1, 32768, 32, 8, 256) == 64          # long single decode: split
+    assert f(256, 1, 8192, 32, 8, 256) == 1          # batch fills the grid: no split
+    assert f(4, 8192, 8192, 32, 8, 256) == 1         # prefill rows present
+    assert f(4098, 2048, 18432, 32, 8, 256) == 1
+    assert f(1, 1, 64, 32, 8, 256) == 1              # too few blocks to split
+    assert 1 < f(2, 1, 4096, 32, 8, 256) <= 256
+    assert f(1, 4, 4096, 32, 8, 256) > 1             # 4 new tokens still pack (G = 4)
+    assert f(1, 5, 4096, 32, 8, 256) == 1
