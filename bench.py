@@ -1,0 +1,456 @@
+#!/usr/bin/env python3
+"""Throughput of one flat paged-attention step on one MI355X.
+
+A step is the whole hot path over one batch of synthetic input: the KV write
+of the step's new tokens through slot_mapping, then causal attention of
+every scheduled row through the block tables (decode kernel with split-KV
+partials + combine, and/or the matrix-core prefill kernel).
+
+Headline workload: long-context single decode (1 request, 1 new token,
+context 32768, 32 query / 8 KV heads, head_dim 128, bf16, 16-token blocks
+scattered over a 4096-block pool).  value = algorithmic HBM bytes of a step /
+wall time per step (GB/s).  Eight replicas of the inputs (separate pools)
+are cycled so that no step finds its 128 MiB of K/V in the 256 MiB Infinity
+Cache left by the previous one.  Steps are replayed from HIP graphs (one per
+replica) so the host launch path is not what is measured.
+
+Also reported, in the same JSON line: the dominant kernel against its
+roofline (durations from HIP events on the kernel's own stream, GPU kept
+ahead of the host), the fp64 CPU oracle on a bounded sample of the same
+workload, and the other workloads (large-batch decode, long prefill, mixed
+chunked-prefill step) with their own rooflines.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode attn HBM GB/s and prefill attn TFLOP/s, % of MI355X roofline"
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+
+WORKLOAD_NAMES = {
+    2: "long-context single decode (B=1, context 32768, Hq 32/Hkv 8, d 128, bf16, 64 splits)",
+    3: "large-batch decode (B=256, contexts U[512,8192], Hq 32/Hkv 8, d 128, bf16, no split)",
+    4: "long prefill (4 x 8192 new tokens, causal, Hq 32/Hkv 8, d 128, bf16)",
+    5: "mixed chunked-prefill step (2 x 2048-token chunks + 4096 decodes, 25% shared "
+       "1024-token prefix, Hq 32/Hkv 8, d 128, bf16)",
+}
+
+
+def parse_args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--replicas", type=int, default=8)
+    ap.add_argument("--eager", action="store_true", help="launch steps from Python, no graphs")
+    ap.add_argument("--only-main", action="store_true", help="skip the other workloads")
+    ap.add_argument("--extra-steps", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a plain 1 GiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------------------
+# algorithmic work of a step (what the method must move / compute)
+# ----------------------------------------------------------------------------
+
+def work_model(step):
+    """Bytes and FLOPs the step must move/compute, independent of the kernels.
+
+    * context K/V: every cached token a request attends to, 2 * Hkv * d * esize
+      bytes, counted once per physical block (shared prefix blocks once);
+    * Q read, output and lse written, block-table entries and metadata read;
+    * the KV write: new K/V read and written, slot_mapping read;
+    * FLOPs: 4 * d * Hq per visible (query, key) pair (QK^T and PV).
+    Split partials are overhead, not counted.
+    """
+    import numpy as np
+    es = 2 if step.dtype == "bf16" else 4
+    hq, hkv, d = step.num_q_heads, step.num_kv_heads, step.head_dim
+    tok_bytes = 2 * hkv * d * es
+    tokens_in_block = {}
+    table_entries = 0
+    pairs = 0
+    dec_tokens = 0
+    pre_pairs = 0
+    ql = step.q_lens
+    for b in range(step.num_seqs):
+        sl = int(step.seq_lens[b])
+        nb = -(-sl // 16)
+        table_entries += nb
+        for j in range(nb):
+            pb = int(step.block_tables[b, j])
+            cnt = min(16, sl - 16 * j)
+            if cnt > tokens_in_block.get(pb, 0):
+                tokens_in_block[pb] = cnt
+        q = int(ql[b])
+        ctx = sl - q
+        pr = q * ctx + q * (q + 1) // 2
+        pairs += pr
+        if q > 16 // (hq // hkv):
+            pre_pairs += pr
+        else:
+            dec_tokens += sl
+    ctx_tokens = sum(tokens_in_block.values())
+    nt = int(step.query_start_loc[-1])
+    kv_bytes = ctx_tokens * tok_bytes
+    io = nt * hq * d * es * 2 + nt * hq * 4 + table_entries * 4 + (2 * step.num_seqs + 1) * 4
+    write = nt * hkv * d * es * 2 * 2 + nt * 8
+    return {
+        "bytes": kv_bytes + io + write,
+        "kv_bytes": kv_bytes,
+        "ctx_tokens": ctx_tokens,
+        "tok_bytes": tok_bytes,
+        "flops": 4.0 * d * hq * pairs,
+        "prefill_flops": 4.0 * d * hq * pre_pairs,
+        "pairs": pairs,
+        "table_entries": table_entries,
+        "q_bytes": nt * hq * d * es,
+        "write_bytes": write,
+    }
+
+
+def decode_kernel_bytes(step):
+    """Algorithmic bytes of the decode kernel alone: K/V of the decode rows'
+    context (unique blocks), their Q, output/partials excluded, table reads."""
+    es = 2 if step.dtype == "bf16" else 4
+    hq, hkv, d = step.num_q_heads, step.num_kv_heads, step.head_dim
+    dq = 16 // (hq // hkv)
+    seen = {}
+    entries = 0
+    rows = 0
+    ql = step.q_lens
+    for b in range(step.num_seqs):
+        if int(ql[b]) > dq or int(ql[b]) == 0:
+            continue
+        sl = int(step.seq_lens[b])
+        nb = -(-sl // 16)
+        entries += nb
+        rows += int(ql[b])
+        for j in range(nb):
+            pb = int(step.block_tables[b, j])
+            cnt = min(16, sl - 16 * j)
+            if cnt > seen.get(pb, 0):
+                seen[pb] = cnt
+    toks = sum(seen.values())
+    return toks * 2 * hkv * d * es + rows * hq * d * es + entries * 4, toks
+
+
+# ----------------------------------------------------------------------------
+# step runners
+# ----------------------------------------------------------------------------
+
+class StepRunner:
+    """Enqueues one step (KV write + attention) on the current stream, calling
+    the C ABI directly with pre-marshalled arguments."""
+
+    def __init__(self, step, dev, num_splits, pools=None):
+        import ctypes
+
+        import torch
+
+        import paged_attention_flat_amd as pa
+        from paged_attention_flat_amd import _lib
+        self.pa, self.lib, self.ctypes, self.torch = pa, _lib.LIB, ctypes, torch
+        self.step = step
+        g = {}
+        for name in ("query", "key", "value"):
+            g[name] = getattr(step, name).to(dev).contiguous()
+        if pools is None:
+            g["kc"] = step.k_pool.to(dev).contiguous()
+            g["vc"] = step.v_pool.to(dev).contiguous()
+        else:
+            g["kc"], g["vc"] = pools
+        g["qsl"] = torch.as_tensor(step.query_start_loc).to(dev)
+        g["sl"] = torch.as_tensor(step.seq_lens).to(dev)
+        g["bt"] = torch.as_tensor(step.block_tables).to(dev)
+        g["sm"] = torch.as_tensor(step.slot_mapping).to(dev)
+        nt, hq, d = g["query"].shape
+        hkv = step.num_kv_heads
+        self.splits = num_splits if num_splits > 0 else pa.choose_num_splits(
+            step.num_seqs, step.max_query_len, step.max_seq_len, hq, hkv)
+        g["out"] = torch.empty_like(g["query"])
+        g["lse"] = torch.empty(nt, hq, dtype=torch.float32, device=dev)
+        ws = pa.workspace_size(step.num_seqs, nt, hq, d, self.splits)
+        g["ws"] = torch.empty(ws, dtype=torch.uint8, device=dev)
+        self.g = g
+        code = _lib.PA_BF16 if step.dtype == "bf16" else _lib.PA_F32
+        P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+        self.kv_args = [P(g["key"]), P(g["value"]), P(g["kc"]), P(g["vc"]), P(g["sm"]), nt, hkv,
+                        d, 16, step.num_blocks, code]
+        self.attn_args = [P(g["query"]), P(g["kc"]), P(g["vc"]), P(g["qsl"]), P(g["sl"]),
+                          P(g["bt"]), step.num_seqs, nt, step.max_query_len, step.max_seq_len,
+                          hq, hkv, d, 16, g["bt"].shape[1], step.num_blocks,
+                          ctypes.c_float(step.scale), self.splits, P(g["out"]), P(g["lse"]),
+                          P(g["ws"]), ws, code]
+
+    def __call__(self):
+        s = self.ctypes.c_void_p(self.torch.cuda.current_stream().cuda_stream)
+        st = self.lib.pa_kv_write(*self.kv_args, s)
+        if st != 0:
+            raise RuntimeError(f"pa_kv_write failed: {st}")
+        st = self.lib.pa_attention_fwd(*self.attn_args, s)
+        if st != 0:
+            raise RuntimeError(f"pa_attention_fwd failed: {st}")
+
+
+def busy_gpu(ms):
+    """Keep the GPU busy for about `ms` so that launches queued behind it run
+    back-to-back (kernel events then measure GPU time, not host gaps)."""
+    import torch
+    try:
+        torch.cuda._sleep(int(ms * 1e-3 * 2.4e9))
+    except Exception:
+        a = torch.randn(4096, 4096, device="cuda", dtype=torch.bfloat16)
+        for _ in range(max(1, int(ms / 0.1))):
+            a = a @ a
+            a = a / a.abs().max()
+
+
+def time_steps(runners, steps, warmup, use_graph, log):
+    """Wall time of exactly `steps` steps (replicas cycled), bracketed by
+    device synchronisation.  Returns (ms_per_step, launch_mode)."""
+    import torch
+    R = len(runners)
+    mode = "eager"
+    graphs = None
+    if use_graph:
+        try:
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                for r in runners:
+                    r()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            graphs = []
+            for r in runners:
+                gr = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gr):
+                    r()
+                graphs.append(gr)
+            torch.cuda.synchronize()
+            mode = "hip-graph"
+        except Exception as e:  # capture unsupported: fall back, say so
+            log(f"graph capture failed ({e!r}); timing eager launches")
+            graphs = None
+    launch = [g.replay for g in graphs] if graphs else list(runners)
+    for i in range(warmup):
+        launch[i % R]()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        launch[i % R]()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return (t1 - t0) * 1e3 / steps, mode
+
+
+def kernel_times(runners, steps, log):
+    """Average duration per library kernel from HIP events recorded around
+    each launch on its stream, with the GPU kept ahead of the host."""
+    import torch
+
+    import paged_attention_flat_amd as pa
+    R = len(runners)
+    for i in range(min(R, 4)):
+        runners[i]()
+    torch.cuda.synchronize()
+    pa.trace_begin(8 * steps + 64)
+    busy_gpu(max(20.0, steps * 0.08))
+    for i in range(steps):
+        runners[i % R]()
+    pa.trace_end()
+    torch.cuda.synchronize()
+    recs = pa.trace_read()
+    agg = {}
+    for name, ms in recs:
+        if ms < 0:
+            continue
+        a = agg.setdefault(name, [0.0, 0])
+        a[0] += ms
+        a[1] += 1
+    return {k: {"avg_us": 1e3 * v[0] / v[1], "launches": v[1]} for k, v in agg.items()}
+
+
+# ----------------------------------------------------------------------------
+# workloads
+# ----------------------------------------------------------------------------
+
+def bench_main(args, log):
+    import torch
+
+    from workloads import config_step
+    dev = torch.device("cuda:0")
+    step = config_step(2, device=dev, fill="zero")
+    base = StepRunner(step, dev, 0)
+    runners = [base]
+    for _ in range(args.replicas - 1):
+        kc = step.k_pool.to(dev).clone()
+        vc = step.v_pool.to(dev).clone()
+        runners.append(StepRunner(step, dev, base.splits, pools=(kc, vc)))
+    wm = work_model(step)
+    ms, mode = time_steps(runners, args.steps, args.warmup, not args.eager, log)
+    kt = kernel_times(runners, min(args.steps, 200), log)
+    kbytes, ktoks = decode_kernel_bytes(step)
+    dom = "decode_split_partial" if base.splits > 1 else "decode"
+    dur_us = kt[dom]["avg_us"]
+    achieved = kbytes / (dur_us * 1e-6) / 1e9
+    res = {
+        "step": step, "ms": ms, "mode": mode, "splits": base.splits, "work": wm,
+        "kernels": kt,
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                     "bytes_per_launch": kbytes, "units_per_launch": ktoks,
+                     "unit_def": "one context token of one request: K and V for 8 KV heads "
+                                 "x 128 dims x 2 B = 4096 B (plus Q and table reads)",
+                     "avg_launch_us": dur_us},
+    }
+    del runners, base
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_extra(cfg, args, log):
+    import torch
+
+    from workloads import config_step
+    dev = torch.device("cuda:0")
+    step = config_step(cfg, device=dev, fill="zero")
+    r = StepRunner(step, dev, 0)
+    wm = work_model(step)
+    ms, mode = time_steps([r], args.extra_steps, 3, not args.eager, log)
+    kt = kernel_times([r], min(args.extra_steps, 20), log)
+    out = {"workload": WORKLOAD_NAMES[cfg], "ms_per_step": ms, "launch": mode,
+           "num_splits": r.splits, "tokens_per_s": step.num_tokens / (ms * 1e-3),
+           "step_GBps": wm["bytes"] / (ms * 1e-3) / 1e9,
+           "step_hbm_frac": wm["bytes"] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+           "step_TFLOPps": wm["flops"] / (ms * 1e-3) / 1e12,
+           "kernels_us": {k: round(v["avg_us"], 2) for k, v in kt.items()}}
+    if "decode" in kt or "decode_split_partial" in kt:
+        name = "decode" if "decode" in kt else "decode_split_partial"
+        kb, _ = decode_kernel_bytes(step)
+        gbs = kb / (kt[name]["avg_us"] * 1e-6) / 1e9
+        out["decode_kernel"] = {"bytes": kb, "GBps": gbs, "frac_hbm": gbs / PEAK_HBM_GBS}
+    if "prefill_mfma" in kt:
+        tf = wm["prefill_flops"] / (kt["prefill_mfma"]["avg_us"] * 1e-6) / 1e12
+        out["prefill_kernel"] = {"flops": wm["prefill_flops"], "TFLOPps": tf,
+                                 "frac_mfma": tf / PEAK_BF16_TFLOPS}
+    if cfg == 5:
+        t_roof = max(wm["bytes"] / (PEAK_HBM_GBS * 1e9), wm["flops"] / (PEAK_BF16_TFLOPS * 1e12))
+        out["step_roofline_frac"] = t_roof / (ms * 1e-3)
+    log(f"config{cfg}: {json.dumps(out)}")
+    del r
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(args, log):
+    """The fp64 oracle (as it stands) on the same workload shape, built on the
+    host: whole steps (KV write + attention of the one decode row), repeated
+    for about args.cpu_seconds.  BLAS is held to one thread."""
+    import threadpoolctl
+
+    import oracle
+    from workloads import config_step, raw_numpy
+    step = config_step(2, device="cpu", fill="zero")
+    key, value = raw_numpy(step.key), raw_numpy(step.value)
+    kp0, vp0 = raw_numpy(step.k_pool), raw_numpy(step.v_pool)
+    q = raw_numpy(step.query)
+    wm = work_model(step)
+    n = 0
+    t_total = 0.0
+    with threadpoolctl.threadpool_limits(1):
+        while t_total < args.cpu_seconds and n < 50:
+            t0 = time.perf_counter()
+            kp, vp = oracle.kv_write(key, value, kp0, vp0, step.slot_mapping)
+            oracle.attention(q, kp, vp, step.query_start_loc, step.seq_lens,
+                             step.block_tables, step.scale, step.num_kv_heads, step.dtype)
+            t_total += time.perf_counter() - t0
+            n += 1
+    per = t_total / n
+    log(f"cpu oracle: {n} steps, {per:.3f} s/step")
+    return {"value": wm["bytes"] / per / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} whole steps of the same workload (KV write + attention of the "
+                      f"decode row, 32 heads x 32768 keys) in fp64, {t_total:.1f} s total, "
+                      f"{per * 1e3:.1f} ms per step"}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): this build has no "
+              "multi-GPU path; see the sharding note in DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 copies of 1073741824 bytes")
+        del src, dst
+    log("main workload: " + WORKLOAD_NAMES[2])
+    res = bench_main(args, log)
+    wm = res["work"]
+    ms = res["ms"]
+    value = wm["bytes"] / (ms * 1e-3) / 1e9
+    log(f"main: {ms * 1e3:.2f} us/step, {value:.1f} GB/s, kernels "
+        f"{json.dumps({k: round(v['avg_us'], 2) for k, v in res['kernels'].items()})}")
+    extras = []
+    if not args.only_main:
+        for cfg in (3, 4, 5):
+            log("extra workload: " + WORKLOAD_NAMES[cfg])
+            extras.append(bench_extra(cfg, args, log))
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args, log)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) Q/K/V rounded to bf16, random block placement",
+        "config": {"workload": WORKLOAD_NAMES[2], "batch": 1, "context": 32768,
+                   "q_heads": 32, "kv_heads": 8, "head_dim": 128, "block_size": 16,
+                   "pool_blocks": 4096, "num_splits": res["splits"], "launch": res["mode"],
+                   "replicas": args.replicas, "step_bytes": wm["bytes"],
+                   "step_hbm_frac": value / PEAK_HBM_GBS},
+        "roofline": {k: (round(v, 4) if isinstance(v, float) else v)
+                     for k, v in res["roofline"].items()},
+        "cpu_baseline": cpu,
+        "kernels_us": {k: round(v["avg_us"], 2) for k, v in res["kernels"].items()},
+        "extra_workloads": extras,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
