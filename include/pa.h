@@ -125,6 +125,8 @@ pa_status pa_kv_write(const void* key, const void* value,
  * (they size the grids).  block_table_stride >= ceil(max_seq_len / 16); table
  * entries past a request's last block are never read.
  *
+ * scale must be positive and finite (e.g. 1 / sqrt(head_dim)).
+ *
  * workspace: device scratch of at least pa_attention_workspace_size(num_seqs,
  * num_tokens, num_q_heads, head_dim, S) bytes, S the split count in use
  * (resolve num_splits = 0 with pa_choose_num_splits first).  It may be NULL

@@ -7,9 +7,10 @@
 // and a split with lse_s = -inf (it saw no key) weighs nothing: its o_s is
 // never read.
 //
-// One wave per (row, query head): the lanes first reduce the split lse
-// values, park the per-split weights in LDS, then each lane accumulates its
-// head_dim / 64 output elements over the splits (coalesced rows of o_s).
+// One work-group per (row, query head).  Its 256 threads first reduce the
+// split lse values (one split per thread), then split the sum over o_s as
+// (group of splits) x (4 consecutive dims): every thread has several
+// independent 16-byte loads in flight, and the groups are folded through LDS.
 // When called from the attention entry point the kernel also gets
 // query_start_loc and skips rows of requests that the matrix-core prefill
 // kernel already finalised.
@@ -34,12 +35,15 @@ struct CombineParams {
 
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
-  constexpr int PER = D / 64;
-  __shared__ float s_w[4][kMaxSplits];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t = blockIdx.x;
-  const int h = blockIdx.y * 4 + wave;
-  if (h >= p.hq) return;
+  constexpr int QUADS = D / 4;          // float4 columns of a row
+  constexpr int GROUPS = 256 / QUADS;   // split groups (8 for D=128, 16 for D=64)
+  __shared__ float s_w[kMaxSplits];
+  __shared__ float s_red[8];
+  __shared__ float4 s_acc[GROUPS][QUADS];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t = blockIdx.x / p.hq;
+  const int h = blockIdx.x - t * p.hq;
   if (p.qsl != nullptr) {
     if (t >= p.qsl[p.num_seqs]) return;
     int lo = 0, hi = p.num_seqs - 1;
@@ -51,60 +55,68 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   }
   const size_t row = (size_t)t * p.hq + h;
   const size_t split_stride = (size_t)p.nt * p.hq;
-  float M = -INFINITY;
-  for (int s = lane; s < p.splits; s += 64) M = fmaxf(M, p.pl[s * split_stride + row]);
+
+  const float x = tid < p.splits ? p.pl[tid * split_stride + row] : -INFINITY;
+  float M = x;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, shfl_xor(M, o));
-  const int d0 = lane * PER;
+  if (lane == 0) s_red[wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
   if (M == -INFINITY) {
     // no split saw a key
-    for (int k = 0; k < PER; ++k) {
-      if (p.out_bf16) reinterpret_cast<uint16_t*>(p.out)[row * D + d0 + k] = 0x7fc0;
-      else reinterpret_cast<float*>(p.out)[row * D + d0 + k] = __builtin_nanf("");
+    for (int d = tid; d < D; d += 256) {
+      if (p.out_bf16) reinterpret_cast<uint16_t*>(p.out)[row * D + d] = 0x7fc0;
+      else reinterpret_cast<float*>(p.out)[row * D + d] = __builtin_nanf("");
     }
-    if (p.lse != nullptr && lane == 0) p.lse[row] = -INFINITY;
+    if (p.lse != nullptr && tid == 0) p.lse[row] = -INFINITY;
     return;
   }
-  float sum = 0.f;
-  for (int s = lane; s < p.splits; s += 64) {
-    const float x = p.pl[s * split_stride + row];
-    const float w = (x == -INFINITY) ? 0.f : fast_exp2((x - M) * kLog2e);
-    s_w[wave][s] = w;
-    sum += w;
-  }
+  const float w = (x == -INFINITY) ? 0.f : fast_exp2((x - M) * kLog2e);
+  if (tid < kMaxSplits) s_w[tid] = w;
+  float sum = w;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) sum += shfl_xor(sum, o);
-  const float inv = 1.f / sum;
-  float acc[PER];
-#pragma unroll
-  for (int k = 0; k < PER; ++k) acc[k] = 0.f;
-  // s_w is written and read by the same wave only
-  __builtin_amdgcn_wave_barrier();
-  for (int s = 0; s < p.splits; ++s) {
-    const float w = s_w[wave][s];
-    if (w == 0.f) continue;
-    const float* src = p.po + (s * split_stride + row) * D + d0;
-    if constexpr (PER == 2) {
-      const float2 v = *reinterpret_cast<const float2*>(src);
-      acc[0] += w * v.x;
-      acc[1] += w * v.y;
-    } else {
-      acc[0] += w * src[0];
-    }
+  if (lane == 0) s_red[4 + wave] = sum;
+  __syncthreads();
+  sum = (s_red[4] + s_red[5]) + (s_red[6] + s_red[7]);
+
+  const int quad = tid % QUADS, grp = tid / QUADS;
+  const float* base = p.po + row * D + quad * 4;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+  for (int s = grp; s < p.splits; s += GROUPS) {
+    const float ws = s_w[s];
+    if (ws == 0.f) continue;
+    const float4 v = *reinterpret_cast<const float4*>(base + s * split_stride * D);
+    acc.x += ws * v.x;
+    acc.y += ws * v.y;
+    acc.z += ws * v.z;
+    acc.w += ws * v.w;
   }
-  if (p.out_bf16) {
-    uint16_t* dst = reinterpret_cast<uint16_t*>(p.out) + row * D + d0;
-    if constexpr (PER == 2) {
-      *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-    } else {
-      dst[0] = (uint16_t)f32_to_bf16_bits(acc[0] * inv);
-    }
-  } else {
-    float* dst = reinterpret_cast<float*>(p.out) + row * D + d0;
+  s_acc[grp][quad] = acc;
+  __syncthreads();
+  if (tid < QUADS) {
+    float4 r = s_acc[0][tid];
 #pragma unroll
-    for (int k = 0; k < PER; ++k) dst[k] = acc[k] * inv;
+    for (int g = 1; g < GROUPS; ++g) {
+      const float4 v = s_acc[g][tid];
+      r.x += v.x;
+      r.y += v.y;
+      r.z += v.z;
+      r.w += v.w;
+    }
+    const float inv = 1.f / sum;
+    if (p.out_bf16) {
+      uint16_t* dst = reinterpret_cast<uint16_t*>(p.out) + row * D + tid * 4;
+      *reinterpret_cast<uint2*>(dst) =
+          make_uint2(pack_bf16x2(r.x * inv, r.y * inv), pack_bf16x2(r.z * inv, r.w * inv));
+    } else {
+      float* dst = reinterpret_cast<float*>(p.out) + row * D + tid * 4;
+      *reinterpret_cast<float4*>(dst) = make_float4(r.x * inv, r.y * inv, r.z * inv, r.w * inv);
+    }
+    if (p.lse != nullptr && tid == 0) p.lse[row] = M + fast_log2(sum) * kLn2;
   }
-  if (p.lse != nullptr && lane == 0) p.lse[row] = M + fast_log2(sum) * kLn2;
 }
 
 }  // namespace
@@ -125,7 +137,7 @@ hipError_t launch_combine(const float* po, const float* pl, int32_t splits, int3
   p.qsl = qsl;
   p.num_seqs = num_seqs;
   p.dq = dq;
-  dim3 grid(nt, (hq + 3) / 4);
+  dim3 grid(nt * hq);
   trace_before(K_COMBINE, stream);
   if (d == 64) hipLaunchKernelGGL(combine_kernel<64>, grid, dim3(256), 0, stream, p);
   else hipLaunchKernelGGL(combine_kernel<128>, grid, dim3(256), 0, stream, p);

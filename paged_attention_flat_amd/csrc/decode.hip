@@ -8,23 +8,30 @@
 // ranges, merged by a second kernel) and "Attention over a block table, not a
 // contiguous tensor" (keys and values gathered through the block table).
 //
-// MI355X design.  One work-group = (request, KV head, split); its four waves
+// MI355X design.  One work-group = (KV head, request, split); its eight waves
 // walk disjoint pairs of 16-token blocks of the split's range and each keeps
-// its own (m, l, acc) state, merged through LDS at the end.  All query heads
-// of the KV head (group size G) and up to 16 / G new tokens are packed as the
-// 16 columns of a 16x16x32 bf16 MFMA, so every K/V byte is read from HBM once
-// per step:
+// its own (m, l, acc) state, merged lane by lane through LDS at the end.  All
+// query heads of the KV head (group size G) and up to 16 / G new tokens are
+// packed as the 16 columns of a 16x16x32 bf16 MFMA, so every K/V byte is read
+// from HBM once per step:
 //   S^T[key][col] = K[key][:] . Q[col][:]    A = K rows (16-byte loads),
 //                                            B = Q (held in registers)
 //   O^T[d][col]  += V^T[d][keys] P[keys][col] A = V (dim-major cache block:
-//                                            8-byte loads of 4 keys),
+//                                            16-byte loads of 8 keys),
 //                                            B = P straight from the S^T
 //                                            accumulator, no shuffles.
-// A pair of blocks gives the 32-key contraction of the P.V product: MFMA
-// slots 0-3 of a lane's key group carry keys 4g..4g+3 of the first block and
-// slots 4-7 the same keys of the second, the order the S^T accumulator
-// produces them in.  Row maxima use two cross-lane exchanges; exponentials
-// are base 2 on log2(e)-prescaled scores.
+// A pair of blocks gives the 32-key contraction of the P.V product; the rows
+// of the two S^T products are assigned to keys so that each lane's P values
+// are 8 consecutive keys of one block, matching one 16-byte V load.  Block
+// ids come 64 at a time from one coalesced table load and are picked with
+// readlane.  Eight waves per work-group (16 per CU at 124 VGPRs) keep enough
+// loads in flight to cover HBM latency.  Row maxima use two cross-lane
+// exchanges; exponentials are base 2 on log2(e)-prescaled scores.
+//
+// Work order: work-group index = KV head fastest, then request rank.  For
+// batches with more work than compute units the ranks come from a device-side
+// counting sort of the decode requests by block count, longest first, so the
+// long requests start early and short ones fill the tail.
 #include "device_common.h"
 #include "pa_internal.h"
 
@@ -38,7 +45,8 @@ struct DecodeParams {
   const int32_t* qsl;
   const int32_t* seq_lens;
   const int32_t* tables;
-  int32_t hq, hkv, table_stride, splits, nt;
+  const int32_t* order;   // nullable: order[0] = count, order[1 + rank] = request
+  int32_t num_seqs, hq, hkv, table_stride, splits, nt;
   float scale_log2;
   uint16_t* out;
   float* lse;
@@ -46,23 +54,89 @@ struct DecodeParams {
   float* part_lse;
 };
 
-constexpr int kWaves = 4;
+// Two launch shapes.  Many work units: 8 waves per work-group, one pair in
+// flight per wave (124 VGPRs, 16 waves per CU).  Few work units (at most two
+// work-groups per CU): 4 waves per work-group, each keeping its next pair in
+// flight while it computes the current one.
+#ifndef PA_DECODE_WAVES_WIDE
+#define PA_DECODE_WAVES_WIDE 8
+#endif
+#ifndef PA_DECODE_WAVES_PIPE
+#define PA_DECODE_WAVES_PIPE 4
+#endif
+constexpr int kBuckets = 4096;
 
-template <int D, int G>
-__global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
+// Counting sort of the decode requests (0 < q_len <= dq) by block count,
+// largest first.  One work-group; ties keep no particular order (the order
+// only schedules work, it never changes a result).
+__global__ __launch_bounds__(1024) void decode_order_kernel(const int32_t* __restrict__ qsl,
+                                                            const int32_t* __restrict__ seq_lens,
+                                                            int32_t num_seqs, int32_t dq,
+                                                            int32_t shift,
+                                                            int32_t* __restrict__ order) {
+  __shared__ int hist[kBuckets];
+  __shared__ int part[1024];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kBuckets; i += 1024) hist[i] = 0;
+  __syncthreads();
+  for (int b = tid; b < num_seqs; b += 1024) {
+    const int ql = qsl[b + 1] - qsl[b];
+    if (ql <= 0 || ql > dq) continue;
+    const int key = min(((seq_lens[b] + 15) >> 4) >> shift, kBuckets - 1);
+    atomicAdd(&hist[kBuckets - 1 - key], 1);
+  }
+  __syncthreads();
+  // exclusive scan of hist: 4 buckets per thread, then a scan of the partials
+  int loc[4], s = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    loc[k] = s;
+    s += hist[tid * 4 + k];
+  }
+  part[tid] = s;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  const int base = part[tid] - s;
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; ++k) hist[tid * 4 + k] = base + loc[k];
+  if (tid == 1023) order[0] = part[1023];
+  __syncthreads();
+  for (int b = tid; b < num_seqs; b += 1024) {
+    const int ql = qsl[b + 1] - qsl[b];
+    if (ql <= 0 || ql > dq) continue;
+    const int key = min(((seq_lens[b] + 15) >> 4) >> shift, kBuckets - 1);
+    const int pos = atomicAdd(&hist[kBuckets - 1 - key], 1);
+    order[1 + pos] = b;
+  }
+}
+
+template <int D, int G, int NW, int PIPE>
+__global__ __launch_bounds__(64 * NW, (PIPE == 2 ? 2 : 1)) void decode_kernel(DecodeParams p) {
   constexpr int DQ = 16 / G;       // new tokens per request packed in the columns
   constexpr int KSTEPS = D / 32;   // MFMA steps over head_dim for S^T
   constexpr int DB = D / 16;       // 16-row blocks of O^T
-  constexpr int ACC_STRIDE = D + 4;
+  constexpr int NREG = 4 * DB + 2; // per-lane state: acc, m, l
 
-  __shared__ float s_m[kWaves][16];
-  __shared__ float s_l[kWaves][16];
-  __shared__ float s_acc[kWaves][16][ACC_STRIDE];
+  // lane-local exchange buffer for the tree merge of the waves' states
+  __shared__ float s_x[NW / 2][NREG][64];
 
-  const int b = blockIdx.x, kvh = blockIdx.y, split = blockIdx.z;
+  const int kvh = blockIdx.x % p.hkv;
+  const int rank = blockIdx.x / p.hkv;
+  const int split = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, kg = lane >> 4;
 
+  int b = rank;
+  if (p.order != nullptr) {
+    if (rank >= p.order[0]) return;
+    b = p.order[1 + rank];
+  }
   const int q0 = p.qsl[b];
   const int q_len = p.qsl[b + 1] - q0;
   if (q_len <= 0 || q_len > DQ) return;  // empty request or a prefill row set
@@ -90,11 +164,18 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
     for (int st = 0; st < KSTEPS; ++st) qf[st] = as_bf16x8(make_uint4(0, 0, 0, 0));
   }
 
+  // Key order inside a pair of blocks (32 keys).  MFMA row r of the first
+  // S^T product is key 8*(r/4) + r%4, of the second key 8*(r/4) + 4 + r%4, so
+  // lane (col, kg) ends up with the 8 consecutive keys 8*kg .. 8*kg+7 of the
+  // pair: the same 8 keys its V operand reads as one 16-byte run of the
+  // dim-major block (block kg/2, keys 8*(kg%2) ..).
+  const int ra = 8 * (col >> 2) + (col & 3);   // pair key of A row `col`, first product
+  const int rb = ra + 4;                       // second product
   const int32_t* table = p.tables + (size_t)b * p.table_stride;
   const size_t head_elems = 16 * D;
   const size_t block_elems = (size_t)p.hkv * head_elems;
-  const uint16_t* kbase = p.kc + kvh * head_elems;
-  const uint16_t* vbase = p.vc + kvh * head_elems;
+  const uint16_t* kbase = p.kc + kvh * head_elems + 8 * kg;
+  const uint16_t* vbase = p.vc + kvh * head_elems + col * 16 + 8 * (kg & 1);
 
   float m = -INFINITY, l = 0.f;
   f32x4 acc[DB];
@@ -102,153 +183,180 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
   for (int i = 0; i < DB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int npairs = blk_hi > blk_lo ? (blk_hi - blk_lo + 1) >> 1 : 0;
-  for (int pr = wave; pr < npairs; pr += kWaves) {
-    const int j0 = blk_lo + 2 * pr;
-    const bool has1 = j0 + 1 < blk_hi;
-    const int phys0 = table[j0];
-    const int phys1 = has1 ? table[j0 + 1] : phys0;
-    const uint16_t* k0 = kbase + (size_t)phys0 * block_elems + col * D + 8 * kg;
-    const uint16_t* k1 = kbase + (size_t)phys1 * block_elems + col * D + 8 * kg;
-    const uint16_t* v0 = vbase + (size_t)phys0 * block_elems + col * 16 + 4 * kg;
-    const uint16_t* v1 = vbase + (size_t)phys1 * block_elems + col * 16 + 4 * kg;
+  int tab = 0, tab_base = -1;
 
-    bf16x8 ka[KSTEPS], kb[KSTEPS];
+  struct Frag {
+    bf16x8 a[KSTEPS], b[KSTEPS];
+    uint4 v[DB];
+  };
+  auto load = [&](Frag& f, int pr) {
+    const int rel = 2 * pr;  // block offset inside the split
+    if ((rel & ~63) != tab_base) {
+      // 64 table entries per load, read back with readlane
+      tab_base = rel & ~63;
+      const int j = blk_lo + tab_base + lane;
+      tab = j < blk_hi ? table[j] : 0;
+    }
+    const bool has1 = blk_lo + rel + 1 < blk_hi;
+    const int phys0 = __builtin_amdgcn_readlane(tab, rel & 63);
+    const int phys1 = has1 ? __builtin_amdgcn_readlane(tab, (rel & 63) + 1) : phys0;
+    const int pa_ = ra < 16 ? phys0 : phys1, pb_ = rb < 16 ? phys0 : phys1;
+    const uint16_t* ka = kbase + (size_t)pa_ * block_elems + (ra & 15) * D;
+    const uint16_t* kb = kbase + (size_t)pb_ * block_elems + (rb & 15) * D;
+    const uint16_t* vp = vbase + (size_t)(kg < 2 ? phys0 : phys1) * block_elems;
 #pragma unroll
     for (int st = 0; st < KSTEPS; ++st) {
-      ka[st] = as_bf16x8(*reinterpret_cast<const uint4*>(k0 + 32 * st));
-      kb[st] = as_bf16x8(*reinterpret_cast<const uint4*>(k1 + 32 * st));
+      f.a[st] = as_bf16x8(*reinterpret_cast<const uint4*>(ka + 32 * st));
+      f.b[st] = as_bf16x8(*reinterpret_cast<const uint4*>(kb + 32 * st));
     }
-    uint2 va[DB], vb[DB];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      va[db] = *reinterpret_cast<const uint2*>(v0 + db * 16 * 16);
-      vb[db] = *reinterpret_cast<const uint2*>(v1 + db * 16 * 16);
-    }
-
+    for (int db = 0; db < DB; ++db) f.v[db] = *reinterpret_cast<const uint4*>(vp + db * 256);
+  };
+  auto compute = [&](Frag& f, int pr) {
+    const int j0 = blk_lo + 2 * pr;
+    const bool has1 = j0 + 1 < blk_hi;
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int st = 0; st < KSTEPS; ++st) {
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[st], qf[st], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[st], qf[st], s1, 0, 0, 0);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[st], qf[st], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.b[st], qf[st], s1, 0, 0, 0);
     }
-
+    // lane (col, kg): sv[e] is the score of pair key 8*kg + e
     float sv[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      sv[i] = s0[i] * p.scale_log2;
-      sv[4 + i] = s1[i] * p.scale_log2;
+      sv[i] = s0[i];
+      sv[4 + i] = s1[i];
     }
-    const int kp0 = 16 * j0 + 4 * kg;  // position of sv[0]
+    const int kp0 = 16 * j0 + 8 * kg;  // position of sv[0]
     if (16 * j0 + 31 > ctx) {
-      // the pair reaches past the first new token: causal mask per column,
-      // and keys past the context (tail of the last block, or a missing
-      // second block) must not reach the P.V product even as NaN * 0
-      uint32_t m0x = 0xffffffffu, m0y = 0xffffffffu, m1x = 0xffffffffu, m1y = 0xffffffffu;
+      // the pair reaches past the first new token: causal mask per column;
+      // keys past the context (tail of the last block, or a missing second
+      // block) must not reach the P.V product even as NaN * 0
+      uint32_t vm[4] = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
+      const bool blk_ok = has1 || kg < 2;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int pa = kp0 + i, pb = kp0 + 16 + i;
-        if (pa > qpos) sv[i] = -INFINITY;
-        if (!has1 || pb > qpos) sv[4 + i] = -INFINITY;
-        const uint32_t half = (i & 1) ? 0xffff0000u : 0x0000ffffu;
-        if (pa >= seq_len) { if (i < 2) m0x &= ~half; else m0y &= ~half; }
-        if (!has1 || pb >= seq_len) { if (i < 2) m1x &= ~half; else m1y &= ~half; }
+      for (int e = 0; e < 8; ++e) {
+        const int kp = kp0 + e;
+        if (!blk_ok || kp > qpos) sv[e] = -INFINITY;
+        if (!blk_ok || kp >= seq_len) vm[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
       }
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        va[db].x &= m0x; va[db].y &= m0y;
-        vb[db].x &= m1x; vb[db].y &= m1y;
+        f.v[db].x &= vm[0];
+        f.v[db].y &= vm[1];
+        f.v[db].z &= vm[2];
+        f.v[db].w &= vm[3];
       }
     }
-
-    float mt = sv[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) mt = fmaxf(mt, sv[i]);
+    float mt = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                     fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
     mt = fmaxf(mt, shfl_xor(mt, 16));
     mt = fmaxf(mt, shfl_xor(mt, 32));
+    mt *= p.scale_log2;  // scale > 0 commutes with max
     const float m_new = fmaxf(m, mt);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     const float alpha = fast_exp2(m - m_use);
     float pv[8], rs = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      pv[i] = fast_exp2(sv[i] - m_use);
+      pv[i] = fast_exp2(__builtin_fmaf(sv[i], p.scale_log2, -m_use));
       rs += pv[i];
     }
     l = l * alpha + rs;
     m = m_new;
 
-    const uint4 pbits = make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
-                                   pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7]));
-    const bf16x8 pf = as_bf16x8(pbits);
+    const bf16x8 pf = as_bf16x8(make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
+                                           pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])));
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       acc[db] *= alpha;
-      acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va[db], vb[db]), pf,
-                                                        acc[db], 0, 0, 0);
+      acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(f.v[db]), pf, acc[db], 0, 0, 0);
+    }
+  };
+
+  if constexpr (PIPE == 1) {
+    for (int pr = wave; pr < npairs; pr += NW) {
+      Frag f;
+      load(f, pr);
+      compute(f, pr);
+    }
+  } else {
+    // two fragment sets: the next pair's loads are in flight during compute
+    Frag fa, fb;
+    int pr = wave;
+    if (pr < npairs) load(fa, pr);
+    while (pr < npairs) {
+      int pn = pr + NW;
+      if (pn < npairs) load(fb, pn);
+      compute(fa, pr);
+      pr = pn;
+      if (pr >= npairs) break;
+      pn = pr + NW;
+      if (pn < npairs) load(fa, pn);
+      compute(fb, pr);
+      pr = pn;
     }
   }
 
   // per-column denominator: sum the four key groups of the wave
   l += shfl_xor(l, 16);
   l += shfl_xor(l, 32);
-  if (kg == 0) {
-    s_m[wave][col] = m;
-    s_l[wave][col] = l;
-  }
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s_acc[wave][col][16 * db + 4 * kg + i] = acc[db][i];
-  __syncthreads();
 
-  // merge the waves: thread -> (column, run of D/16 dims)
-  constexpr int RUN = D / 16;
-  const int c = threadIdx.x >> 4;
-  const int d0 = (threadIdx.x & 15) * RUN;
-  const int cqi = c / G, cg = c - (c / G) * G;
-  if (cqi >= q_len) return;
-  float M = -INFINITY;
+  // tree merge of the waves; every wave holds the same (column, dim) layout,
+  // so the merge is lane-local
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][c]);
-  float wgt[kWaves], L = 0.f;
+  for (int half = NW / 2; half >= 1; half >>= 1) {
+    if (wave >= half && wave < 2 * half) {
+      float* x = &s_x[wave - half][0][lane];
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    wgt[w] = (s_m[w][c] == -INFINITY) ? 0.f : fast_exp2(s_m[w][c] - M);
-    L += wgt[w] * s_l[w][c];
-  }
-  float o[RUN];
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-  for (int k = 0; k < RUN; ++k) {
-    float x = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) x += wgt[w] * s_acc[w][c][d0 + k];
-    o[k] = x;
-  }
-  const int t = q0 + cqi;
-  const int h = kvh * G + cg;
-  if (p.splits == 1) {
-    const float inv = 1.f / L;
-    uint32_t packed[RUN / 2];
-#pragma unroll
-    for (int k = 0; k < RUN / 2; ++k) packed[k] = pack_bf16x2(o[2 * k] * inv, o[2 * k + 1] * inv);
-    uint16_t* dst = p.out + ((size_t)t * p.hq + h) * D + d0;
-    if constexpr (RUN == 8) {
-      *reinterpret_cast<uint4*>(dst) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-    } else {
-      *reinterpret_cast<uint2*>(dst) = make_uint2(packed[0], packed[1]);
+        for (int i = 0; i < 4; ++i) x[(4 * db + i) * 64] = acc[db][i];
+      x[(4 * DB) * 64] = m;
+      x[(4 * DB + 1) * 64] = l;
     }
-    if (p.lse != nullptr && d0 == 0) p.lse[(size_t)t * p.hq + h] = (M + fast_log2(L)) * kLn2;
-  } else {
-    const bool empty = (L == 0.f);
-    const float inv = empty ? 0.f : 1.f / L;
-    float* dst = p.part_out + (((size_t)split * p.nt + t) * p.hq + h) * D + d0;
+    __syncthreads();
+    if (wave < half) {
+      const float* x = &s_x[wave][0][lane];
+      const float mo = x[(4 * DB) * 64], lo = x[(4 * DB + 1) * 64];
+      const float M = fmaxf(m, mo);
+      const float wa = (m == -INFINITY) ? 0.f : fast_exp2(m - M);
+      const float wb = (mo == -INFINITY) ? 0.f : fast_exp2(mo - M);
 #pragma unroll
-    for (int k = 0; k < RUN; k += 4)
-      *reinterpret_cast<float4*>(dst + k) =
-          make_float4(o[k] * inv, o[k + 1] * inv, o[k + 2] * inv, o[k + 3] * inv);
-    if (d0 == 0)
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[db][i] = acc[db][i] * wa + x[(4 * db + i) * 64] * wb;
+      l = l * wa + lo * wb;
+      m = M;
+    }
+    __syncthreads();
+  }
+  if (wave != 0 || !col_valid) return;
+
+  // wave 0, lane (col, kg) holds dims 16*db + 4*kg .. +4 of column col
+  const int t = q0 + qi;
+  const int h = kvh * G + g;
+  if (p.splits == 1) {
+    const float inv = 1.f / l;
+    uint16_t* dst = p.out + ((size_t)t * p.hq + h) * D + 4 * kg;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      *reinterpret_cast<uint2*>(dst + 16 * db) =
+          make_uint2(pack_bf16x2(acc[db][0] * inv, acc[db][1] * inv),
+                     pack_bf16x2(acc[db][2] * inv, acc[db][3] * inv));
+    if (p.lse != nullptr && kg == 0) p.lse[(size_t)t * p.hq + h] = (m + fast_log2(l)) * kLn2;
+  } else {
+    const bool empty = (l == 0.f);
+    const float inv = empty ? 0.f : 1.f / l;
+    float* dst = p.part_out + (((size_t)split * p.nt + t) * p.hq + h) * D + 4 * kg;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      *reinterpret_cast<float4*>(dst + 16 * db) =
+          make_float4(acc[db][0] * inv, acc[db][1] * inv, acc[db][2] * inv, acc[db][3] * inv);
+    if (kg == 0)
       p.part_lse[((size_t)split * p.nt + t) * p.hq + h] =
-          empty ? -INFINITY : (M + fast_log2(L)) * kLn2;
+          empty ? -INFINITY : (m + fast_log2(l)) * kLn2;
   }
 }
 
@@ -261,6 +369,8 @@ void launch_dg(const AttnArgs& a, hipStream_t stream) {
   p.qsl = a.qsl;
   p.seq_lens = a.seq_lens;
   p.tables = a.tables;
+  p.order = a.decode_order;
+  p.num_seqs = a.num_seqs;
   p.hq = a.hq;
   p.hkv = a.hkv;
   p.table_stride = a.table_stride;
@@ -271,9 +381,25 @@ void launch_dg(const AttnArgs& a, hipStream_t stream) {
   p.lse = a.lse;
   p.part_out = a.part_out;
   p.part_lse = a.part_lse;
-  dim3 grid(a.num_seqs, a.hkv, a.splits);
+  if (a.decode_order != nullptr) {
+    int shift = 0;
+    const int max_blocks = (a.max_seq_len + 15) / 16;
+    while ((max_blocks >> shift) >= kBuckets) ++shift;
+    trace_before(K_DECODE_ORDER, stream);
+    hipLaunchKernelGGL(decode_order_kernel, dim3(1), dim3(1024), 0, stream, a.qsl, a.seq_lens,
+                       a.num_seqs, 16 / G, shift, a.decode_order);
+    trace_after(stream);
+  }
+  dim3 grid(a.num_seqs * a.hkv, a.splits);
+  const int64_t units = (int64_t)a.num_seqs * a.hkv * a.splits;
   trace_before(a.splits > 1 ? K_DECODE_SPLIT : K_DECODE, stream);
-  hipLaunchKernelGGL((decode_kernel<D, G>), grid, dim3(256), 0, stream, p);
+  if (units <= 2 * (int64_t)a.num_cus) {
+    constexpr int NW = PA_DECODE_WAVES_PIPE;
+    hipLaunchKernelGGL((decode_kernel<D, G, NW, 2>), grid, dim3(64 * NW), 0, stream, p);
+  } else {
+    constexpr int NW = PA_DECODE_WAVES_WIDE;
+    hipLaunchKernelGGL((decode_kernel<D, G, NW, 1>), grid, dim3(64 * NW), 0, stream, p);
+  }
   trace_after(stream);
 }
 

@@ -24,9 +24,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h));
 }
 
-// Pack two floats into one dword of two bf16 (lo in the low half).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Pack two floats into one dword of two bf16 (lo in the low half), round to
+// nearest even: a single v_cvt_pk_bf16_f32 on gfx950.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {

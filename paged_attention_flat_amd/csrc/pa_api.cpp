@@ -43,12 +43,18 @@ void destroy_events(TraceState& t) {
 }
 
 int32_t device_cu_count() {
+  static std::atomic<int32_t> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev >= 0 && dev < 64) {
+    const int32_t c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       cus <= 0)
     return 256;
+  if (dev >= 0 && dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
   return cus;
 }
 
@@ -65,18 +71,37 @@ size_t plan_capacity(int32_t num_seqs, int32_t num_tokens) {
   return by_tokens + reqs;
 }
 
-size_t workspace_bytes_for(int32_t num_seqs, int32_t num_tokens, int32_t hq, int32_t d,
-                           int32_t splits) {
-  size_t bytes = 256 + (1 + 2 * plan_capacity(num_seqs, num_tokens)) * sizeof(int32_t);
-  bytes = (bytes + 255) & ~size_t(255);
+// Workspace layout (each region 256-byte aligned):
+//   [plan: 1 + 2 * cap ints][plan_tmp: 2 * cap ints][decode order: 1 + num_seqs ints]
+//   [partial out: splits * nt * hq * d floats][partial lse: splits * nt * hq floats]
+struct WsLayout {
+  size_t plan, plan_tmp, order, part_out, part_lse, total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+WsLayout ws_layout(int32_t num_seqs, int32_t num_tokens, int32_t hq, int32_t d, int32_t splits) {
+  WsLayout w;
+  const size_t cap = plan_capacity(num_seqs, num_tokens);
+  w.plan = 0;
+  w.plan_tmp = align256(w.plan + (1 + 2 * cap) * sizeof(int32_t));
+  w.order = align256(w.plan_tmp + 2 * cap * sizeof(int32_t));
+  w.part_out = align256(w.order + (1 + (size_t)num_seqs) * sizeof(int32_t));
+  w.part_lse = w.part_out;
+  w.total = w.part_out;
   if (splits > 1) {
     const size_t rows = (size_t)splits * num_tokens * hq;
-    bytes += rows * d * sizeof(float);
-    bytes = (bytes + 255) & ~size_t(255);
-    bytes += rows * sizeof(float);
+    w.part_lse = align256(w.part_out + rows * d * sizeof(float));
+    w.total = align256(w.part_lse + rows * sizeof(float));
   }
-  return bytes;
+  return w;
 }
+
+size_t workspace_bytes_for(int32_t num_seqs, int32_t num_tokens, int32_t hq, int32_t d,
+                           int32_t splits) {
+  return ws_layout(num_seqs, num_tokens, hq, d, splits).total;
+}
+
 
 }  // namespace
 
@@ -128,6 +153,7 @@ const char* pa_kernel_name(int32_t id) {
     case K_PREFILL: return "prefill_mfma";
     case K_F32_ATTN: return "attn_f32";
     case K_F32_ATTN_SPLIT: return "attn_f32_split_partial";
+    case K_DECODE_ORDER: return "decode_order";
   }
   return "unknown";
 }
@@ -243,7 +269,8 @@ pa_status pa_attention_fwd(const void* query, const void* key_cache, const void*
                            int32_t num_splits, void* out, float* lse, void* workspace,
                            size_t workspace_bytes, pa_dtype dtype, void* stream) {
   if (num_seqs < 0 || num_tokens < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
-      num_blocks <= 0 || num_splits < 0 || num_splits > PA_MAX_SPLITS || !std::isfinite(scale))
+      num_blocks <= 0 || num_splits < 0 || num_splits > PA_MAX_SPLITS || !std::isfinite(scale) ||
+      !(scale > 0.f))
     return PA_ERR_INVALID;
   if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_INVALID;
   if (num_q_heads % num_kv_heads != 0) return PA_ERR_INVALID;
@@ -289,7 +316,9 @@ pa_status pa_attention_fwd(const void* query, const void* key_cache, const void*
   a.out = out;
   a.lse = lse;
   char* ws = static_cast<char*>(workspace);
-  a.plan = reinterpret_cast<int32_t*>(ws + 256);
+  const WsLayout lay = ws_layout(num_seqs, num_tokens, num_q_heads, head_dim, splits);
+  a.plan = reinterpret_cast<int32_t*>(ws + lay.plan);
+  a.plan_tmp = reinterpret_cast<int32_t*>(ws + lay.plan_tmp);
   {
     // tighter bound for this group size (the workspace holds the loosest one)
     const int64_t tq = prefill_tile_tokens(group), dq = decode_max_q(group);
@@ -297,16 +326,16 @@ pa_status pa_attention_fwd(const void* query, const void* key_cache, const void*
                         std::min<int64_t>(num_seqs, num_tokens / (dq + 1) + 1);
     a.plan_cap = (int32_t)std::min<int64_t>(cap, (int64_t)plan_capacity(num_seqs, num_tokens));
   }
-  size_t off = 256 + (1 + 2 * plan_capacity(num_seqs, num_tokens)) * sizeof(int32_t);
-  off = (off + 255) & ~size_t(255);
+  // rank decode requests longest-first when they outnumber the compute units
+  a.num_cus = device_cu_count();
+  a.decode_order = nullptr;
+  if ((int64_t)num_seqs * num_kv_heads * splits > a.num_cus && num_seqs >= 64)
+    a.decode_order = reinterpret_cast<int32_t*>(ws + lay.order);
   a.part_out = nullptr;
   a.part_lse = nullptr;
   if (splits > 1) {
-    const size_t rows = (size_t)splits * num_tokens * num_q_heads;
-    a.part_out = reinterpret_cast<float*>(ws + off);
-    off += rows * head_dim * sizeof(float);
-    off = (off + 255) & ~size_t(255);
-    a.part_lse = reinterpret_cast<float*>(ws + off);
+    a.part_out = reinterpret_cast<float*>(ws + lay.part_out);
+    a.part_lse = reinterpret_cast<float*>(ws + lay.part_lse);
   }
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipSuccess;

@@ -17,7 +17,8 @@ enum KernelId : int32_t {
   K_PREFILL = 5,
   K_F32_ATTN = 6,
   K_F32_ATTN_SPLIT = 7,
-  K_COUNT = 8
+  K_DECODE_ORDER = 8,
+  K_COUNT = 9
 };
 
 // Tracing hooks (pa_api.cpp).  trace_before/after bracket one launch.
@@ -44,14 +45,21 @@ struct AttnArgs {
   float* lse;
   float* part_out;      // [splits][nt][hq][d] when splits > 1
   float* part_lse;      // [splits][nt][hq]
-  int32_t* plan;        // work list of the matrix-core kernel
+  int32_t* plan;        // work list of the matrix-core kernel: count + 2 ints/item
+  int32_t* plan_tmp;    // unsorted work list (2 ints/item)
   int32_t plan_cap;     // capacity of the work list (items)
+  int32_t* decode_order;  // nullable: count + ranked decode requests
+  int32_t num_cus;        // compute units of the current device
 };
 
 // Largest number of new tokens per request that the decode kernel packs.
 inline int32_t decode_max_q(int32_t group) { return 16 / group; }
+// Waves per work-group of the prefill kernel (each owns 32 query rows).
+#ifndef PA_PREFILL_WAVES
+#define PA_PREFILL_WAVES 8
+#endif
 // Query tokens per work-group of the prefill kernel.
-inline int32_t prefill_tile_tokens(int32_t group) { return 128 / group; }
+inline int32_t prefill_tile_tokens(int32_t group) { return 32 * PA_PREFILL_WAVES / group; }
 
 hipError_t launch_decode_bf16(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t stream);

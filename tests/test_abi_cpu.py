@@ -76,6 +76,8 @@ def test_attention_validation(lib):
     assert _fwd(lib, splits=-1) == 2
     assert _fwd(lib, splits=257) == 2
     assert _fwd(lib, scale=float("nan")) == 2
+    assert _fwd(lib, scale=0.0) == 2
+    assert _fwd(lib, scale=-0.5) == 2
     assert _fwd(lib, dtype=5) == 2
     assert _fwd(lib, mq=4) == 2                       # max_query_len > num_tokens
     assert _fwd(lib, ms=1) == 2                       # max_seq_len < max_query_len

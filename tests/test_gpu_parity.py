@@ -356,3 +356,27 @@ def test_full_config5():
     sharer = [int(b) for b in dec if int(step.block_tables[b, 0]) in shared][:3]
     ids = sorted(set(prefill + dec[np.argsort(sl)[-3:]].tolist() + dec[:6].tolist() + sharer))
     sampled_parity(step, ids, rows_per_req=12, seed=5)
+
+
+def test_bf16_rounding_matches_torch_rne():
+    # a single split passes o_0 through unchanged (weight 1), so the bf16
+    # output is exactly the kernel's fp32 -> bf16 rounding of o_0
+    pa = pa_mod()
+    rng = np.random.default_rng(17)
+    po = (rng.standard_normal((1, 64, 8, 128)) * 7).astype(np.float32)
+    # values that sit exactly on rounding ties and next to them
+    # (the sum over splits starts from +0, so a -0 input or a subnormal would
+    # test the accumulation, not the rounding: none are used)
+    po[0, 0, 0, :8] = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 2 ** -120,
+                                65504.5, 3.4e38, 1 + 5 * 2 ** -9, 1 + 2 ** -9], dtype=np.float32)
+    pl = np.zeros((1, 64, 8), dtype=np.float32)
+    out, lse = pa.split_combine(torch.from_numpy(po).cuda(), torch.from_numpy(pl).cuda(),
+                                dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ref = torch.from_numpy(po[0]).to(torch.bfloat16)
+    got = out.cpu().view(torch.int16).numpy()
+    want = ref.view(torch.int16).numpy()
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, [(tuple(i), float(po[0][tuple(i)]), hex(got[tuple(i)] & 0xffff),
+                            hex(want[tuple(i)] & 0xffff)) for i in bad[:8]]
+    assert np.all(lse.cpu().numpy() == 0.0)
