@@ -54,12 +54,18 @@ struct AttnArgs {
 
 // Largest number of new tokens per request that the decode kernel packs.
 inline int32_t decode_max_q(int32_t group) { return 16 / group; }
-// Waves per work-group of the prefill kernel (each owns 32 query rows).
+// Prefill work-group shape: PA_PREFILL_WAVES waves, each owning
+// PA_PREFILL_ROW_GROUPS groups of 32 query rows.
 #ifndef PA_PREFILL_WAVES
 #define PA_PREFILL_WAVES 8
 #endif
+#ifndef PA_PREFILL_ROW_GROUPS
+#define PA_PREFILL_ROW_GROUPS 1
+#endif
 // Query tokens per work-group of the prefill kernel.
-inline int32_t prefill_tile_tokens(int32_t group) { return 32 * PA_PREFILL_WAVES / group; }
+inline int32_t prefill_tile_tokens(int32_t group) {
+  return 32 * PA_PREFILL_ROW_GROUPS * PA_PREFILL_WAVES / group;
+}
 
 hipError_t launch_decode_bf16(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t stream);

@@ -138,27 +138,32 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   if (tid == 0) plan[0] = count;
 }
 
-constexpr int kBK = 64;     // keys per tile
 constexpr int kKPad = 8;    // bf16 padding per K row in LDS
 constexpr int kVPad = 8;    // bf16 padding per V^T row in LDS
 constexpr float kLazy = 8.f;  // base-2 headroom before the running max moves
 constexpr int kTabWin = 512;  // block-table entries held in LDS (8192 keys)
+#ifndef PA_PREFILL_KEYS
+#define PA_PREFILL_KEYS 64    // keys per K/V tile
+#endif
 
 // position of key k (0..15) of a 16-key group in the V^T tile
 __device__ __forceinline__ int vperm(int k) {
   return (k & 3) | ((k & 4) << 1) | ((k & 8) >> 1);
 }
 
-template <int D, int G, int NW>
-__global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 1)) void prefill_kernel(PrefillParams p) {
-  constexpr int NT = 64 * NW;         // threads
-  constexpr int TQ = 32 * NW / G;     // tokens per work-group
-  constexpr int QSTEPS = D / 16;      // MFMA k-steps over head_dim
-  constexpr int DB = D / 32;          // 32-row blocks of O^T
-  constexpr int KCH = kBK * D / 8 / NT;  // 16-byte K chunks per thread per tile
-  constexpr int VCH = D * kBK / 8 / NT;  // 16-byte V chunks per thread per tile
+template <int D, int G, int NW, int RG, int kBK>
+__global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
+  constexpr int KB = kBK / 32;            // 32-key halves per tile
+  constexpr int PS = kBK / 16;            // 16-key P.V steps per tile
+  constexpr int NT = 64 * NW;             // threads
+  constexpr int WROWS = 32 * RG;          // query rows per wave
+  constexpr int TQ = WROWS * NW / G;      // tokens per work-group
+  constexpr int QSTEPS = D / 16;          // MFMA k-steps over head_dim
+  constexpr int DB = D / 32;              // 32-row blocks of O^T
+  constexpr int KCH = kBK * D / 8 / NT;   // 16-byte K chunks per thread per tile
+  constexpr int VCH = D * kBK / 8 / NT;   // 16-byte V chunks per thread per tile
   __shared__ __align__(16) uint16_t sK[2][kBK][D + kKPad];
-  __shared__ __align__(16) uint16_t sV[2][D][kBK + kVPad];
+  __shared__ __align__(16) uint16_t sV[3][D][kBK + kVPad];
   __shared__ int s_tab[kTabWin];
 
   const int kvh = blockIdx.x % p.hkv;
@@ -176,24 +181,34 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 1)) void prefill_kernel(Pre
   const int ctx = seq_len - q_len;
   const int tok0 = tile * TQ;
 
-  const int r = 32 * wave + row;
-  const int tq = r / G, g = r - (r / G) * G;
-  const int tok = tok0 + tq;
-  const bool row_valid = tok < q_len;
-  const int pos = ctx + min(tok, q_len - 1);
-  const int wpos_lo = ctx + min(tok0 + (32 * wave) / G, q_len - 1);
-  const int wpos_hi = ctx + min(tok0 + (32 * wave + 31) / G, q_len - 1);
+  // row group rg of this wave: work-group rows WROWS*wave + 32*rg + row,
+  // token-major over the G query heads of the KV head
+  int tokr[RG], gr[RG], pos[RG];
+  bool valid[RG];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) {
+    const int r = WROWS * wave + 32 * rg + row;
+    tokr[rg] = tok0 + r / G;
+    gr[rg] = r - (r / G) * G;
+    valid[rg] = tokr[rg] < q_len;
+    pos[rg] = ctx + min(tokr[rg], q_len - 1);
+  }
+  const int wpos_lo = ctx + min(tok0 + (WROWS * wave) / G, q_len - 1);
   const int kend = ctx + min(tok0 + TQ, q_len);  // one past the last visible key
 
-  bf16x8 qf[QSTEPS];
-  if (row_valid) {
-    const uint16_t* qrow = p.q + ((size_t)(q0 + tok) * p.hq + kvh * G + g) * D + 8 * kg;
+  bf16x8 qf[RG][QSTEPS];
 #pragma unroll
-    for (int st = 0; st < QSTEPS; ++st)
-      qf[st] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 16 * st));
-  } else {
+  for (int rg = 0; rg < RG; ++rg) {
+    if (valid[rg]) {
+      const uint16_t* qrow =
+          p.q + ((size_t)(q0 + tokr[rg]) * p.hq + kvh * G + gr[rg]) * D + 8 * kg;
 #pragma unroll
-    for (int st = 0; st < QSTEPS; ++st) qf[st] = as_bf16x8(make_uint4(0, 0, 0, 0));
+      for (int st = 0; st < QSTEPS; ++st)
+        qf[rg][st] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 16 * st));
+    } else {
+#pragma unroll
+      for (int st = 0; st < QSTEPS; ++st) qf[rg][st] = as_bf16x8(make_uint4(0, 0, 0, 0));
+    }
   }
 
   const int32_t* table = p.tables + (size_t)b * p.table_stride;
@@ -271,9 +286,9 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 1)) void prefill_kernel(Pre
       vr[i] = v;
     }
   };
-  auto lstore = [&](int buf) {
-    uint16_t* k_lds = &sK[buf][0][0];
-    uint16_t* v_lds = &sV[buf][0][0];
+  auto lstore = [&](int kbuf, int vbuf) {
+    uint16_t* k_lds = &sK[kbuf][0][0];
+    uint16_t* v_lds = &sV[vbuf][0][0];
 #pragma unroll
     for (int i = 0; i < KCH; ++i) *reinterpret_cast<uint4*>(k_lds + k_dst[i]) = kr[i];
 #pragma unroll
@@ -286,12 +301,20 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 1)) void prefill_kernel(Pre
     }
   };
 
-  float m = -INFINITY, l = 0.f;
-  f32x16 acc[DB];
+  float m[RG], l[RG], alpha[RG];
+  bool rescale[RG];
+  f32x16 acc[RG][DB];
 #pragma unroll
-  for (int i = 0; i < DB; ++i)
+  for (int rg = 0; rg < RG; ++rg) {
+    m[rg] = -INFINITY;
+    l[rg] = 0.f;
+    alpha[rg] = 1.f;
+    rescale[rg] = false;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) acc[i][j] = 0.f;
+    for (int i = 0; i < DB; ++i)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[rg][i][j] = 0.f;
+  }
 
   // block-table window: entries [tab_base, tab_base + kTabWin) live in LDS.
   // It covers every block of the request: a 64-key tile can reach past the
@@ -304,11 +327,54 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 1)) void prefill_kernel(Pre
   load_tab(0);
   __syncthreads();
   gload(0);
-  lstore(0);
+  lstore(0, 0);
   __syncthreads();
-  int buf = 0;
-  for (int k0 = 0; k0 < kend; k0 += kBK) {
+
+  // O^T += V^T P^T over a tile: four 16-key steps; each V^T fragment read
+  // from LDS feeds the MFMAs of every row group of the wave
+  auto pv = [&](int vbuf, const bf16x8 (&pf)[RG][PS]) {
+#pragma unroll
+    for (int ps = 0; ps < PS; ++ps) {
+      const int base = 16 * ps + 8 * kg;
+      uint4 fv[DB];
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        fv[db] = *reinterpret_cast<const uint4*>(&sV[vbuf][32 * db + row][base]);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg)
+          acc[rg][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fv[db]), pf[rg][ps],
+                                                                acc[rg][db], 0, 0, 0);
+    }
+  };
+
+  // Software pipeline per wave: iteration `it` computes S of tile it, then
+  // issues the P.V products of tile it-1 (P kept in registers, V^T still in
+  // its LDS buffer) in the same basic block as the softmax of tile it, so the
+  // MFMAs run while the exponentials issue.  K is double-buffered in LDS, V
+  // triple-buffered (tile it-1 is still read while tile it+1 is stored).
+  // Tiles past a row's position are computed anyway (masked: P = 0), which
+  // keeps the loop body branch-free.  Before the first tile, P = 0 against
+  // the finite V^T of tile 0.
+  bf16x8 pprev[RG][PS];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+    for (int ps = 0; ps < PS; ++ps) pprev[rg][ps] = as_bf16x8(make_uint4(0, 0, 0, 0));
+  int vprev = 0;
+  int it = 0;
+  for (int k0 = 0; k0 < kend; k0 += kBK, ++it) {
+    const int kbuf = it & 1, vbuf = it % 3;
     const bool more = k0 + kBK < kend;
+    // a moved max of the previous tile: acc now holds every P.V up to two
+    // tiles back, accumulated at the old max
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+      if (rescale[rg]) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[rg][db] *= alpha[rg];
+      }
     if (more && ((k0 + kBK) >> 4) >= tab_base + kTabWin) {
       // the next tile starts a new window (tiles never straddle one); every
       // thread is past its last use of the old entries
@@ -317,110 +383,137 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 1)) void prefill_kernel(Pre
       __syncthreads();
     }
     if (more) gload(k0 + kBK);
-    if (k0 <= wpos_hi) {
-      // ---- S^T = K Q^T over two 32-key halves --------------------------------
-      f32x16 s[2];
+    // ---- S^T = K Q^T: every K fragment feeds all row groups ------------------
+    f32x16 s[RG][KB];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) s[kb][j] = 0.f;
-      const uint16_t* k_row0 = &sK[buf][row][8 * kg];
-      const uint16_t* k_row1 = &sK[buf][32 + row][8 * kg];
-      // two independent accumulation chains, operands fetched 4 steps ahead
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int s0 = 0; s0 < QSTEPS; s0 += 4) {
-        uint4 fa[4], fb[4];
+        for (int j = 0; j < 16; ++j) s[rg][kb][j] = 0.f;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          fa[u] = *reinterpret_cast<const uint4*>(k_row0 + 16 * (s0 + u));
-          fb[u] = *reinterpret_cast<const uint4*>(k_row1 + 16 * (s0 + u));
-        }
+    for (int s0 = 0; s0 < QSTEPS; s0 += 4) {
+      uint4 fk[KB][4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa[u]), qf[s0 + u], s[0], 0, 0, 0);
-          s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fb[u]), qf[s0 + u], s[1], 0, 0, 0);
-        }
-      }
-      if (k0 + kBK - 1 > wpos_lo) {
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int u = 0; u < 4; ++u)
+          fk[kb][u] = *reinterpret_cast<const uint4*>(&sK[kbuf][32 * kb + row][8 * kg + 16 * (s0 + u)]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int rg = 0; rg < RG; ++rg)
+            s[rg][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fk[kb][u]), qf[rg][s0 + u],
+                                                                s[rg][kb], 0, 0, 0);
+    }
+    if (k0 + kBK - 1 > wpos_lo) {
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const int key = k0 + 32 * kb + 8 * i + 4 * kg + j;
-              if (key > pos) s[kb][4 * i + j] = -INFINITY;
+              if (key > pos[rg]) s[rg][kb][4 * i + j] = -INFINITY;
             }
+    }
+    float m_new[RG];
+    bool move[RG];
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) {
+      // row max as a tree (short dependence chains)
+      float mx[4 * KB];
+#pragma unroll
+      for (int u = 0; u < 4 * KB; ++u) {
+        const f32x16& sv = s[rg][u >> 2];
+        const int o = 4 * (u & 3);
+        mx[u] = fmaxf(fmaxf(sv[o], sv[o + 1]), fmaxf(sv[o + 2], sv[o + 3]));
       }
-      float mt = s[0][0];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int w = 4 * KB; w > 1; w >>= 1)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) mt = fmaxf(mt, s[kb][j]);
+        for (int u = 0; u < w / 2; ++u) mx[u] = fmaxf(mx[u], mx[u + w / 2]);
+      float mt = mx[0];
       mt = fmaxf(mt, shfl_xor(mt, 32)) * p.scale_log2;  // scale > 0 commutes with max
-      if (__ballot(mt > m + kLazy) != 0) {
-        const float m_new = fmaxf(m, mt);  // finite: key 0 is in the first tile
-        const float alpha = fast_exp2(m - m_new);
-        l *= alpha;
+      move[rg] = __ballot(mt > m[rg] + kLazy) != 0;
+      // finite once the wave has met key 0, which every row sees
+      m_new[rg] = move[rg] ? fmaxf(m[rg], mt) : m[rg];
+    }
+
+    // ---- P.V of the previous tile, interleaved with this tile's softmax -----
+    pv(vprev, pprev);
 #pragma unroll
-        for (int db = 0; db < DB; ++db) acc[db] *= alpha;
-        m = m_new;
-      }
-      float rs = 0.f;
+    for (int rg = 0; rg < RG; ++rg) {
+      float ps4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          s[kb][j] = fast_exp2(__builtin_fmaf(s[kb][j], p.scale_log2, -m));
-          rs += s[kb][j];
+          s[rg][kb][j] = fast_exp2(__builtin_fmaf(s[rg][kb][j], p.scale_log2, -m_new[rg]));
+          ps4[j & 3] += s[rg][kb][j];
         }
-      l += rs;
-
-      // ---- O^T += V^T P^T, four 16-key steps ----------------------------------
+      const float rs = (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
 #pragma unroll
-      for (int ps = 0; ps < 4; ++ps) {
-        const int kb = ps >> 1, ih = ps & 1;
-        const f32x16& sp = s[kb];
-        const bf16x8 pf = as_bf16x8(make_uint4(
-            pack_bf16x2(sp[8 * ih + 0], sp[8 * ih + 1]), pack_bf16x2(sp[8 * ih + 2], sp[8 * ih + 3]),
-            pack_bf16x2(sp[8 * ih + 4], sp[8 * ih + 5]), pack_bf16x2(sp[8 * ih + 6], sp[8 * ih + 7])));
-        const int base = 32 * kb + 16 * ih + 8 * kg;
-        uint4 fv[DB];
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-          fv[db] = *reinterpret_cast<const uint4*>(&sV[buf][32 * db + row][base]);
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fv[db]), pf, acc[db], 0, 0, 0);
+      for (int ps = 0; ps < PS; ++ps) {
+        const f32x16& sp = s[rg][ps >> 1];
+        const int o = 8 * (ps & 1);
+        pprev[rg][ps] = as_bf16x8(make_uint4(
+            pack_bf16x2(sp[o + 0], sp[o + 1]), pack_bf16x2(sp[o + 2], sp[o + 3]),
+            pack_bf16x2(sp[o + 4], sp[o + 5]), pack_bf16x2(sp[o + 6], sp[o + 7])));
       }
+      // a moved max rescales l now and acc at the top of the next iteration,
+      // after the previous tile's P.V (accumulated at the old max) is in
+      alpha[rg] = fast_exp2(m[rg] - m_new[rg]);  // 1 when the max stays
+      rescale[rg] = move[rg];
+      l[rg] = l[rg] * alpha[rg] + rs;
+      m[rg] = m_new[rg];
     }
-    if (more) lstore(buf ^ 1);
+    vprev = vbuf;
+    // unconditional: after the last tile it stores stale registers into
+    // buffers nothing reads again (keeps the loop body one basic block)
+    lstore(kbuf ^ 1, (it + 1) % 3);
     __syncthreads();
-    buf ^= 1;
   }
-
-  l += shfl_xor(l, 32);
-  if (!row_valid) return;
-  const float inv = 1.f / l;
-  const int t = q0 + tok;
-  const int h = kvh * G + g;
-  uint16_t* orow = p.out + ((size_t)t * p.hq + h) * D;
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int rg = 0; rg < RG; ++rg)
+    if (rescale[rg]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int d = 32 * db + 8 * i + 4 * kg;
-      const f32x16& a = acc[db];
-      *reinterpret_cast<uint2*>(orow + d) =
-          make_uint2(pack_bf16x2(a[4 * i] * inv, a[4 * i + 1] * inv),
-                     pack_bf16x2(a[4 * i + 2] * inv, a[4 * i + 3] * inv));
+      for (int db = 0; db < DB; ++db) acc[rg][db] *= alpha[rg];
     }
-  if (p.lse != nullptr && kg == 0) p.lse[(size_t)t * p.hq + h] = (m + fast_log2(l)) * kLn2;
+  pv(vprev, pprev);
+
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) {
+    const float lt = l[rg] + shfl_xor(l[rg], 32);
+    if (!valid[rg]) continue;
+    const float inv = 1.f / lt;
+    const int t = q0 + tokr[rg];
+    const int h = kvh * G + gr[rg];
+    uint16_t* orow = p.out + ((size_t)t * p.hq + h) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d = 32 * db + 8 * i + 4 * kg;
+        const f32x16& a = acc[rg][db];
+        *reinterpret_cast<uint2*>(orow + d) =
+            make_uint2(pack_bf16x2(a[4 * i] * inv, a[4 * i + 1] * inv),
+                       pack_bf16x2(a[4 * i + 2] * inv, a[4 * i + 3] * inv));
+      }
+    if (p.lse != nullptr && kg == 0)
+      p.lse[(size_t)t * p.hq + h] = (m[rg] + fast_log2(lt)) * kLn2;
+  }
 }
 
 template <int D, int G>
 void launch_dg(const AttnArgs& a, hipStream_t stream) {
   constexpr int NW = PA_PREFILL_WAVES;
+  constexpr int RG = PA_PREFILL_ROW_GROUPS;
+  constexpr int BK = PA_PREFILL_KEYS;
   PrefillParams p;
   p.q = (const uint16_t*)a.q;
   p.kc = (const uint16_t*)a.kc;
@@ -443,7 +536,7 @@ void launch_dg(const AttnArgs& a, hipStream_t stream) {
                      a.plan_cap);
   trace_after(stream);
   trace_before(K_PREFILL, stream);
-  hipLaunchKernelGGL((prefill_kernel<D, G, NW>), dim3(a.plan_cap * a.hkv), dim3(64 * NW), 0,
+  hipLaunchKernelGGL((prefill_kernel<D, G, NW, RG, BK>), dim3(a.plan_cap * a.hkv), dim3(64 * NW), 0,
                      stream, p);
   trace_after(stream);
 }
