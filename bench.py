@@ -4,15 +4,17 @@
 A step is the whole hot path over one batch of synthetic input: the KV write
 of the step's new tokens through slot_mapping, then causal attention of
 every scheduled row through the block tables (decode kernel with split-KV
-partials + combine, and/or the matrix-core prefill kernel).
+partials merged by the last split to finish, and/or the matrix-core prefill
+kernel).
 
 Headline workload: long-context single decode (1 request, 1 new token,
 context 32768, 32 query / 8 KV heads, head_dim 128, bf16, 16-token blocks
 scattered over a 4096-block pool).  value = algorithmic HBM bytes of a step /
 wall time per step (GB/s).  Eight replicas of the inputs (separate pools)
 are cycled so that no step finds its 128 MiB of K/V in the 256 MiB Infinity
-Cache left by the previous one.  Steps are replayed from HIP graphs (one per
-replica) so the host launch path is not what is measured.
+Cache left by the previous one.  Steps are replayed from HIP graphs (one
+graph holds one step on each replica in turn) so the host launch path is not
+what is measured.
 
 Also reported, in the same JSON line: the dominant kernel against its
 roofline (durations from HIP events on the kernel's own stream, GPU kept
@@ -38,7 +40,7 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
 
 WORKLOAD_NAMES = {
-    2: "long-context single decode (B=1, context 32768, Hq 32/Hkv 8, d 128, bf16, 64 splits)",
+    2: "long-context single decode (B=1, context 32768, Hq 32/Hkv 8, d 128, bf16, 32 splits)",
     3: "large-batch decode (B=256, contexts U[512,8192], Hq 32/Hkv 8, d 128, bf16, no split)",
     4: "long prefill (4 x 8192 new tokens, causal, Hq 32/Hkv 8, d 128, bf16)",
     5: "mixed chunked-prefill step (2 x 2048-token chunks + 4096 decodes, 25% shared "
@@ -183,8 +185,8 @@ class StepRunner:
             step.num_seqs, step.max_query_len, step.max_seq_len, hq, hkv)
         g["out"] = torch.empty_like(g["query"])
         g["lse"] = torch.empty(nt, hq, dtype=torch.float32, device=dev)
-        ws = pa.workspace_size(step.num_seqs, nt, hq, d, self.splits)
-        g["ws"] = torch.empty(ws, dtype=torch.uint8, device=dev)
+        g["ws"] = pa.workspace(step.num_seqs, nt, hq, d, self.splits, device=dev)
+        ws = g["ws"].numel()
         self.g = g
         code = _lib.PA_BF16 if step.dtype == "bf16" else _lib.PA_F32
         P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
@@ -219,13 +221,16 @@ def busy_gpu(ms):
             a = a / a.abs().max()
 
 
-def time_steps(runners, steps, warmup, use_graph, log):
+def time_steps(runners, steps, warmup, use_graph, log, per_graph=1):
     """Wall time of exactly `steps` steps (replicas cycled), bracketed by
-    device synchronisation.  Returns (ms_per_step, launch_mode)."""
+    device synchronisation.  With graphs, `per_graph` consecutive steps (one
+    per replica, in order) are captured into one graph; a remainder of steps
+    runs from one-step graphs.  Returns (ms_per_step, launch_mode)."""
     import torch
     R = len(runners)
     mode = "eager"
     graphs = None
+    per_graph = max(1, min(per_graph, R)) if use_graph else 1
     if use_graph:
         try:
             side = torch.cuda.Stream()
@@ -241,18 +246,37 @@ def time_steps(runners, steps, warmup, use_graph, log):
                 with torch.cuda.graph(gr):
                     r()
                 graphs.append(gr)
+            chunks = []
+            if per_graph > 1:
+                for c0 in range(0, R - per_graph + 1, per_graph):
+                    gr = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(gr):
+                        for r in runners[c0:c0 + per_graph]:
+                            r()
+                    chunks.append(gr)
             torch.cuda.synchronize()
-            mode = "hip-graph"
+            mode = "hip-graph" if per_graph == 1 else f"hip-graph x{per_graph}"
         except Exception as e:  # capture unsupported: fall back, say so
             log(f"graph capture failed ({e!r}); timing eager launches")
             graphs = None
+            per_graph = 1
     launch = [g.replay for g in graphs] if graphs else list(runners)
-    for i in range(warmup):
-        launch[i % R]()
+
+    def run(n):
+        i = 0
+        if per_graph > 1:
+            nc = len(chunks)
+            while n - i >= per_graph:
+                chunks[(i // per_graph) % nc].replay()
+                i += per_graph
+        while i < n:
+            launch[i % R]()
+            i += 1
+
+    run(warmup)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(steps):
-        launch[i % R]()
+    run(steps)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     return (t1 - t0) * 1e3 / steps, mode
@@ -302,7 +326,9 @@ def bench_main(args, log):
         vc = step.v_pool.to(dev).clone()
         runners.append(StepRunner(step, dev, base.splits, pools=(kc, vc)))
     wm = work_model(step)
-    ms, mode = time_steps(runners, args.steps, args.warmup, not args.eager, log)
+    # one graph holds one step on each replica in turn (R steps per replay)
+    ms, mode = time_steps(runners, args.steps, args.warmup, not args.eager, log,
+                          per_graph=len(runners))
     kt = kernel_times(runners, min(args.steps, 200), log)
     kbytes, ktoks = decode_kernel_bytes(step)
     dom = "decode_split_partial" if base.splits > 1 else "decode"

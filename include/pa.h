@@ -81,10 +81,11 @@ typedef enum pa_dtype {
  * For every t < num_tokens with s = slot_mapping[t] >= 0, and every KV head h:
  *   key_cache  [s / bs][h][s % bs][:] = key  [t][h][:]
  *   value_cache[s / bs][h][:][s % bs] = value[t][h][:]
- * A negative slot marks a padded token: nothing is written for it.  The copy
- * is bit-exact (cache dtype = input dtype, nothing converts) and no other
- * cache entry changes.  Slots must be distinct and < num_blocks * bs
- * (unchecked).
+ * A negative slot marks a padded token: nothing is written for it; a slot at
+ * or past num_blocks * bs is dropped the same way (the pool is never written
+ * out of bounds).  The copy is bit-exact (cache dtype = input dtype, nothing
+ * converts) and no other cache entry changes.  Slots must be distinct
+ * (unchecked; with duplicates the surviving row is unspecified).
  *
  * Supported: head_dim in {64, 128}, block_size == 16, num_kv_heads >= 1.
  * num_tokens == 0 is a no-op (pointers may then be NULL).
@@ -116,7 +117,9 @@ pa_status pa_kv_write(const void* key, const void* value,
  * bandwidth-bound kernel; with num_splits > 1 their key range is cut into
  * num_splits block ranges whose partial results are merged by a second
  * reduction (the split-KV method of "Prefill has a full grid; decode at batch
- * 1 has almost none").  Rows of requests with many new tokens run the tiled
+ * 1 has almost none"): in bf16 mode the last split of each request and KV
+ * head to finish performs it inside the same launch, in fp32 mode a separate
+ * combine kernel does.  Rows of requests with many new tokens run the tiled
  * matrix-core kernel.  num_splits: 0 = pa_choose_num_splits() for these
  * scalars, 1 = no split, 2..PA_MAX_SPLITS = forced.  The result does not
  * depend on num_splits beyond rounding.
@@ -129,8 +132,12 @@ pa_status pa_kv_write(const void* key, const void* value,
  *
  * workspace: device scratch of at least pa_attention_workspace_size(num_seqs,
  * num_tokens, num_q_heads, head_dim, S) bytes, S the split count in use
- * (resolve num_splits = 0 with pa_choose_num_splits first).  It may be NULL
- * when that size is 0.  Its contents on entry do not matter.
+ * (resolve num_splits = 0 with pa_choose_num_splits first), 16-byte aligned.
+ * Its first num_seqs * num_q_heads int32 are arrival counters of the split
+ * merge: they must be zero before the first call (pa_attention_workspace_init
+ * or any zero-filled allocation) and every call leaves them zero.  The rest
+ * of the workspace needs no initialisation.  Calls that share a workspace
+ * must not overlap in time (use one stream, or one workspace per stream).
  *
  * Supported: dtype PA_BF16 or PA_F32, head_dim in {64, 128}, block_size 16,
  * num_q_heads % num_kv_heads == 0 with group size in {1, 2, 4, 8, 16}.
@@ -149,6 +156,13 @@ pa_status pa_attention_fwd(const void* query,
                            void* out, float* lse,
                            void* workspace, size_t workspace_bytes,
                            pa_dtype dtype, void* stream);
+
+/*
+ * pa_attention_workspace_init -- zero `workspace_bytes` of a workspace on
+ * `stream` with a kernel (no memset node, so it may be captured in a HIP
+ * graph).  Needed once for a new workspace whose memory is not already zero.
+ */
+pa_status pa_attention_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * pa_split_combine -- merge split-KV partials ("Prefill has a full grid;

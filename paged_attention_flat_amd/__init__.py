@@ -22,7 +22,7 @@ from ._lib import LIB, PA_BF16, PA_F32, PA_BLOCK_SIZE, PA_MAX_SPLITS  # noqa: F4
 
 __all__ = [
     "PaError", "kv_write", "attention", "split_combine", "workspace_size",
-    "choose_num_splits", "alloc_cache", "trace_begin", "trace_end", "trace_read",
+    "choose_num_splits", "alloc_cache", "workspace", "trace_begin", "trace_end", "trace_read",
     "kernel_name", "version",
 ]
 
@@ -134,7 +134,8 @@ def attention(query, key_cache, value_cache, query_start_loc, seq_lens, block_ta
         lse = torch.empty(nt, hq, dtype=torch.float32, device=query.device)
     need = workspace_size(ns, nt, hq, d, splits)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+        # zero-filled: the split-merge counters must start at zero
+        workspace = torch.zeros(need, dtype=torch.uint8, device=query.device)
     st = LIB.pa_attention_fwd(
         _dev(query, "query"), _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
         _dev(query_start_loc, "query_start_loc"), _dev(seq_lens, "seq_lens"),
@@ -163,6 +164,16 @@ def split_combine(partial_out, partial_lse, out=None, lse=None, dtype=torch.bflo
                               _dtype_code(out), _stream(stream))
     _check(st, "pa_split_combine")
     return out, lse
+
+
+def workspace(num_seqs: int, num_tokens: int, num_q_heads: int, head_dim: int,
+              num_splits: int, device="cuda", stream=None):
+    """A ready-to-use attention workspace (counters zeroed by the library)."""
+    n = workspace_size(num_seqs, num_tokens, num_q_heads, head_dim, num_splits)
+    ws = torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+    _check(LIB.pa_attention_workspace_init(_dev(ws, "workspace"), ws.numel(), _stream(stream)),
+           "pa_attention_workspace_init")
+    return ws
 
 
 def trace_begin(capacity: int = 4096) -> None:

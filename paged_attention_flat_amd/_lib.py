@@ -36,6 +36,7 @@ PROTOTYPES = {
     "pa_attention_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                 _i32, _i32, _i32, _i32, _i64, _f32, _i32, _vp, _vp, _vp, _sz,
                                 _i32, _vp]),
+    "pa_attention_workspace_init": (_i32, [_vp, _sz, _vp]),
     "pa_split_combine": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp]),
     "pa_attention_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "pa_choose_num_splits": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32]),
@@ -52,7 +53,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise ImportError(
             f"{path} is missing: build the HIP library first "
-            "(python -m paged_attention_flat_amd.build)")
+            "(python paged_attention_flat_amd/build.py)")
     lib = ctypes.CDLL(path)
     for name, (res, args) in PROTOTYPES.items():
         fn = getattr(lib, name)

@@ -1,7 +1,8 @@
 """Build libpa.so (the HIP kernels and the C ABI) in-tree for gfx950.
 
-Run as ``python -m paged_attention_flat_amd.build`` or through
-``__graft_entry__.build()``.  Compiles every time it is called.
+Run as ``python paged_attention_flat_amd/build.py`` or through
+``__graft_entry__.build()``.  Compiles every time it is called.  This file
+imports nothing from the package (whose import loads the built library).
 """
 
 from __future__ import annotations

@@ -119,7 +119,27 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   }
 }
 
+// Zero fill for workspace initialisation (a kernel rather than a memset, so a
+// captured HIP graph holds only kernel nodes).
+__global__ __launch_bounds__(256) void zero_kernel(uint4* __restrict__ p, size_t n16,
+                                                   uint8_t* __restrict__ tail, int ntail) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n16) p[i] = make_uint4(0, 0, 0, 0);
+  if (blockIdx.x == 0 && (int)threadIdx.x < ntail) tail[threadIdx.x] = 0;
+}
+
 }  // namespace
+
+hipError_t launch_zero(void* ptr, size_t bytes, hipStream_t stream) {
+  const size_t n16 = bytes / 16;
+  const int ntail = (int)(bytes - n16 * 16);
+  const size_t blocks = (n16 + 255) / 256;
+  trace_before(K_ZERO, stream);
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)(blocks > 0 ? blocks : 1)), dim3(256), 0, stream,
+                     (uint4*)ptr, n16, (uint8_t*)ptr + n16 * 16, ntail);
+  trace_after(stream);
+  return hipGetLastError();
+}
 
 hipError_t launch_combine(const float* po, const float* pl, int32_t splits, int32_t nt,
                           int32_t hq, int32_t d, void* out, float* lse, int32_t out_bf16,

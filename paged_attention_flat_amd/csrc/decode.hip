@@ -47,6 +47,8 @@ struct DecodeParams {
   const int32_t* tables;
   const int32_t* order;   // nullable: order[0] = count, order[1 + rank] = request
   int32_t num_seqs, hq, hkv, table_stride, splits, nt;
+  int32_t split_blocks;   // blocks per split (even), from max_seq_len
+  int32_t* sem;           // nullable: per (request, KV head) arrival counters
   float scale_log2;
   uint16_t* out;
   float* lse;
@@ -117,7 +119,8 @@ __global__ __launch_bounds__(1024) void decode_order_kernel(const int32_t* __res
 }
 
 template <int D, int G, int NW, int PIPE>
-__global__ __launch_bounds__(64 * NW, (PIPE == 2 ? 2 : 1)) void decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(64 * NW, (PIPE == 2 && NW < 8 ? 8 / NW : 1)) void decode_kernel(
+    DecodeParams p) {
   constexpr int DQ = 16 / G;       // new tokens per request packed in the columns
   constexpr int KSTEPS = D / 32;   // MFMA steps over head_dim for S^T
   constexpr int DB = D / 16;       // 16-row blocks of O^T
@@ -137,16 +140,24 @@ __global__ __launch_bounds__(64 * NW, (PIPE == 2 ? 2 : 1)) void decode_kernel(De
     if (rank >= p.order[0]) return;
     b = p.order[1 + rank];
   }
+  // Split s covers blocks [s * bps, (s + 1) * bps) of every request, bps from
+  // the host-known max_seq_len, so the first 64 block-table entries can be
+  // fetched together with query_start_loc / seq_lens (one round trip fewer
+  // before the first K/V load).  Splits past a shorter request are empty.
+  const int blk_lo = split * p.split_blocks;
+  const int32_t* table = p.tables + (size_t)b * p.table_stride;
+  int tab = 0, tab_base = 0;
+  {
+    const int j = blk_lo + lane;
+    tab = j < p.table_stride ? table[j] : 0;
+  }
   const int q0 = p.qsl[b];
   const int q_len = p.qsl[b + 1] - q0;
   if (q_len <= 0 || q_len > DQ) return;  // empty request or a prefill row set
   const int seq_len = p.seq_lens[b];
   const int ctx = seq_len - q_len;
   const int nblocks = (seq_len + 15) >> 4;
-  int bps = (nblocks + p.splits - 1) / p.splits;
-  bps = (bps + 1) & ~1;  // whole pairs per split
-  const int blk_lo = split * bps;
-  const int blk_hi = min(nblocks, blk_lo + bps);
+  const int blk_hi = min(nblocks, blk_lo + p.split_blocks);
 
   const int qi = col / G, g = col - (col / G) * G;
   const bool col_valid = qi < q_len;
@@ -171,7 +182,6 @@ __global__ __launch_bounds__(64 * NW, (PIPE == 2 ? 2 : 1)) void decode_kernel(De
   // dim-major block (block kg/2, keys 8*(kg%2) ..).
   const int ra = 8 * (col >> 2) + (col & 3);   // pair key of A row `col`, first product
   const int rb = ra + 4;                       // second product
-  const int32_t* table = p.tables + (size_t)b * p.table_stride;
   const size_t head_elems = 16 * D;
   const size_t block_elems = (size_t)p.hkv * head_elems;
   const uint16_t* kbase = p.kc + kvh * head_elems + 8 * kg;
@@ -183,7 +193,6 @@ __global__ __launch_bounds__(64 * NW, (PIPE == 2 ? 2 : 1)) void decode_kernel(De
   for (int i = 0; i < DB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int npairs = blk_hi > blk_lo ? (blk_hi - blk_lo + 1) >> 1 : 0;
-  int tab = 0, tab_base = -1;
 
   struct Frag {
     bf16x8 a[KSTEPS], b[KSTEPS];
@@ -197,6 +206,8 @@ __global__ __launch_bounds__(64 * NW, (PIPE == 2 ? 2 : 1)) void decode_kernel(De
       const int j = blk_lo + tab_base + lane;
       tab = j < blk_hi ? table[j] : 0;
     }
+    // (entries at or past blk_hi are never picked: a missing second block
+    // of a pair falls back to the first)
     const bool has1 = blk_lo + rel + 1 < blk_hi;
     const int phys0 = __builtin_amdgcn_readlane(tab, rel & 63);
     const int phys1 = has1 ? __builtin_amdgcn_readlane(tab, (rel & 63) + 1) : phys0;
@@ -332,32 +343,154 @@ __global__ __launch_bounds__(64 * NW, (PIPE == 2 ? 2 : 1)) void decode_kernel(De
     }
     __syncthreads();
   }
-  if (wave != 0 || !col_valid) return;
-
   // wave 0, lane (col, kg) holds dims 16*db + 4*kg .. +4 of column col
   const int t = q0 + qi;
   const int h = kvh * G + g;
-  if (p.splits == 1) {
-    const float inv = 1.f / l;
-    uint16_t* dst = p.out + ((size_t)t * p.hq + h) * D + 4 * kg;
+  if (wave == 0 && col_valid) {
+    if (p.splits == 1) {
+      const float inv = 1.f / l;
+      uint16_t* dst = p.out + ((size_t)t * p.hq + h) * D + 4 * kg;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-      *reinterpret_cast<uint2*>(dst + 16 * db) =
-          make_uint2(pack_bf16x2(acc[db][0] * inv, acc[db][1] * inv),
-                     pack_bf16x2(acc[db][2] * inv, acc[db][3] * inv));
-    if (p.lse != nullptr && kg == 0) p.lse[(size_t)t * p.hq + h] = (m + fast_log2(l)) * kLn2;
-  } else {
-    const bool empty = (l == 0.f);
-    const float inv = empty ? 0.f : 1.f / l;
-    float* dst = p.part_out + (((size_t)split * p.nt + t) * p.hq + h) * D + 4 * kg;
+      for (int db = 0; db < DB; ++db)
+        *reinterpret_cast<uint2*>(dst + 16 * db) =
+            make_uint2(pack_bf16x2(acc[db][0] * inv, acc[db][1] * inv),
+                       pack_bf16x2(acc[db][2] * inv, acc[db][3] * inv));
+      if (p.lse != nullptr && kg == 0) p.lse[(size_t)t * p.hq + h] = (m + fast_log2(l)) * kLn2;
+    } else {
+      const bool empty = (l == 0.f);
+      const float inv = empty ? 0.f : 1.f / l;
+      float* dst = p.part_out + (((size_t)split * p.nt + t) * p.hq + h) * D + 4 * kg;
+      // device-scope atomic stores write through this XCD's L2, so the
+      // merging work-group (possibly on another XCD) reads them from memory
+      // without an L2 write-back here
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-      *reinterpret_cast<float4*>(dst + 16 * db) =
-          make_float4(acc[db][0] * inv, acc[db][1] * inv, acc[db][2] * inv, acc[db][3] * inv);
-    if (kg == 0)
-      p.part_lse[((size_t)split * p.nt + t) * p.hq + h] =
-          empty ? -INFINITY : (m + fast_log2(l)) * kLn2;
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          __hip_atomic_store(dst + 16 * db + i, acc[db][i] * inv, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      if (kg == 0)
+        __hip_atomic_store(p.part_lse + ((size_t)split * p.nt + t) * p.hq + h,
+                           empty ? -INFINITY : (m + fast_log2(l)) * kLn2, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
+  if (p.splits == 1 || p.sem == nullptr) return;
+
+  // ---- merge of the split partials by the last split to finish ------------
+  // ("combining the partials in a second reduction", here done by whichever
+  // work-group of this (request, KV head) completes last, so the step needs
+  // no second launch).  Only wave 0 stored partials, all of them device-scope
+  // atomic stores: once the wave's store counter has drained they are visible
+  // device-wide, and its lane 0 then counts the arrival.  (A release fence
+  // would also write back this XCD's whole L2, which costs microseconds per
+  // work-group; nothing else here needs publishing.)  The last arrival
+  // acquires, which drops stale L2 lines, before reading the other splits'
+  // partials.  The counter is returned to zero for the next call.
+  __shared__ int s_last;
+  int* sem = p.sem + (size_t)b * p.hkv + kvh;
+  if (threadIdx.x == 0) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    s_last = __hip_atomic_fetch_add(sem, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             p.splits - 1;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+
+  // Items are (row, 4 dims); with fewer items than threads the splits are
+  // dealt round-robin to SG groups of threads.  Each thread keeps its own
+  // running (max, sum, acc) over chunks of CH splits whose loads are all in
+  // flight together, then the groups are merged through LDS.
+  constexpr int NT = 64 * NW;
+  constexpr int QUADS = D / 4;
+  constexpr int CH = (PIPE == 2) ? 16 : 8;
+  const int rows = q_len * G;
+  const int items = rows * QUADS;
+  const int sg = items >= NT ? 1 : NT / items;
+  const size_t split_rows = (size_t)p.nt * p.hq;
+  float* s_m = &s_x[0][0][0];  // [6][NT] staging for the group merge
+  static_assert(sizeof(s_x) >= 6 * NT * sizeof(float), "LDS staging too small");
+  for (int base = 0; base < items * sg; base += NT) {
+    const int slot = base + threadIdx.x;
+    const bool act = slot < items * sg;
+    const int item = slot % items, grp = slot / items;
+    const int r = item / QUADS, quad = item - (item / QUADS) * QUADS;
+    const int tt = q0 + r / G, hh = kvh * G + (r - (r / G) * G);
+    const size_t rowi = (size_t)tt * p.hq + hh;
+    const float* ob = p.part_out + rowi * D + quad * 4;
+    float mm = -INFINITY, ll = 0.f;
+    float4 ac = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (act) {
+      for (int s0 = grp; s0 < p.splits; s0 += CH * sg) {
+        float x[CH];
+        float4 v[CH];
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+          const int sp = s0 + c * sg;
+          const bool ok = sp < p.splits;
+          x[c] = ok ? p.part_lse[sp * split_rows + rowi] : -INFINITY;
+          v[c] = ok ? *reinterpret_cast<const float4*>(ob + sp * split_rows * D)
+                    : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        float mc = mm;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) mc = fmaxf(mc, x[c]);
+        if (mc == -INFINITY) continue;  // only empty splits so far
+        const float a = fast_exp2((mm - mc) * kLog2e);  // 0 while mm = -inf
+        ac.x *= a; ac.y *= a; ac.z *= a; ac.w *= a;
+        ll *= a;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+          const float w = fast_exp2((x[c] - mc) * kLog2e);  // 0 for an empty split
+          // empty splits carry zeros, so w * v stays finite
+          ac.x += w * v[c].x; ac.y += w * v[c].y; ac.z += w * v[c].z; ac.w += w * v[c].w;
+          ll += w;
+        }
+        mm = mc;
+      }
+    }
+    if (sg == 1) {
+      if (act) {
+        const float inv = 1.f / ll;
+        uint16_t* dst = p.out + rowi * D + quad * 4;
+        *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(ac.x * inv, ac.y * inv),
+                                                    pack_bf16x2(ac.z * inv, ac.w * inv));
+        if (p.lse != nullptr && quad == 0) p.lse[rowi] = mm + fast_log2(ll) * kLn2;
+      }
+      continue;
+    }
+    // sg > 1: a single pass (items * sg <= NT); merge the groups of each item
+    s_m[0 * NT + threadIdx.x] = mm;
+    s_m[1 * NT + threadIdx.x] = ll;
+    s_m[2 * NT + threadIdx.x] = ac.x;
+    s_m[3 * NT + threadIdx.x] = ac.y;
+    s_m[4 * NT + threadIdx.x] = ac.z;
+    s_m[5 * NT + threadIdx.x] = ac.w;
+    __syncthreads();
+    if ((int)threadIdx.x < items) {
+      float M = -INFINITY;
+      for (int g2 = 0; g2 < sg; ++g2) M = fmaxf(M, s_m[g2 * items + threadIdx.x]);
+      float L = 0.f;
+      float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int g2 = 0; g2 < sg; ++g2) {
+        const int k = g2 * items + threadIdx.x;
+        const float mg = s_m[k];
+        const float a = mg == -INFINITY ? 0.f : fast_exp2((mg - M) * kLog2e);
+        L += a * s_m[NT + k];
+        A.x += a * s_m[2 * NT + k];
+        A.y += a * s_m[3 * NT + k];
+        A.z += a * s_m[4 * NT + k];
+        A.w += a * s_m[5 * NT + k];
+      }
+      const float inv = 1.f / L;
+      uint16_t* dst = p.out + rowi * D + quad * 4;
+      *reinterpret_cast<uint2*>(dst) =
+          make_uint2(pack_bf16x2(A.x * inv, A.y * inv), pack_bf16x2(A.z * inv, A.w * inv));
+      if (p.lse != nullptr && quad == 0) p.lse[rowi] = M + fast_log2(L) * kLn2;
+    }
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(sem, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int D, int G>
@@ -376,11 +509,17 @@ void launch_dg(const AttnArgs& a, hipStream_t stream) {
   p.table_stride = a.table_stride;
   p.splits = a.splits;
   p.nt = a.num_tokens;
+  {
+    const int max_blocks = (a.max_seq_len + 15) / 16;
+    const int bps = (max_blocks + a.splits - 1) / a.splits;
+    p.split_blocks = (bps + 1) & ~1;  // whole pairs per split
+  }
   p.scale_log2 = a.scale * kLog2e;
   p.out = (uint16_t*)a.out;
   p.lse = a.lse;
   p.part_out = a.part_out;
   p.part_lse = a.part_lse;
+  p.sem = a.sem;
   if (a.decode_order != nullptr) {
     int shift = 0;
     const int max_blocks = (a.max_seq_len + 15) / 16;

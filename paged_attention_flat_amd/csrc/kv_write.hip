@@ -21,33 +21,38 @@ template <typename E>
 __global__ __launch_bounds__(256) void kv_write_kernel(
     const E* __restrict__ key, const E* __restrict__ value, E* __restrict__ kc,
     E* __restrict__ vc, const int64_t* __restrict__ slots, int32_t nt,
-    int32_t hkv, int32_t d) {
+    int32_t hkv, int32_t d, int64_t num_slots) {
   constexpr int kPad = 16 / sizeof(E);  // keeps LDS rows 16-byte aligned
   __shared__ __align__(16) E vrow[kTok][128 + kPad];
   __shared__ int64_t sslot[kTok];
   const int tid = threadIdx.x;
   const int t0 = blockIdx.x * kTok;
   const int h = blockIdx.y;
-  if (tid < kTok) sslot[tid] = (t0 + tid < nt) ? slots[t0 + tid] : -1;
-  __syncthreads();
+  const int ntok = min(kTok, nt - t0);
 
+  // The K/V loads do not depend on the slot, so they are issued together with
+  // the slot load (one memory round trip before the stores).
   const int cpr = d * (int)sizeof(E) / 16;  // 16-byte pieces per row
   for (int c = tid; c < kTok * cpr; c += 256) {
     const int ti = c / cpr, part = c - ti * cpr;
-    const int64_t s = sslot[ti];
-    if (s < 0) continue;
+    if (ti >= ntok) break;
+    int64_t s = slots[t0 + ti];
+    if (s >= num_slots) s = -1;  // out of the pool: dropped like a padded token
     const size_t src = ((size_t)(t0 + ti) * hkv + h) * d;
     const uint4 kv = reinterpret_cast<const uint4*>(key + src)[part];
     const uint4 vv = reinterpret_cast<const uint4*>(value + src)[part];
+    if (part == 0) sslot[ti] = s;
+    reinterpret_cast<uint4*>(&vrow[ti][0])[part] = vv;
+    if (s < 0) continue;
     const size_t blk = (size_t)(s >> 4), off = (size_t)(s & 15);
     E* kdst = kc + ((blk * hkv + h) * kTok + off) * d;
     reinterpret_cast<uint4*>(kdst)[part] = kv;
-    reinterpret_cast<uint4*>(&vrow[ti][0])[part] = vv;
   }
   __syncthreads();
 
   for (int e = tid; e < kTok * d; e += 256) {
     const int ti = e & (kTok - 1), c = e >> 4;
+    if (ti >= ntok) continue;
     const int64_t s = sslot[ti];
     if (s < 0) continue;
     const size_t blk = (size_t)(s >> 4), off = (size_t)(s & 15);
@@ -59,17 +64,17 @@ __global__ __launch_bounds__(256) void kv_write_kernel(
 
 hipError_t launch_kv_write(const void* key, const void* value, void* kc, void* vc,
                            const int64_t* slots, int32_t nt, int32_t hkv,
-                           int32_t d, int32_t esize, hipStream_t stream) {
+                           int32_t d, int32_t esize, int64_t num_blocks, hipStream_t stream) {
   dim3 grid((nt + kTok - 1) / kTok, hkv);
   trace_before(K_KV_WRITE, stream);
   if (esize == 2) {
     hipLaunchKernelGGL(kv_write_kernel<uint16_t>, grid, dim3(256), 0, stream,
                        (const uint16_t*)key, (const uint16_t*)value, (uint16_t*)kc,
-                       (uint16_t*)vc, slots, nt, hkv, d);
+                       (uint16_t*)vc, slots, nt, hkv, d, num_blocks * kTok);
   } else {
     hipLaunchKernelGGL(kv_write_kernel<uint32_t>, grid, dim3(256), 0, stream,
                        (const uint32_t*)key, (const uint32_t*)value, (uint32_t*)kc,
-                       (uint32_t*)vc, slots, nt, hkv, d);
+                       (uint32_t*)vc, slots, nt, hkv, d, num_blocks * kTok);
   }
   trace_after(stream);
   return hipGetLastError();

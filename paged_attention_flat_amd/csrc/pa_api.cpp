@@ -72,10 +72,11 @@ size_t plan_capacity(int32_t num_seqs, int32_t num_tokens) {
 }
 
 // Workspace layout (each region 256-byte aligned):
+//   [split-merge counters: num_seqs * hq ints, zero between calls]
 //   [plan: 1 + 2 * cap ints][plan_tmp: 2 * cap ints][decode order: 1 + num_seqs ints]
 //   [partial out: splits * nt * hq * d floats][partial lse: splits * nt * hq floats]
 struct WsLayout {
-  size_t plan, plan_tmp, order, part_out, part_lse, total;
+  size_t sem, plan, plan_tmp, order, part_out, part_lse, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -83,7 +84,10 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 WsLayout ws_layout(int32_t num_seqs, int32_t num_tokens, int32_t hq, int32_t d, int32_t splits) {
   WsLayout w;
   const size_t cap = plan_capacity(num_seqs, num_tokens);
-  w.plan = 0;
+  // arrival counters of the split merge, one per (request, KV head <= Hq);
+  // must be zero on entry and are left zero by every call
+  w.sem = 0;
+  w.plan = align256((size_t)num_seqs * hq * sizeof(int32_t));
   w.plan_tmp = align256(w.plan + (1 + 2 * cap) * sizeof(int32_t));
   w.order = align256(w.plan_tmp + 2 * cap * sizeof(int32_t));
   w.part_out = align256(w.order + (1 + (size_t)num_seqs) * sizeof(int32_t));
@@ -154,6 +158,7 @@ const char* pa_kernel_name(int32_t id) {
     case K_F32_ATTN: return "attn_f32";
     case K_F32_ATTN_SPLIT: return "attn_f32_split_partial";
     case K_DECODE_ORDER: return "decode_order";
+    case K_ZERO: return "workspace_zero";
   }
   return "unknown";
 }
@@ -217,7 +222,9 @@ int32_t pa_choose_num_splits(int32_t num_seqs, int32_t max_query_len, int32_t ma
   if (num_cus <= 0) num_cus = device_cu_count();
   const int64_t units = (int64_t)num_seqs * num_kv_heads;
   if (units >= num_cus) return 1;
-  const int64_t want = (2 * (int64_t)num_cus + units - 1) / units;
+  // one split work-group per CU: each split adds a partial to merge, and a
+  // second resident work-group per CU gains less than that costs
+  const int64_t want = ((int64_t)num_cus + units - 1) / units;
   const int64_t blocks = (max_seq_len + PA_BLOCK_SIZE - 1) / PA_BLOCK_SIZE;
   const int64_t by_blocks = std::max<int64_t>(1, blocks / 8);  // >= 8 blocks per split
   int64_t s = std::min<int64_t>(want, by_blocks);
@@ -239,7 +246,15 @@ pa_status pa_kv_write(const void* key, const void* value, void* key_cache, void*
     return PA_ERR_INVALID;
   const int32_t esize = dtype == PA_BF16 ? 2 : 4;
   hipError_t e = launch_kv_write(key, value, key_cache, value_cache, slot_mapping, num_tokens,
-                                 num_kv_heads, head_dim, esize, (hipStream_t)stream);
+                                 num_kv_heads, head_dim, esize, num_blocks, (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status pa_attention_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  if (workspace_bytes == 0) return PA_OK;
+  if (workspace == nullptr) return PA_ERR_NULL;
+  if (!aligned16(workspace)) return PA_ERR_INVALID;
+  hipError_t e = launch_zero(workspace, workspace_bytes, (hipStream_t)stream);
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
@@ -333,9 +348,11 @@ pa_status pa_attention_fwd(const void* query, const void* key_cache, const void*
     a.decode_order = reinterpret_cast<int32_t*>(ws + lay.order);
   a.part_out = nullptr;
   a.part_lse = nullptr;
+  a.sem = nullptr;
   if (splits > 1) {
     a.part_out = reinterpret_cast<float*>(ws + lay.part_out);
     a.part_lse = reinterpret_cast<float*>(ws + lay.part_lse);
+    a.sem = reinterpret_cast<int32_t*>(ws + lay.sem);
   }
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipSuccess;
@@ -345,12 +362,11 @@ pa_status pa_attention_fwd(const void* query, const void* key_cache, const void*
       e = launch_combine(a.part_out, a.part_lse, splits, num_tokens, num_q_heads, head_dim, out,
                          lse, 0, query_start_loc, num_seqs, 1 << 30, s);
   } else {
+    // the bf16 decode kernel merges its own split partials (the last split of
+    // each request and KV head to finish does it)
     const int32_t dq = decode_max_q(group);
     if (max_query_len > dq) e = launch_prefill_bf16(a, s);
     if (e == hipSuccess) e = launch_decode_bf16(a, s);
-    if (e == hipSuccess && splits > 1)
-      e = launch_combine(a.part_out, a.part_lse, splits, num_tokens, num_q_heads, head_dim, out,
-                         lse, 1, query_start_loc, num_seqs, dq, s);
   }
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }

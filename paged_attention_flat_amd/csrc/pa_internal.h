@@ -18,7 +18,8 @@ enum KernelId : int32_t {
   K_F32_ATTN = 6,
   K_F32_ATTN_SPLIT = 7,
   K_DECODE_ORDER = 8,
-  K_COUNT = 9
+  K_ZERO = 9,
+  K_COUNT = 10
 };
 
 // Tracing hooks (pa_api.cpp).  trace_before/after bracket one launch.
@@ -28,7 +29,8 @@ void trace_after(hipStream_t stream);
 // ---- launchers (each enqueues on `stream` and returns hipGetLastError) ------
 hipError_t launch_kv_write(const void* key, const void* value, void* kc, void* vc,
                            const int64_t* slots, int32_t nt, int32_t hkv,
-                           int32_t d, int32_t esize, hipStream_t stream);
+                           int32_t d, int32_t esize, int64_t num_blocks,
+                           hipStream_t stream);
 
 struct AttnArgs {
   const void* q;
@@ -50,6 +52,7 @@ struct AttnArgs {
   int32_t plan_cap;     // capacity of the work list (items)
   int32_t* decode_order;  // nullable: count + ranked decode requests
   int32_t num_cus;        // compute units of the current device
+  int32_t* sem;           // nullable: zeroed arrival counters, one per (request, KV head)
 };
 
 // Largest number of new tokens per request that the decode kernel packs.
@@ -70,6 +73,7 @@ inline int32_t prefill_tile_tokens(int32_t group) {
 hipError_t launch_decode_bf16(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_zero(void* ptr, size_t bytes, hipStream_t stream);
 hipError_t launch_combine(const float* po, const float* pl, int32_t splits,
                           int32_t nt, int32_t hq, int32_t d, void* out, float* lse,
                           int32_t out_bf16, const int32_t* qsl, int32_t num_seqs,

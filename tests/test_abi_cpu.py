@@ -109,7 +109,7 @@ def test_workspace_size_grows_with_splits(lib):
 
 def test_split_heuristic_crossover(lib):
     f = lib.pa_choose_num_splits
-    assert f(1, 1, 32768, 32, 8, 256) == 64          # long single decode: split
+    assert f(1, 1, 32768, 32, 8, 256) == 32          # long single decode: a split per CU
     assert f(256, 1, 8192, 32, 8, 256) == 1          # batch fills the grid: no split
     assert f(4, 8192, 8192, 32, 8, 256) == 1         # prefill rows present
     assert f(4098, 2048, 18432, 32, 8, 256) == 1

@@ -141,6 +141,24 @@ def test_kv_write_skips_padded_tokens():
     assert same_bits(g["v_pool"], vp)
 
 
+def test_kv_write_drops_slots_past_the_pool():
+    # a slot at or past num_blocks * 16 is dropped like a padded token
+    reqs = [Request(3, 20, [5, 1]), Request(0, 1, [2])]
+    step = build_step("oob", reqs, dtype="bf16", num_q_heads=8, num_kv_heads=2, head_dim=128,
+                      num_blocks=8, seed=43, pad_tokens=4)
+    bad = step.slot_mapping.copy()
+    bad[-4:] = [8 * 16, 8 * 16 + 5, 1 << 40, 8 * 16 + 15]
+    pa = pa_mod()
+    g = upload(step)
+    g["slots"] = torch.as_tensor(bad).to("cuda")
+    pa.kv_write(g["key"], g["value"], g["k_pool"], g["v_pool"], g["slots"])
+    torch.cuda.synchronize()
+    kp, vp = oracle.kv_write(raw_numpy(step.key), raw_numpy(step.value), raw_numpy(step.k_pool),
+                             raw_numpy(step.v_pool), step.slot_mapping)
+    assert same_bits(g["k_pool"], kp)
+    assert same_bits(g["v_pool"], vp)
+
+
 def test_kv_write_f32_head_dim_128_and_bf16_64():
     for dtype, d in (("f32", 128), ("bf16", 64)):
         reqs = [Request(0, 37, [3, 0, 6]), Request(9, 2, [1])]
@@ -263,6 +281,34 @@ def test_shared_prefix_is_bitwise_equal_to_private_copies():
     priv.num_blocks = nb
     out_p, lse_p, _ = run_gpu(priv, num_splits=1)
     assert same_bits(out_s, out_p) and same_bits(lse_s, lse_p)
+
+
+def test_split_merge_deterministic_and_workspace_reusable():
+    # the last split to finish merges; which one that is varies between runs,
+    # the merge order does not.  One workspace serves every call: the arrival
+    # counters at its head must be back to zero after each.
+    pa = pa_mod()
+    step = config_step(5, scale_down=SMALL[5])
+    g = upload(step)
+    (ro, rl), _ = run_oracle(step)
+    hq = step.query.shape[1]
+    ws = pa.workspace(step.num_seqs, step.num_tokens, hq, step.query.shape[2], 64)
+    first = {}
+    for rep in range(3):
+        for splits in (8, 64, 3):
+            pa.kv_write(g["key"], g["value"], g["k_pool"], g["v_pool"], g["slots"])
+            out, lse = pa.attention(g["query"], g["k_pool"], g["v_pool"], g["qsl"],
+                                    g["seq_lens"], g["tables"], step.max_query_len,
+                                    step.max_seq_len, step.scale, num_splits=splits,
+                                    workspace=ws)
+            torch.cuda.synchronize()
+            sem = ws[:4 * step.num_seqs * hq].view(torch.int32)
+            assert int(sem.abs().sum()) == 0, f"counters not reset (S={splits})"
+            if rep == 0:
+                check(step, out, lse, ro, rl, what=f"shared workspace S={splits}")
+                first[splits] = (out.clone(), lse.clone())
+            else:
+                assert same_bits(out, first[splits][0]) and same_bits(lse, first[splits][1])
 
 
 def test_split_results_agree_with_each_other():
