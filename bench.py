@@ -47,6 +47,10 @@ WORKLOAD_NAMES = {
        "1024-token prefix, Hq 32/Hkv 8, d 128, bf16)",
 }
 
+# names of the per-workload rocprofv3 summaries in profiles/
+PROFILE_NAMES = {2: "long_context_decode", 3: "large_batch_decode", 4: "long_prefill",
+                 5: "mixed_chunked_prefill_step"}
+
 
 def parse_args():
     ap = argparse.ArgumentParser()
@@ -309,6 +313,36 @@ def kernel_times(runners, steps, log):
     return {k: {"avg_us": 1e3 * v[0] / v[1], "launches": v[1]} for k, v in agg.items()}
 
 
+def kernel_sources_sha256():
+    """Hash of the kernel sources (and the ABI header) of this tree."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_attention_flat_amd", "csrc")
+    files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc)
+                   if f.endswith((".hip", ".cpp", ".h")))
+    for f in files + [os.path.join(ROOT, "include", "pa.h")]:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (profiles/hbm_traffic.json), or None when the kernels changed since the
+    counters were taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("sources_sha256") != kernel_sources_sha256():
+        return None
+    k = t.get("kernels", {}).get(workload, {}).get(kernel)
+    return None if k is None else k["hbm_bytes_per_launch"]
+
+
 # ----------------------------------------------------------------------------
 # workloads
 # ----------------------------------------------------------------------------
@@ -338,7 +372,8 @@ def bench_main(args, log):
         "step": step, "ms": ms, "mode": mode, "splits": base.splits, "work": wm,
         "kernels": kt,
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                     "traffic": measured_traffic("long_context_decode", "decode"),
                      "bytes_per_launch": kbytes, "units_per_launch": ktoks,
                      "unit_def": "one context token of one request: K and V for 8 KV heads "
                                  "x 128 dims x 2 B = 4096 B (plus Q and table reads)",
@@ -369,11 +404,13 @@ def bench_extra(cfg, args, log):
         name = "decode" if "decode" in kt else "decode_split_partial"
         kb, _ = decode_kernel_bytes(step)
         gbs = kb / (kt[name]["avg_us"] * 1e-6) / 1e9
-        out["decode_kernel"] = {"bytes": kb, "GBps": gbs, "frac_hbm": gbs / PEAK_HBM_GBS}
+        out["decode_kernel"] = {"bytes": kb, "GBps": gbs, "frac_hbm": gbs / PEAK_HBM_GBS,
+                                "traffic": measured_traffic(PROFILE_NAMES[cfg], "decode")}
     if "prefill_mfma" in kt:
         tf = wm["prefill_flops"] / (kt["prefill_mfma"]["avg_us"] * 1e-6) / 1e12
         out["prefill_kernel"] = {"flops": wm["prefill_flops"], "TFLOPps": tf,
-                                 "frac_mfma": tf / PEAK_BF16_TFLOPS}
+                                 "frac_mfma": tf / PEAK_BF16_TFLOPS,
+                                 "traffic": measured_traffic(PROFILE_NAMES[cfg], "prefill_mfma")}
     if cfg == 5:
         t_roof = max(wm["bytes"] / (PEAK_HBM_GBS * 1e9), wm["flops"] / (PEAK_BF16_TFLOPS * 1e12))
         out["step_roofline_frac"] = t_roof / (ms * 1e-3)
