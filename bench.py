@@ -307,10 +307,14 @@ def kernel_times(runners, steps, log):
     for name, ms in recs:
         if ms < 0:
             continue
-        a = agg.setdefault(name, [0.0, 0])
-        a[0] += ms
-        a[1] += 1
-    return {k: {"avg_us": 1e3 * v[0] / v[1], "launches": v[1]} for k, v in agg.items()}
+        agg.setdefault(name, []).append(1e3 * ms)
+    out = {}
+    for k, v in agg.items():
+        v = sorted(v)
+        q = lambda f: v[min(len(v) - 1, int(f * (len(v) - 1) + 0.5))]
+        out[k] = {"avg_us": sum(v) / len(v), "launches": len(v), "p10_us": q(0.1),
+                  "p50_us": q(0.5), "p90_us": q(0.9)}
+    return out
 
 
 def kernel_sources_sha256():
@@ -382,6 +386,96 @@ def bench_main(args, log):
     del runners, base
     torch.cuda.empty_cache()
     return res
+
+
+def split_sweep(args, log, splits=(1, 8, 16, 32, 64, 128)):
+    """Step time of the long single decode at fixed split counts (graph
+    replay, the same eight rotating pool replicas as the headline)."""
+    import torch
+
+    from workloads import config_step
+    dev = torch.device("cuda:0")
+    step = config_step(2, device=dev, fill="zero")
+    pools = [(step.k_pool, step.v_pool)]
+    for _ in range(args.replicas - 1):
+        pools.append((step.k_pool.clone(), step.v_pool.clone()))
+    wm = work_model(step)
+    out = []
+    for S in splits:
+        runners = [StepRunner(step, dev, S, pools=pl) for pl in pools]
+        n = args.replicas * (4 if S == 1 else 10)
+        ms, _ = time_steps(runners, n, args.replicas, not args.eager, log,
+                           per_graph=len(runners))
+        out.append({"num_splits": S, "us_per_step": round(ms * 1e3, 2),
+                    "step_GBps": round(wm["bytes"] / (ms * 1e-3) / 1e9, 1)})
+        log(f"split sweep: S={S} {ms * 1e3:.2f} us/step")
+        del runners
+    del pools, step
+    torch.cuda.empty_cache()
+    return out
+
+
+def achievable(log):
+    """What plain library code reaches on this machine: a 1 GiB device copy
+    (read + write bytes) and an 8192^3 bf16 GEMM through torch."""
+    import torch
+    res = {}
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / 10
+    res["device_copy_GBps"] = round(2 * (1 << 30) / dt / 1e9, 1)
+    del src, dst
+    n = 8192
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(10):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / 10
+    res["gemm_bf16_8192_TFLOPps"] = round(2 * n ** 3 / dt / 1e12, 1)
+    del a, b
+    torch.cuda.empty_cache()
+    log(f"achievable: {json.dumps(res)}")
+    return res
+
+
+def bench_config1(args, log):
+    """The tiny fp32 mixed step: GPU time per step and the oracle's
+    CPU-seconds for the same step (correctness workload, no roofline)."""
+    import torch
+
+    import oracle
+    from workloads import config_step, raw_numpy
+    dev = torch.device("cuda:0")
+    step = config_step(1, device=dev, fill="zero")
+    r = StepRunner(step, dev, 0)
+    ms, mode = time_steps([r], args.extra_steps, 3, not args.eager, log)
+    cpu_step = config_step(1, device="cpu", fill="zero")
+    t0 = time.process_time()
+    kp, vp = oracle.kv_write(raw_numpy(cpu_step.key), raw_numpy(cpu_step.value),
+                             raw_numpy(cpu_step.k_pool), raw_numpy(cpu_step.v_pool),
+                             cpu_step.slot_mapping)
+    oracle.attention(raw_numpy(cpu_step.query), kp, vp, cpu_step.query_start_loc,
+                     cpu_step.seq_lens, cpu_step.block_tables, cpu_step.scale,
+                     cpu_step.num_kv_heads, cpu_step.dtype)
+    cpu_s = time.process_time() - t0
+    out = {"workload": "tiny mixed fp32 step (prefill 37 + decodes at 5, 17, 64; Hq 4/Hkv 2, "
+                       "d 64)", "us_per_step": round(ms * 1e3, 2), "launch": mode,
+           "oracle_cpu_seconds": round(cpu_s, 4)}
+    log(f"config1: {json.dumps(out)}")
+    del r
+    return out
 
 
 def bench_extra(cfg, args, log):
@@ -481,10 +575,16 @@ def main():
     log(f"main: {ms * 1e3:.2f} us/step, {value:.1f} GB/s, kernels "
         f"{json.dumps({k: round(v['avg_us'], 2) for k, v in res['kernels'].items()})}")
     extras = []
+    sweep = None
+    ach = None
+    cfg1 = None
     if not args.only_main:
+        sweep = split_sweep(args, log)
         for cfg in (3, 4, 5):
             log("extra workload: " + WORKLOAD_NAMES[cfg])
             extras.append(bench_extra(cfg, args, log))
+        cfg1 = bench_config1(args, log)
+        ach = achievable(log)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args, log)
@@ -509,8 +609,12 @@ def main():
         "roofline": {k: (round(v, 4) if isinstance(v, float) else v)
                      for k, v in res["roofline"].items()},
         "cpu_baseline": cpu,
-        "kernels_us": {k: round(v["avg_us"], 2) for k, v in res["kernels"].items()},
+        "kernels_us": {k: {m: round(v[m], 2) for m in ("avg_us", "p10_us", "p50_us", "p90_us")}
+                       for k, v in res["kernels"].items()},
+        "split_sweep": sweep,
         "extra_workloads": extras,
+        "correctness_workload": cfg1,
+        "achievable": ach,
     }
     print(json.dumps(line), flush=True)
 
