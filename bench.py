@@ -367,6 +367,10 @@ def bench_main(args, log):
     # one graph holds one step on each replica in turn (R steps per replay)
     ms, mode = time_steps(runners, args.steps, args.warmup, not args.eager, log,
                           per_graph=len(runners))
+    eager_ms = None
+    if not args.eager:
+        # the same steps launched one call at a time from the host (no graph)
+        eager_ms, _ = time_steps(runners, min(args.steps, 200), args.warmup, False, log)
     kt = kernel_times(runners, min(args.steps, 200), log)
     kbytes, ktoks = decode_kernel_bytes(step)
     dom = "decode_split_partial" if base.splits > 1 else "decode"
@@ -374,6 +378,7 @@ def bench_main(args, log):
     achieved = kbytes / (dur_us * 1e-6) / 1e9
     res = {
         "step": step, "ms": ms, "mode": mode, "splits": base.splits, "work": wm,
+        "eager_ms": eager_ms,
         "kernels": kt,
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
@@ -549,7 +554,8 @@ def main():
     args = parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): this build has no "
-              "multi-GPU path; see the sharding note in DESIGN.md", file=sys.stderr)
+              "multi-GPU path (attention shards by KV head or by request with no exchange "
+              "inside the step)", file=sys.stderr)
         sys.exit(2)
 
     def log(msg):
@@ -611,6 +617,9 @@ def main():
         "cpu_baseline": cpu,
         "kernels_us": {k: {m: round(v[m], 2) for m in ("avg_us", "p10_us", "p50_us", "p90_us")}
                        for k, v in res["kernels"].items()},
+        "launch_path": {"graph_us_per_step": round(ms * 1e3, 2),
+                        "eager_us_per_step": None if res["eager_ms"] is None
+                        else round(res["eager_ms"] * 1e3, 2)},
         "split_sweep": sweep,
         "extra_workloads": extras,
         "correctness_workload": cfg1,

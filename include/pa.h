@@ -207,6 +207,26 @@ int32_t pa_choose_num_splits(int32_t num_seqs, int32_t max_query_len,
                              int32_t max_seq_len, int32_t num_q_heads,
                              int32_t num_kv_heads, int32_t num_cus);
 
+/*
+ * pa_capture_size -- the padded size a step of num_tokens tokens is replayed
+ * at from a captured HIP graph ("Model execution", section "Code": graphs are
+ * captured for a ladder of batch sizes 1, 2, 4, then every multiple of 8
+ * below 256, then every multiple of 16 up to the largest captured size, and a
+ * step runs the graph of the smallest size that holds it, the extra rows
+ * padded; larger steps run without a graph).  max_size is the largest
+ * captured size (512 on the page; it must be a ladder size >= 256 or one of
+ * the sizes below 256).  Returns the ladder size, or -1 when num_tokens < 1 or
+ * num_tokens > max_size.  Host-only.
+ *
+ * Padding that keeps a captured step exact: padded tokens get slot -1 (the
+ * KV write skips them) and belong to no request's rows; padded requests have
+ * q_len 0 and seq_len 0 (no rows, no keys).  Grids are then sized from the
+ * padded shapes and host bounds fixed at capture (max_query_len, and
+ * max_seq_len = the block-table capacity), so one graph serves every step of
+ * that size.
+ */
+int32_t pa_capture_size(int32_t num_tokens, int32_t max_size);
+
 /* pa_status_string -- static text for a status code (never NULL). */
 const char* pa_status_string(pa_status status);
 

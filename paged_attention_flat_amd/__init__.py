@@ -22,7 +22,8 @@ from ._lib import LIB, PA_BF16, PA_F32, PA_BLOCK_SIZE, PA_MAX_SPLITS  # noqa: F4
 
 __all__ = [
     "PaError", "kv_write", "attention", "split_combine", "workspace_size",
-    "choose_num_splits", "alloc_cache", "workspace", "trace_begin", "trace_end", "trace_read",
+    "choose_num_splits", "capture_size", "alloc_cache", "workspace", "trace_begin", "trace_end",
+    "trace_read",
     "kernel_name", "version",
 ]
 
@@ -104,6 +105,12 @@ def choose_num_splits(num_seqs: int, max_query_len: int, max_seq_len: int, num_q
                       num_kv_heads: int, num_cus: int = 0) -> int:
     return int(LIB.pa_choose_num_splits(num_seqs, max_query_len, max_seq_len, num_q_heads,
                                         num_kv_heads, num_cus))
+
+
+def capture_size(num_tokens: int, max_size: int = 512):
+    """Ladder size a step of num_tokens is replayed at, or None (no graph)."""
+    n = int(LIB.pa_capture_size(int(num_tokens), int(max_size)))
+    return None if n < 0 else n
 
 
 def attention(query, key_cache, value_cache, query_start_loc, seq_lens, block_tables,

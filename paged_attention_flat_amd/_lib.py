@@ -40,6 +40,7 @@ PROTOTYPES = {
     "pa_split_combine": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp]),
     "pa_attention_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "pa_choose_num_splits": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "pa_capture_size": (_i32, [_i32, _i32]),
     "pa_status_string": (ctypes.c_char_p, [_i32]),
     "pa_version": (_i32, []),
     "pa_trace_begin": (_i32, [_i32]),

@@ -232,6 +232,16 @@ int32_t pa_choose_num_splits(int32_t num_seqs, int32_t max_query_len, int32_t ma
   return (int32_t)std::max<int64_t>(1, s);
 }
 
+int32_t pa_capture_size(int32_t num_tokens, int32_t max_size) {
+  if (num_tokens < 1 || num_tokens > max_size) return -1;
+  int32_t size;
+  if (num_tokens <= 2) size = num_tokens;
+  else if (num_tokens <= 4) size = 4;
+  else if (num_tokens < 256) size = (num_tokens + 7) & ~7;
+  else size = (num_tokens + 15) & ~15;
+  return size <= max_size ? size : -1;
+}
+
 pa_status pa_kv_write(const void* key, const void* value, void* key_cache, void* value_cache,
                       const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
                       int32_t head_dim, int32_t block_size, int64_t num_blocks, pa_dtype dtype,

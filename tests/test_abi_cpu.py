@@ -117,3 +117,20 @@ def test_split_heuristic_crossover(lib):
     assert 1 < f(2, 1, 4096, 32, 8, 256) <= 256
     assert f(1, 4, 4096, 32, 8, 256) > 1             # 4 new tokens still pack (G = 4)
     assert f(1, 5, 4096, 32, 8, 256) == 1
+
+
+def test_capture_size_matches_printed_ladder(lib):
+    # "Model execution", section "Code": the printed padding table and ladder
+    from conftest import read_golden
+    g = read_golden("capture_ladder_printed.txt")
+    for tokens, used, padded in g["pad"]:
+        got = lib.pa_capture_size(tokens, 512)
+        assert got == used, (tokens, got, used)
+        if used > 0:
+            assert got - tokens == padded
+    sizes = sorted({lib.pa_capture_size(n, 512) for n in range(1, 513)})
+    assert len(sizes) == g["count"][0][0]
+    assert sizes[:6] == g["first"][0] and sizes[-3:] == g["last"][0]
+    assert lib.pa_capture_size(0, 512) == -1 and lib.pa_capture_size(-3, 512) == -1
+    # a smaller top size cuts the ladder there
+    assert lib.pa_capture_size(200, 128) == -1 and lib.pa_capture_size(128, 128) == 128
