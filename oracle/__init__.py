@@ -20,6 +20,8 @@ reference pages):
   same section as a self-check variant.
 * Same page, section "Prefill has a full grid; decode at batch 1 has almost
   none": the split-KV partials and their combine as a self-check variant.
+* ``fp8``: an FP8 (OCP E4M3) KV cache with per-KV-head scales -- the
+  quantising write and attention over the dequantised pools.
 
 Every function works in float64.  bf16 data is carried as its raw uint16 bit
 pattern and widened exactly.
@@ -38,4 +40,13 @@ from .paged_attention import (  # noqa: F401
     attention_online,
     attention_split_partials,
     combine_partials,
+)
+from .fp8 import (  # noqa: F401
+    E4M3_MAX,
+    e4m3_decode,
+    e4m3_encode,
+    quantize,
+    kv_write_fp8,
+    dequantize_pool,
+    attention_fp8,
 )

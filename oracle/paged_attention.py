@@ -33,7 +33,8 @@ BLOCK_SIZE = 16
 # ----------------------------------------------------------------------------
 
 def to_f64(x, dtype: str) -> np.ndarray:
-    """Widen bf16 bit patterns (uint16) or float32 values to float64 exactly.
+    """Widen bf16 bit patterns (uint16) or float32 values to float64 exactly
+    (float64 input passes through).
 
     A bf16 value is the upper half of the float32 with the same bits, so the
     widening is a 16-bit left shift followed by a reinterpretation.
@@ -43,6 +44,8 @@ def to_f64(x, dtype: str) -> np.ndarray:
         return bits.view(np.float32).astype(np.float64)
     if dtype == "f32":
         return np.asarray(x, dtype=np.float32).astype(np.float64)
+    if dtype == "f64":
+        return np.asarray(x, dtype=np.float64)
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
