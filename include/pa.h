@@ -158,6 +158,59 @@ pa_status pa_attention_fwd(const void* query,
                            pa_dtype dtype, void* stream);
 
 /*
+ * FP8 KV cache (E4M3).  The pages name an 8-bit cache as the way to halve the
+ * bytes every decode step reads ("Anatomy of a serving engine", KV-cache
+ * capacity; "Model execution", section "Attention backends") without fixing
+ * the format.  Format here: OCP E4M3 -- sign, 4-bit exponent (bias 7), 3-bit
+ * mantissa, subnormals m/8 * 2^-6, no infinities, 0x7F / 0xFF NaN, largest
+ * finite magnitude 448.  Same block layouts as the 16-bit cache, one byte per
+ * element: K [num_blocks][num_kv_heads][16][head_dim], V
+ * [num_blocks][num_kv_heads][head_dim][16].  Scales: k_scale[num_kv_heads],
+ * v_scale[num_kv_heads], device fp32, positive and finite (unchecked): a
+ * cached value of KV head h stands for code * scale[h].
+ */
+
+/*
+ * pa_kv_write_fp8 -- quantising scatter of the step's new K and V into an
+ * E4M3 cache.  For every t < num_tokens with 0 <= s = slot_mapping[t] <
+ * num_blocks * 16 and every KV head h:
+ *   key_cache[s / 16][h][s % 16][j] = e4m3(clamp(key[t][h][j] / k_scale[h]))
+ * (and V dim-major), where the division is IEEE fp32 (key widened exactly
+ * from bf16 or fp32, `dtype`), clamp is to [-448, 448] and e4m3() rounds to
+ * the nearest code, ties to the even mantissa.  NaN inputs give a NaN code.
+ * Negative or out-of-pool slots write nothing.  Errors as pa_kv_write.
+ */
+pa_status pa_kv_write_fp8(const void* key, const void* value,
+                          void* key_cache, void* value_cache,
+                          const int64_t* slot_mapping,
+                          const float* k_scale, const float* v_scale,
+                          int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, int64_t num_blocks,
+                          pa_dtype dtype, void* stream);
+
+/*
+ * pa_attention_fwd_fp8 -- pa_attention_fwd over an E4M3 cache: every
+ * argument as there (query and out bf16, dtype implied), plus the cache's
+ * per-KV-head scales.  Computes exactly the attention of pa_attention_fwd
+ * with K[j] = code * k_scale[h] and V[j] = code * v_scale[h]; the codes are
+ * widened to bf16 exactly, k_scale folds into the score scale and v_scale
+ * multiplies the normalised output, so no extra rounding enters.  Same
+ * workspace (pa_attention_workspace_size), same split behaviour.
+ */
+pa_status pa_attention_fwd_fp8(const void* query, const void* key_cache,
+                               const void* value_cache,
+                               const float* k_scale, const float* v_scale,
+                               const int32_t* query_start_loc, const int32_t* seq_lens,
+                               const int32_t* block_tables,
+                               int32_t num_seqs, int32_t num_tokens,
+                               int32_t max_query_len, int32_t max_seq_len,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, int32_t block_table_stride,
+                               int64_t num_blocks, float scale, int32_t num_splits,
+                               void* out, float* lse, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
  * pa_attention_workspace_init -- zero `workspace_bytes` of a workspace on
  * `stream` with a kernel (no memset node, so it may be captured in a HIP
  * graph).  Needed once for a new workspace whose memory is not already zero.

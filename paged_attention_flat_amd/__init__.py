@@ -22,6 +22,7 @@ from ._lib import LIB, PA_BF16, PA_F32, PA_BLOCK_SIZE, PA_MAX_SPLITS  # noqa: F4
 
 __all__ = [
     "PaError", "kv_write", "attention", "split_combine", "workspace_size",
+    "kv_write_fp8", "attention_fp8", "alloc_cache_fp8",
     "choose_num_splits", "capture_size", "alloc_cache", "workspace", "trace_begin", "trace_end",
     "trace_read",
     "kernel_name", "version",
@@ -93,6 +94,95 @@ def kv_write(key, value, key_cache, value_cache, slot_mapping, stream=None) -> N
                          _dev(value_cache, "value_cache"), _dev(slot_mapping, "slot_mapping"),
                          nt, hkv, d, PA_BLOCK_SIZE, nb, _dtype_code(key), _stream(stream))
     _check(st, "pa_kv_write")
+
+
+_FP8_DTYPES = (torch.uint8,) + ((torch.float8_e4m3fn,) if hasattr(torch, "float8_e4m3fn") else ())
+
+
+def _check_fp8_cache(key_cache, value_cache, hkv, d):
+    nb = key_cache.shape[0]
+    if key_cache.dtype not in _FP8_DTYPES or value_cache.dtype not in _FP8_DTYPES:
+        raise ValueError("an FP8 cache holds E4M3 codes: uint8 or float8_e4m3fn tensors")
+    if tuple(key_cache.shape) != (nb, hkv, PA_BLOCK_SIZE, d) or \
+            tuple(value_cache.shape) != (nb, hkv, d, PA_BLOCK_SIZE):
+        raise ValueError("cache shapes must be [NB, Hkv, 16, d] and [NB, Hkv, d, 16]")
+    return nb
+
+
+def _check_scales(k_scale, v_scale, hkv):
+    for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+        if t.dtype != torch.float32 or tuple(t.shape) != (hkv,):
+            raise ValueError(f"{name} must be float32 [num_kv_heads]")
+
+
+def alloc_cache_fp8(num_blocks: int, num_kv_heads: int, head_dim: int, device="cuda"):
+    """Allocate an (uninitialised) E4M3 K and V cache pair (uint8 codes)."""
+    k = torch.empty(num_blocks, num_kv_heads, PA_BLOCK_SIZE, head_dim, dtype=torch.uint8,
+                    device=device)
+    v = torch.empty(num_blocks, num_kv_heads, head_dim, PA_BLOCK_SIZE, dtype=torch.uint8,
+                    device=device)
+    return k, v
+
+
+def kv_write_fp8(key, value, key_cache, value_cache, slot_mapping, k_scale, v_scale,
+                 stream=None) -> None:
+    """Quantise the step's new K/V ([Nt, Hkv, d], bf16 or fp32) into an E4M3
+    cache at their slots, with per-KV-head scales."""
+    nt, hkv, d = key.shape
+    if value.shape != key.shape or value.dtype != key.dtype:
+        raise ValueError("key and value must match")
+    nb = _check_fp8_cache(key_cache, value_cache, hkv, d)
+    _check_scales(k_scale, v_scale, hkv)
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (nt,):
+        raise ValueError("slot_mapping must be int64 [num_tokens]")
+    st = LIB.pa_kv_write_fp8(_dev(key, "key"), _dev(value, "value"),
+                             _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+                             _dev(slot_mapping, "slot_mapping"), _dev(k_scale, "k_scale"),
+                             _dev(v_scale, "v_scale"), nt, hkv, d, PA_BLOCK_SIZE, nb,
+                             _dtype_code(key), _stream(stream))
+    _check(st, "pa_kv_write_fp8")
+
+
+def attention_fp8(query, key_cache, value_cache, k_scale, v_scale, query_start_loc, seq_lens,
+                  block_tables, max_query_len: int, max_seq_len: int, scale: float,
+                  num_splits: int = 0, out=None, lse=None, want_lse: bool = True,
+                  workspace=None, stream=None):
+    """attention() over an E4M3 cache (bf16 query and output).  Returns (out, lse)."""
+    nt, hq, d = query.shape
+    hkv = key_cache.shape[1]
+    if query.dtype != torch.bfloat16:
+        raise ValueError("an FP8 cache is read with a bf16 query")
+    nb = _check_fp8_cache(key_cache, value_cache, hkv, d)
+    _check_scales(k_scale, v_scale, hkv)
+    for name, t in (("query_start_loc", query_start_loc), ("seq_lens", seq_lens),
+                    ("block_tables", block_tables)):
+        if t.dtype != torch.int32:
+            raise ValueError(f"{name} must be int32")
+    ns = seq_lens.shape[0]
+    if query_start_loc.shape != (ns + 1,) or block_tables.dim() != 2 or \
+            block_tables.shape[0] != ns:
+        raise ValueError("metadata shapes disagree")
+    splits = num_splits
+    if splits == 0:
+        splits = choose_num_splits(ns, max_query_len, max_seq_len, hq, hkv)
+    if out is None:
+        out = torch.empty_like(query)
+    if lse is None and want_lse:
+        lse = torch.empty(nt, hq, dtype=torch.float32, device=query.device)
+    need = workspace_size(ns, nt, hq, d, splits)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=query.device)
+    st = LIB.pa_attention_fwd_fp8(
+        _dev(query, "query"), _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+        _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"),
+        _dev(query_start_loc, "query_start_loc"), _dev(seq_lens, "seq_lens"),
+        _dev(block_tables, "block_tables"), ns, nt, int(max_query_len), int(max_seq_len),
+        hq, hkv, d, PA_BLOCK_SIZE, block_tables.shape[1], nb, float(scale), splits,
+        _dev(out, "out"), None if lse is None else _dev(lse, "lse"),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream))
+    _check(st, "pa_attention_fwd_fp8")
+    return out, lse
 
 
 def workspace_size(num_seqs: int, num_tokens: int, num_q_heads: int, head_dim: int,

@@ -5,8 +5,12 @@
 // sections "Never materialise the T x T matrix" (online softmax: running max m
 // and denominator l, accumulator rescaled by e^(m_old - m_new)), "Prefill has a
 // full grid; decode at batch 1 has almost none" (split-KV partials over block
-// ranges, merged by a second kernel) and "Attention over a block table, not a
-// contiguous tensor" (keys and values gathered through the block table).
+// ranges, merged in a second reduction -- here by the last split of each
+// request and KV head to finish, inside this launch) and "Attention over a
+// block table, not a contiguous tensor" (keys and values gathered through the
+// block table).  The cache holds bf16, or E4M3 codes with per-KV-head scales
+// (converted to bf16 exactly in registers; K's scale folds into the score
+// scale, V's into the output).
 //
 // MI355X design.  One work-group = (KV head, request, split); its eight waves
 // walk disjoint pairs of 16-token blocks of the split's range and each keeps
@@ -40,8 +44,10 @@ namespace {
 
 struct DecodeParams {
   const uint16_t* q;
-  const uint16_t* kc;
-  const uint16_t* vc;
+  const void* kc;         // bf16 elements, or E4M3 codes (F8 kernels)
+  const void* vc;
+  const float* k_scale;   // F8 kernels: per-KV-head dequantisation scales
+  const float* v_scale;
   const int32_t* qsl;
   const int32_t* seq_lens;
   const int32_t* tables;
@@ -118,9 +124,11 @@ __global__ __launch_bounds__(1024) void decode_order_kernel(const int32_t* __res
   }
 }
 
-template <int D, int G, int NW, int PIPE>
+template <int D, int G, int NW, int PIPE, bool F8>
 __global__ __launch_bounds__(64 * NW, (PIPE == 2 && NW < 8 ? 8 / NW : 1)) void decode_kernel(
     DecodeParams p) {
+  typedef typename Frag8<F8>::elem CT;
+  typedef typename Frag8<F8>::raw RT;
   constexpr int DQ = 16 / G;       // new tokens per request packed in the columns
   constexpr int KSTEPS = D / 32;   // MFMA steps over head_dim for S^T
   constexpr int DB = D / 16;       // 16-row blocks of O^T
@@ -184,8 +192,12 @@ __global__ __launch_bounds__(64 * NW, (PIPE == 2 && NW < 8 ? 8 / NW : 1)) void d
   const int rb = ra + 4;                       // second product
   const size_t head_elems = 16 * D;
   const size_t block_elems = (size_t)p.hkv * head_elems;
-  const uint16_t* kbase = p.kc + kvh * head_elems + 8 * kg;
-  const uint16_t* vbase = p.vc + kvh * head_elems + col * 16 + 8 * (kg & 1);
+  const CT* kbase = static_cast<const CT*>(p.kc) + kvh * head_elems + 8 * kg;
+  const CT* vbase = static_cast<const CT*>(p.vc) + kvh * head_elems + col * 16 + 8 * (kg & 1);
+  // E4M3 cache: a cached K value is code * k_scale, so the scale folds into
+  // the score scale; V's scale multiplies the normalised output
+  const float scale_log2 = F8 ? p.scale_log2 * p.k_scale[kvh] : p.scale_log2;
+  const float v_scale = F8 ? p.v_scale[kvh] : 1.f;
 
   float m = -INFINITY, l = 0.f;
   f32x4 acc[DB];
@@ -195,8 +207,8 @@ __global__ __launch_bounds__(64 * NW, (PIPE == 2 && NW < 8 ? 8 / NW : 1)) void d
   const int npairs = blk_hi > blk_lo ? (blk_hi - blk_lo + 1) >> 1 : 0;
 
   struct Frag {
-    bf16x8 a[KSTEPS], b[KSTEPS];
-    uint4 v[DB];
+    RT a[KSTEPS], b[KSTEPS];
+    RT v[DB];
   };
   auto load = [&](Frag& f, int pr) {
     const int rel = 2 * pr;  // block offset inside the split
@@ -212,16 +224,16 @@ __global__ __launch_bounds__(64 * NW, (PIPE == 2 && NW < 8 ? 8 / NW : 1)) void d
     const int phys0 = __builtin_amdgcn_readlane(tab, rel & 63);
     const int phys1 = has1 ? __builtin_amdgcn_readlane(tab, (rel & 63) + 1) : phys0;
     const int pa_ = ra < 16 ? phys0 : phys1, pb_ = rb < 16 ? phys0 : phys1;
-    const uint16_t* ka = kbase + (size_t)pa_ * block_elems + (ra & 15) * D;
-    const uint16_t* kb = kbase + (size_t)pb_ * block_elems + (rb & 15) * D;
-    const uint16_t* vp = vbase + (size_t)(kg < 2 ? phys0 : phys1) * block_elems;
+    const CT* ka = kbase + (size_t)pa_ * block_elems + (ra & 15) * D;
+    const CT* kb = kbase + (size_t)pb_ * block_elems + (rb & 15) * D;
+    const CT* vp = vbase + (size_t)(kg < 2 ? phys0 : phys1) * block_elems;
 #pragma unroll
     for (int st = 0; st < KSTEPS; ++st) {
-      f.a[st] = as_bf16x8(*reinterpret_cast<const uint4*>(ka + 32 * st));
-      f.b[st] = as_bf16x8(*reinterpret_cast<const uint4*>(kb + 32 * st));
+      f.a[st] = *reinterpret_cast<const RT*>(ka + 32 * st);
+      f.b[st] = *reinterpret_cast<const RT*>(kb + 32 * st);
     }
 #pragma unroll
-    for (int db = 0; db < DB; ++db) f.v[db] = *reinterpret_cast<const uint4*>(vp + db * 256);
+    for (int db = 0; db < DB; ++db) f.v[db] = *reinterpret_cast<const RT*>(vp + db * 256);
   };
   auto compute = [&](Frag& f, int pr) {
     const int j0 = blk_lo + 2 * pr;
@@ -229,8 +241,10 @@ __global__ __launch_bounds__(64 * NW, (PIPE == 2 && NW < 8 ? 8 / NW : 1)) void d
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int st = 0; st < KSTEPS; ++st) {
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[st], qf[st], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.b[st], qf[st], s1, 0, 0, 0);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Frag8<F8>::bits(f.a[st])), qf[st], s0,
+                                                   0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Frag8<F8>::bits(f.b[st])), qf[st], s1,
+                                                   0, 0, 0);
     }
     // lane (col, kg): sv[e] is the score of pair key 8*kg + e
     float sv[8];
@@ -250,28 +264,36 @@ __global__ __launch_bounds__(64 * NW, (PIPE == 2 && NW < 8 ? 8 / NW : 1)) void d
       for (int e = 0; e < 8; ++e) {
         const int kp = kp0 + e;
         if (!blk_ok || kp > qpos) sv[e] = -INFINITY;
-        if (!blk_ok || kp >= seq_len) vm[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+        if (!blk_ok || kp >= seq_len) {
+          if constexpr (F8) vm[e >> 2] &= ~(0xffu << (8 * (e & 3)));  // code 0 = +0
+          else vm[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+        }
       }
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        f.v[db].x &= vm[0];
-        f.v[db].y &= vm[1];
-        f.v[db].z &= vm[2];
-        f.v[db].w &= vm[3];
+        if constexpr (F8) {
+          f.v[db].x &= vm[0];
+          f.v[db].y &= vm[1];
+        } else {
+          f.v[db].x &= vm[0];
+          f.v[db].y &= vm[1];
+          f.v[db].z &= vm[2];
+          f.v[db].w &= vm[3];
+        }
       }
     }
     float mt = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
                      fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
     mt = fmaxf(mt, shfl_xor(mt, 16));
     mt = fmaxf(mt, shfl_xor(mt, 32));
-    mt *= p.scale_log2;  // scale > 0 commutes with max
+    mt *= scale_log2;  // scale > 0 commutes with max
     const float m_new = fmaxf(m, mt);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     const float alpha = fast_exp2(m - m_use);
     float pv[8], rs = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      pv[i] = fast_exp2(__builtin_fmaf(sv[i], p.scale_log2, -m_use));
+      pv[i] = fast_exp2(__builtin_fmaf(sv[i], scale_log2, -m_use));
       rs += pv[i];
     }
     l = l * alpha + rs;
@@ -282,7 +304,8 @@ __global__ __launch_bounds__(64 * NW, (PIPE == 2 && NW < 8 ? 8 / NW : 1)) void d
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       acc[db] *= alpha;
-      acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(f.v[db]), pf, acc[db], 0, 0, 0);
+      acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Frag8<F8>::bits(f.v[db])), pf,
+                                                        acc[db], 0, 0, 0);
     }
   };
 
@@ -348,7 +371,7 @@ __global__ __launch_bounds__(64 * NW, (PIPE == 2 && NW < 8 ? 8 / NW : 1)) void d
   const int h = kvh * G + g;
   if (wave == 0 && col_valid) {
     if (p.splits == 1) {
-      const float inv = 1.f / l;
+      const float inv = v_scale / l;
       uint16_t* dst = p.out + ((size_t)t * p.hq + h) * D + 4 * kg;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -358,7 +381,7 @@ __global__ __launch_bounds__(64 * NW, (PIPE == 2 && NW < 8 ? 8 / NW : 1)) void d
       if (p.lse != nullptr && kg == 0) p.lse[(size_t)t * p.hq + h] = (m + fast_log2(l)) * kLn2;
     } else {
       const bool empty = (l == 0.f);
-      const float inv = empty ? 0.f : 1.f / l;
+      const float inv = empty ? 0.f : v_scale / l;
       float* dst = p.part_out + (((size_t)split * p.nt + t) * p.hq + h) * D + 4 * kg;
       // device-scope atomic stores write through this XCD's L2, so the
       // merging work-group (possibly on another XCD) reads them from memory
@@ -493,12 +516,14 @@ __global__ __launch_bounds__(64 * NW, (PIPE == 2 && NW < 8 ? 8 / NW : 1)) void d
   if (threadIdx.x == 0) __hip_atomic_store(sem, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int D, int G>
+template <int D, int G, bool F8>
 void launch_dg(const AttnArgs& a, hipStream_t stream) {
   DecodeParams p;
   p.q = (const uint16_t*)a.q;
-  p.kc = (const uint16_t*)a.kc;
-  p.vc = (const uint16_t*)a.vc;
+  p.kc = a.kc;
+  p.vc = a.vc;
+  p.k_scale = a.k_scale;
+  p.v_scale = a.v_scale;
   p.qsl = a.qsl;
   p.seq_lens = a.seq_lens;
   p.tables = a.tables;
@@ -534,30 +559,35 @@ void launch_dg(const AttnArgs& a, hipStream_t stream) {
   trace_before(a.splits > 1 ? K_DECODE_SPLIT : K_DECODE, stream);
   if (units <= 2 * (int64_t)a.num_cus) {
     constexpr int NW = PA_DECODE_WAVES_PIPE;
-    hipLaunchKernelGGL((decode_kernel<D, G, NW, 2>), grid, dim3(64 * NW), 0, stream, p);
+    hipLaunchKernelGGL((decode_kernel<D, G, NW, 2, F8>), grid, dim3(64 * NW), 0, stream, p);
   } else {
     constexpr int NW = PA_DECODE_WAVES_WIDE;
-    hipLaunchKernelGGL((decode_kernel<D, G, NW, 1>), grid, dim3(64 * NW), 0, stream, p);
+    hipLaunchKernelGGL((decode_kernel<D, G, NW, 1, F8>), grid, dim3(64 * NW), 0, stream, p);
   }
   trace_after(stream);
 }
 
-template <int D>
+template <int D, bool F8>
 void launch_d(const AttnArgs& a, hipStream_t stream) {
   switch (a.hq / a.hkv) {
-    case 1: launch_dg<D, 1>(a, stream); break;
-    case 2: launch_dg<D, 2>(a, stream); break;
-    case 4: launch_dg<D, 4>(a, stream); break;
-    case 8: launch_dg<D, 8>(a, stream); break;
-    default: launch_dg<D, 16>(a, stream); break;
+    case 1: launch_dg<D, 1, F8>(a, stream); break;
+    case 2: launch_dg<D, 2, F8>(a, stream); break;
+    case 4: launch_dg<D, 4, F8>(a, stream); break;
+    case 8: launch_dg<D, 8, F8>(a, stream); break;
+    default: launch_dg<D, 16, F8>(a, stream); break;
   }
 }
 
 }  // namespace
 
 hipError_t launch_decode_bf16(const AttnArgs& a, hipStream_t stream) {
-  if (a.d == 64) launch_d<64>(a, stream);
-  else launch_d<128>(a, stream);
+  if (a.cache_fp8) {
+    if (a.d == 64) launch_d<64, true>(a, stream);
+    else launch_d<128, true>(a, stream);
+  } else {
+    if (a.d == 64) launch_d<64, false>(a, stream);
+    else launch_d<128, false>(a, stream);
+  }
   return hipGetLastError();
 }
 

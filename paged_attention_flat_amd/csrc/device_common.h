@@ -42,6 +42,35 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint2 lo, uint2 hi) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// Eight E4M3 codes (bytes 0..7 of v) to eight bf16, exactly (every E4M3
+// value is a bf16 value): four v_cvt_scalef32_pk_bf16_fp8 at scale 1.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint2 v) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, true);
+  return bf16x8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
+
+// Cache fragments of eight elements: raw bits as loaded (16 bytes of bf16 or
+// 8 bytes of E4M3 codes) and their bf16 operand form.
+template <bool F8>
+struct Frag8;
+template <>
+struct Frag8<false> {
+  typedef uint16_t elem;
+  typedef uint4 raw;
+  static __device__ __forceinline__ uint4 bits(raw r) { return r; }
+};
+template <>
+struct Frag8<true> {
+  typedef uint8_t elem;
+  typedef uint2 raw;
+  static __device__ __forceinline__ uint4 bits(raw r) {
+    return __builtin_bit_cast(uint4, e4m3x8_to_bf16x8(r));
+  }
+};
+
 // Cross-lane exchange inside a wave64 (ds_bpermute based).
 __device__ __forceinline__ float shfl_xor(float v, int mask) {
   return __shfl_xor(v, mask, 64);

@@ -159,6 +159,7 @@ const char* pa_kernel_name(int32_t id) {
     case K_F32_ATTN_SPLIT: return "attn_f32_split_partial";
     case K_DECODE_ORDER: return "decode_order";
     case K_ZERO: return "workspace_zero";
+    case K_KV_WRITE_FP8: return "kv_write_fp8";
   }
   return "unknown";
 }
@@ -285,14 +286,21 @@ pa_status pa_split_combine(const float* partial_out, const float* partial_lse,
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
-pa_status pa_attention_fwd(const void* query, const void* key_cache, const void* value_cache,
-                           const int32_t* query_start_loc, const int32_t* seq_lens,
-                           const int32_t* block_tables, int32_t num_seqs, int32_t num_tokens,
-                           int32_t max_query_len, int32_t max_seq_len, int32_t num_q_heads,
-                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                           int32_t block_table_stride, int64_t num_blocks, float scale,
-                           int32_t num_splits, void* out, float* lse, void* workspace,
-                           size_t workspace_bytes, pa_dtype dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by pa_attention_fwd (cache in the query dtype) and
+// pa_attention_fwd_fp8 (E4M3 cache with per-KV-head scales, bf16 query).
+pa_status attention_impl(const void* query, const void* key_cache, const void* value_cache,
+                         const float* k_scale, const float* v_scale,
+                         const int32_t* query_start_loc, const int32_t* seq_lens,
+                         const int32_t* block_tables, int32_t num_seqs, int32_t num_tokens,
+                         int32_t max_query_len, int32_t max_seq_len, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         int32_t block_table_stride, int64_t num_blocks, float scale,
+                         int32_t num_splits, void* out, float* lse, void* workspace,
+                         size_t workspace_bytes, pa_dtype dtype, bool cache_fp8, void* stream) {
   if (num_seqs < 0 || num_tokens < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
       num_blocks <= 0 || num_splits < 0 || num_splits > PA_MAX_SPLITS || !std::isfinite(scale) ||
       !(scale > 0.f))
@@ -310,6 +318,7 @@ pa_status pa_attention_fwd(const void* query, const void* key_cache, const void*
   if (!query || !key_cache || !value_cache || !query_start_loc || !seq_lens || !block_tables ||
       !out)
     return PA_ERR_NULL;
+  if (cache_fp8 && (!k_scale || !v_scale)) return PA_ERR_NULL;
   if (!aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache) || !aligned16(out))
     return PA_ERR_INVALID;
 
@@ -356,6 +365,9 @@ pa_status pa_attention_fwd(const void* query, const void* key_cache, const void*
   a.decode_order = nullptr;
   if ((int64_t)num_seqs * num_kv_heads * splits > a.num_cus && num_seqs >= 64)
     a.decode_order = reinterpret_cast<int32_t*>(ws + lay.order);
+  a.cache_fp8 = cache_fp8 ? 1 : 0;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
   a.part_out = nullptr;
   a.part_lse = nullptr;
   a.sem = nullptr;
@@ -378,6 +390,62 @@ pa_status pa_attention_fwd(const void* query, const void* key_cache, const void*
     if (max_query_len > dq) e = launch_prefill_bf16(a, s);
     if (e == hipSuccess) e = launch_decode_bf16(a, s);
   }
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_attention_fwd(const void* query, const void* key_cache, const void* value_cache,
+                           const int32_t* query_start_loc, const int32_t* seq_lens,
+                           const int32_t* block_tables, int32_t num_seqs, int32_t num_tokens,
+                           int32_t max_query_len, int32_t max_seq_len, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int32_t block_table_stride, int64_t num_blocks, float scale,
+                           int32_t num_splits, void* out, float* lse, void* workspace,
+                           size_t workspace_bytes, pa_dtype dtype, void* stream) {
+  return attention_impl(query, key_cache, value_cache, nullptr, nullptr, query_start_loc,
+                        seq_lens, block_tables, num_seqs, num_tokens, max_query_len, max_seq_len,
+                        num_q_heads, num_kv_heads, head_dim, block_size, block_table_stride,
+                        num_blocks, scale, num_splits, out, lse, workspace, workspace_bytes,
+                        dtype, false, stream);
+}
+
+pa_status pa_attention_fwd_fp8(const void* query, const void* key_cache,
+                               const void* value_cache, const float* k_scale,
+                               const float* v_scale, const int32_t* query_start_loc,
+                               const int32_t* seq_lens, const int32_t* block_tables,
+                               int32_t num_seqs, int32_t num_tokens, int32_t max_query_len,
+                               int32_t max_seq_len, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size, int32_t block_table_stride,
+                               int64_t num_blocks, float scale, int32_t num_splits, void* out,
+                               float* lse, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  return attention_impl(query, key_cache, value_cache, k_scale, v_scale, query_start_loc,
+                        seq_lens, block_tables, num_seqs, num_tokens, max_query_len, max_seq_len,
+                        num_q_heads, num_kv_heads, head_dim, block_size, block_table_stride,
+                        num_blocks, scale, num_splits, out, lse, workspace, workspace_bytes,
+                        PA_BF16, true, stream);
+}
+
+pa_status pa_kv_write_fp8(const void* key, const void* value, void* key_cache, void* value_cache,
+                          const int64_t* slot_mapping, const float* k_scale, const float* v_scale,
+                          int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, int64_t num_blocks, pa_dtype dtype, void* stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_INVALID;
+  if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_INVALID;
+  if (block_size != PA_BLOCK_SIZE) return PA_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping || !k_scale || !v_scale)
+    return PA_ERR_NULL;
+  if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) || !aligned16(value_cache))
+    return PA_ERR_INVALID;
+  const int32_t esize = dtype == PA_BF16 ? 2 : 4;
+  hipError_t e = launch_kv_write_fp8(key, value, key_cache, value_cache, slot_mapping, k_scale,
+                                     v_scale, num_tokens, num_kv_heads, head_dim, esize,
+                                     num_blocks, (hipStream_t)stream);
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

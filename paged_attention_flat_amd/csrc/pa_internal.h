@@ -19,7 +19,8 @@ enum KernelId : int32_t {
   K_F32_ATTN_SPLIT = 7,
   K_DECODE_ORDER = 8,
   K_ZERO = 9,
-  K_COUNT = 10
+  K_KV_WRITE_FP8 = 10,
+  K_COUNT = 11
 };
 
 // Tracing hooks (pa_api.cpp).  trace_before/after bracket one launch.
@@ -31,6 +32,12 @@ hipError_t launch_kv_write(const void* key, const void* value, void* kc, void* v
                            const int64_t* slots, int32_t nt, int32_t hkv,
                            int32_t d, int32_t esize, int64_t num_blocks,
                            hipStream_t stream);
+// Quantising write into an E4M3 cache (one byte per element), per-KV-head
+// float scales: code = e4m3(clamp(x / scale[h], -448, 448)), ties to even.
+hipError_t launch_kv_write_fp8(const void* key, const void* value, void* kc, void* vc,
+                               const int64_t* slots, const float* k_scale,
+                               const float* v_scale, int32_t nt, int32_t hkv, int32_t d,
+                               int32_t esize, int64_t num_blocks, hipStream_t stream);
 
 struct AttnArgs {
   const void* q;
@@ -53,6 +60,9 @@ struct AttnArgs {
   int32_t* decode_order;  // nullable: count + ranked decode requests
   int32_t num_cus;        // compute units of the current device
   int32_t* sem;           // nullable: zeroed arrival counters, one per (request, KV head)
+  int32_t cache_fp8;      // 1: kc / vc hold E4M3 codes (query and out bf16)
+  const float* k_scale;   // [hkv] when cache_fp8: a cached K value is code * k_scale[h]
+  const float* v_scale;   // [hkv] when cache_fp8
 };
 
 // Largest number of new tokens per request that the decode kernel packs.

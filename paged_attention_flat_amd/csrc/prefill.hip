@@ -46,8 +46,10 @@ namespace {
 
 struct PrefillParams {
   const uint16_t* q;
-  const uint16_t* kc;
-  const uint16_t* vc;
+  const void* kc;         // bf16 elements, or E4M3 codes (F8 kernels)
+  const void* vc;
+  const float* k_scale;   // F8 kernels: per-KV-head dequantisation scales
+  const float* v_scale;
   const int32_t* qsl;
   const int32_t* seq_lens;
   const int32_t* tables;
@@ -151,8 +153,10 @@ __device__ __forceinline__ int vperm(int k) {
   return (k & 3) | ((k & 4) << 1) | ((k & 8) >> 1);
 }
 
-template <int D, int G, int NW, int RG, int kBK>
+template <int D, int G, int NW, int RG, int kBK, bool F8>
 __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
+  typedef typename Frag8<F8>::elem CT;
+  typedef typename Frag8<F8>::raw RT;
   constexpr int KB = kBK / 32;            // 32-key halves per tile
   constexpr int PS = kBK / 16;            // 16-key P.V steps per tile
   constexpr int NT = 64 * NW;             // threads
@@ -214,8 +218,12 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
   const int32_t* table = p.tables + (size_t)b * p.table_stride;
   const size_t head_elems = 16 * D;
   const size_t block_elems = (size_t)p.hkv * head_elems;
-  const uint16_t* kbase = p.kc + kvh * head_elems;
-  const uint16_t* vbase = p.vc + kvh * head_elems;
+  const CT* kbase = static_cast<const CT*>(p.kc) + kvh * head_elems;
+  const CT* vbase = static_cast<const CT*>(p.vc) + kvh * head_elems;
+  // E4M3 cache: K's scale folds into the score scale, V's into the output;
+  // the codes become bf16 exactly when a tile is staged into LDS
+  const float scale_log2 = F8 ? p.scale_log2 * p.k_scale[kvh] : p.scale_log2;
+  const float v_scale = F8 ? p.v_scale[kvh] : 1.f;
 
   // ---- staging: global -> registers -> LDS --------------------------------
   // Per-thread chunk geometry is fixed; only the tile's first block moves.
@@ -243,44 +251,52 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
     v_dst[i] = d * (kBK + kVPad) + bi * 16;
   }
   int tab_base = 0;
-  uint4 kr[KCH], vr[VCH];
+  RT kr[KCH], vr[VCH];
   auto gload = [&](int k0) {
     const int tb = (k0 >> 4) - tab_base;
     if (k0 + kBK <= seq_len) {
       // whole tile inside the context: no per-key checks
 #pragma unroll
       for (int i = 0; i < KCH; ++i)
-        kr[i] = *reinterpret_cast<const uint4*>(kbase + (size_t)s_tab[tb + k_blk[i]] * block_elems +
-                                                k_src[i]);
+        kr[i] = *reinterpret_cast<const RT*>(kbase + (size_t)s_tab[tb + k_blk[i]] * block_elems +
+                                              k_src[i]);
 #pragma unroll
       for (int i = 0; i < VCH; ++i)
-        vr[i] = *reinterpret_cast<const uint4*>(vbase + (size_t)s_tab[tb + v_blk[i]] * block_elems +
-                                                v_src[i]);
+        vr[i] = *reinterpret_cast<const RT*>(vbase + (size_t)s_tab[tb + v_blk[i]] * block_elems +
+                                              v_src[i]);
       return;
     }
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
       const int kpos = k0 + (k_src[i] / D) + 16 * k_blk[i];
-      uint4 v = make_uint4(0, 0, 0, 0);
+      RT v = {};
       if (kpos < seq_len)
-        v = *reinterpret_cast<const uint4*>(kbase + (size_t)s_tab[tb + k_blk[i]] * block_elems +
-                                            k_src[i]);
+        v = *reinterpret_cast<const RT*>(kbase + (size_t)s_tab[tb + k_blk[i]] * block_elems +
+                                         k_src[i]);
       kr[i] = v;
     }
 #pragma unroll
     for (int i = 0; i < VCH; ++i) {
       const int kpos = k0 + v_key[i];
-      uint4 v = make_uint4(0, 0, 0, 0);
+      RT v = {};
       if (kpos < seq_len) {
-        v = *reinterpret_cast<const uint4*>(vbase + (size_t)s_tab[tb + v_blk[i]] * block_elems +
-                                            v_src[i]);
+        v = *reinterpret_cast<const RT*>(vbase + (size_t)s_tab[tb + v_blk[i]] * block_elems +
+                                         v_src[i]);
         if (kpos + 8 > seq_len) {
           // keys past the context may hold anything (even NaN): zero them
-          uint32_t w[4] = {v.x, v.y, v.z, v.w};
+          if constexpr (F8) {
+            uint32_t w[2] = {v.x, v.y};
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (kpos + e >= seq_len) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-          v = make_uint4(w[0], w[1], w[2], w[3]);
+            for (int e = 0; e < 8; ++e)
+              if (kpos + e >= seq_len) w[e >> 2] &= ~(0xffu << (8 * (e & 3)));  // code 0 = +0
+            v = make_uint2(w[0], w[1]);
+          } else {
+            uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (kpos + e >= seq_len) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+            v = make_uint4(w[0], w[1], w[2], w[3]);
+          }
         }
       }
       vr[i] = v;
@@ -290,14 +306,16 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
     uint16_t* k_lds = &sK[kbuf][0][0];
     uint16_t* v_lds = &sV[vbuf][0][0];
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) *reinterpret_cast<uint4*>(k_lds + k_dst[i]) = kr[i];
+    for (int i = 0; i < KCH; ++i)
+      *reinterpret_cast<uint4*>(k_lds + k_dst[i]) = Frag8<F8>::bits(kr[i]);
 #pragma unroll
     for (int i = 0; i < VCH; ++i) {
       // keys 8*half .. +3 and +4 .. +7 of the block go to their permuted slots
       const int h8 = v_key[i] & 8;
       uint16_t* dst = v_lds + v_dst[i];
-      *reinterpret_cast<uint2*>(dst + vperm(h8)) = make_uint2(vr[i].x, vr[i].y);
-      *reinterpret_cast<uint2*>(dst + vperm(h8 + 4)) = make_uint2(vr[i].z, vr[i].w);
+      const uint4 vv = Frag8<F8>::bits(vr[i]);
+      *reinterpret_cast<uint2*>(dst + vperm(h8)) = make_uint2(vv.x, vv.y);
+      *reinterpret_cast<uint2*>(dst + vperm(h8 + 4)) = make_uint2(vv.z, vv.w);
     }
   };
 
@@ -438,7 +456,7 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
 #pragma unroll
         for (int u = 0; u < w / 2; ++u) mx[u] = fmaxf(mx[u], mx[u + w / 2]);
       float mt = mx[0];
-      mt = fmaxf(mt, shfl_xor(mt, 32)) * p.scale_log2;  // scale > 0 commutes with max
+      mt = fmaxf(mt, shfl_xor(mt, 32)) * scale_log2;  // scale > 0 commutes with max
       move[rg] = __ballot(mt > m[rg] + kLazy) != 0;
       // finite once the wave has met key 0, which every row sees
       m_new[rg] = move[rg] ? fmaxf(m[rg], mt) : m[rg];
@@ -453,7 +471,7 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          s[rg][kb][j] = fast_exp2(__builtin_fmaf(s[rg][kb][j], p.scale_log2, -m_new[rg]));
+          s[rg][kb][j] = fast_exp2(__builtin_fmaf(s[rg][kb][j], scale_log2, -m_new[rg]));
           ps4[j & 3] += s[rg][kb][j];
         }
       const float rs = (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
@@ -490,7 +508,7 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
   for (int rg = 0; rg < RG; ++rg) {
     const float lt = l[rg] + shfl_xor(l[rg], 32);
     if (!valid[rg]) continue;
-    const float inv = 1.f / lt;
+    const float inv = v_scale / lt;
     const int t = q0 + tokr[rg];
     const int h = kvh * G + gr[rg];
     uint16_t* orow = p.out + ((size_t)t * p.hq + h) * D;
@@ -509,15 +527,17 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
   }
 }
 
-template <int D, int G>
+template <int D, int G, bool F8>
 void launch_dg(const AttnArgs& a, hipStream_t stream) {
   constexpr int NW = PA_PREFILL_WAVES;
   constexpr int RG = PA_PREFILL_ROW_GROUPS;
   constexpr int BK = PA_PREFILL_KEYS;
   PrefillParams p;
   p.q = (const uint16_t*)a.q;
-  p.kc = (const uint16_t*)a.kc;
-  p.vc = (const uint16_t*)a.vc;
+  p.kc = a.kc;
+  p.vc = a.vc;
+  p.k_scale = a.k_scale;
+  p.v_scale = a.v_scale;
   p.qsl = a.qsl;
   p.seq_lens = a.seq_lens;
   p.tables = a.tables;
@@ -536,27 +556,32 @@ void launch_dg(const AttnArgs& a, hipStream_t stream) {
                      a.plan_cap);
   trace_after(stream);
   trace_before(K_PREFILL, stream);
-  hipLaunchKernelGGL((prefill_kernel<D, G, NW, RG, BK>), dim3(a.plan_cap * a.hkv), dim3(64 * NW), 0,
-                     stream, p);
+  hipLaunchKernelGGL((prefill_kernel<D, G, NW, RG, BK, F8>), dim3(a.plan_cap * a.hkv),
+                     dim3(64 * NW), 0, stream, p);
   trace_after(stream);
 }
 
-template <int D>
+template <int D, bool F8>
 void launch_d(const AttnArgs& a, hipStream_t stream) {
   switch (a.hq / a.hkv) {
-    case 1: launch_dg<D, 1>(a, stream); break;
-    case 2: launch_dg<D, 2>(a, stream); break;
-    case 4: launch_dg<D, 4>(a, stream); break;
-    case 8: launch_dg<D, 8>(a, stream); break;
-    default: launch_dg<D, 16>(a, stream); break;
+    case 1: launch_dg<D, 1, F8>(a, stream); break;
+    case 2: launch_dg<D, 2, F8>(a, stream); break;
+    case 4: launch_dg<D, 4, F8>(a, stream); break;
+    case 8: launch_dg<D, 8, F8>(a, stream); break;
+    default: launch_dg<D, 16, F8>(a, stream); break;
   }
 }
 
 }  // namespace
 
 hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t stream) {
-  if (a.d == 64) launch_d<64>(a, stream);
-  else launch_d<128>(a, stream);
+  if (a.cache_fp8) {
+    if (a.d == 64) launch_d<64, true>(a, stream);
+    else launch_d<128, true>(a, stream);
+  } else {
+    if (a.d == 64) launch_d<64, false>(a, stream);
+    else launch_d<128, false>(a, stream);
+  }
   return hipGetLastError();
 }
 

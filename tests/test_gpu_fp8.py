@@ -1,0 +1,182 @@
+"""GPU parity of the FP8 (E4M3) KV cache against the fp64 oracle.
+
+* the quantising KV write: every code bit-exact (both sides divide in fp32
+  and round to nearest-even, ties to even; inputs span subnormal codes to
+  saturation);
+* attention over the E4M3 cache: output within 2e-2, lse within 1e-3 of the
+  oracle's attention over the dequantised pools (code * scale, exact).
+Pools are poisoned with the NaN code 0x7F outside the prior context.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import Request, build_step, config_step, fp8_cache, raw_numpy
+
+pytestmark = pytest.mark.gpu
+
+TOL_OUT = 2e-2
+TOL_LSE = 1e-3
+# supplementary: relative Frobenius error; bf16 rounding of P and of the
+# output gives ~1e-3, while a zeroed or mis-scaled output (which can pass the
+# absolute bar when long contexts average the output toward 0) gives ~1
+TOL_REL = 2e-2
+
+SMALL = {
+    2: {"context": 1000, "pool_blocks": 200},
+    3: {"batch": 12, "lo": 40, "hi": 700},
+    4: {"batch": 2, "new": 300, "pool_blocks": 48},
+    5: {"chunk": 90, "priors": (70, 300), "decodes": 40, "lo": 20, "hi": 900,
+        "prefix": 64, "sharers": 10, "stride": 64},
+}
+
+
+def upload(step, dev="cuda"):
+    g = {n: getattr(step, n).to(dev).contiguous()
+         for n in ("query", "key", "value", "k_pool", "v_pool", "k_scale", "v_scale")}
+    g["qsl"] = torch.as_tensor(step.query_start_loc).to(dev)
+    g["seq_lens"] = torch.as_tensor(step.seq_lens).to(dev)
+    g["tables"] = torch.as_tensor(step.block_tables).to(dev)
+    g["slots"] = torch.as_tensor(step.slot_mapping).to(dev)
+    return g
+
+
+def run_gpu(step, num_splits=0, g=None):
+    import paged_attention_flat_amd as pa
+    g = g or upload(step)
+    pa.kv_write_fp8(g["key"], g["value"], g["k_pool"], g["v_pool"], g["slots"], g["k_scale"],
+                    g["v_scale"])
+    out = torch.full_like(g["query"], float("nan"))
+    out, lse = pa.attention_fp8(g["query"], g["k_pool"], g["v_pool"], g["k_scale"],
+                                g["v_scale"], g["qsl"], g["seq_lens"], g["tables"],
+                                step.max_query_len, step.max_seq_len, step.scale,
+                                num_splits=num_splits, out=out)
+    torch.cuda.synchronize()
+    return out, lse, g
+
+
+def oracle_write(step):
+    return oracle.kv_write_fp8(raw_numpy(step.key), raw_numpy(step.value),
+                               raw_numpy(step.k_pool), raw_numpy(step.v_pool),
+                               step.slot_mapping, step.k_scale.cpu().numpy(),
+                               step.v_scale.cpu().numpy(), step.dtype)
+
+
+def oracle_attn(step, kp, vp, rows=None):
+    return oracle.attention_fp8(raw_numpy(step.query), kp, vp, step.k_scale.cpu().numpy(),
+                                step.v_scale.cpu().numpy(), step.query_start_loc,
+                                step.seq_lens, step.block_tables, step.scale,
+                                step.num_kv_heads, query_dtype=step.dtype, rows=rows)
+
+
+def check(step, out, lse, ro, rl, rows=None, what=""):
+    rows = np.arange(int(step.query_start_loc[-1])) if rows is None else np.asarray(rows)
+    o = out.float().cpu().double().numpy()[rows]
+    assert np.isfinite(o).all(), f"{what}: non-finite output"
+    err = float(np.abs(o - ro[rows]).max())
+    assert err <= TOL_OUT, f"{what}: max |out - oracle| = {err}"
+    rel = float(np.linalg.norm(o - ro[rows]) / max(np.linalg.norm(ro[rows]), 1e-30))
+    assert rel <= TOL_REL, f"{what}: |out - oracle| / |oracle| = {rel}"
+    le = float(np.abs(lse.cpu().double().numpy()[rows] - rl[rows]).max())
+    assert le <= TOL_LSE, f"{what}: max |lse - oracle| = {le}"
+
+
+def same_codes(gpu, ref):
+    return np.array_equal(gpu.cpu().numpy(), np.asarray(ref, dtype=np.uint8))
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_fp8_kv_write_bit_exact(cfg):
+    step = fp8_cache(config_step(cfg, scale_down=SMALL[cfg]), cfg)
+    import paged_attention_flat_amd as pa
+    g = upload(step)
+    pa.kv_write_fp8(g["key"], g["value"], g["k_pool"], g["v_pool"], g["slots"], g["k_scale"],
+                    g["v_scale"])
+    torch.cuda.synchronize()
+    kp, vp = oracle_write(step)
+    assert same_codes(g["k_pool"], kp) and same_codes(g["v_pool"], vp)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_fp8_kv_write_full_range(dtype):
+    # magnitudes from far below the smallest subnormal to far past 448, and
+    # padded / out-of-pool slots that must write nothing
+    import paged_attention_flat_amd as pa
+    reqs = [Request(0, 40, [3, 0, 5]), Request(7, 9, [1, 6])]
+    step = build_step("range", reqs, dtype=dtype, num_q_heads=4, num_kv_heads=2, head_dim=128,
+                      num_blocks=8, seed=21, pad_tokens=3)
+    step = fp8_cache(step, 21)
+    dt = step.torch_dtype
+    mag = torch.exp2(torch.linspace(-14, 12, 128)).to(dt)
+    step.key = (step.key.float().sign() * mag).to(dt)
+    step.value = (step.value.float() * mag.flip(0)).to(dt)
+    bad = step.slot_mapping.copy()
+    bad[-3:] = [8 * 16, 8 * 16 + 3, 1 << 40]
+    step.slot_mapping = bad
+    g = upload(step)
+    pa.kv_write_fp8(g["key"], g["value"], g["k_pool"], g["v_pool"], g["slots"], g["k_scale"],
+                    g["v_scale"])
+    torch.cuda.synchronize()
+    good = step.slot_mapping.copy()
+    good[good >= 8 * 16] = -1
+    step.slot_mapping = good
+    kp, vp = oracle_write(step)
+    assert same_codes(g["k_pool"], kp) and same_codes(g["v_pool"], vp)
+    codes = np.concatenate([kp.ravel(), vp.ravel()])
+    assert (codes & 0x7F == 0x7E).any(), "saturation not exercised"
+    assert ((codes & 0x78) == 0).any(), "subnormal codes not exercised"
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_fp8_attention_small_configs(cfg):
+    step = fp8_cache(config_step(cfg, scale_down=SMALL[cfg]), cfg)
+    out, lse, g = run_gpu(step)
+    kp, vp = oracle_write(step)
+    assert same_codes(g["k_pool"], kp) and same_codes(g["v_pool"], vp)
+    ro, rl = oracle_attn(step, kp, vp)
+    check(step, out, lse, ro, rl, what=f"fp8 config{cfg} small")
+
+
+@pytest.mark.parametrize("splits", [1, 3, 32])
+def test_fp8_split_sweep(splits):
+    step = fp8_cache(config_step(2, scale_down=SMALL[2]), 2)
+    out, lse, g = run_gpu(step, num_splits=splits)
+    kp, vp = oracle_write(step)
+    ro, rl = oracle_attn(step, kp, vp)
+    check(step, out, lse, ro, rl, what=f"fp8 decode S={splits}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("hq,hkv", [(8, 4), (16, 1), (32, 4)])
+def test_fp8_head_dims_and_groups(d, hq, hkv):
+    rng = np.random.default_rng(hq * 10 + d)
+    shapes = [(45, 70), (130, 1), (17, 2), (0, 33), (12, 0)]
+    need = [-(-(p + n) // 16) for p, n in shapes]
+    nb = sum(need) + 4
+    perm = rng.permutation(nb)
+    tables, k = [], 0
+    for n in need:
+        tables.append(list(perm[k:k + n]))
+        k += n
+    step = build_step("mix8", [Request(p, n, t) for (p, n), t in zip(shapes, tables)],
+                      dtype="bf16", num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                      num_blocks=nb, seed=int(rng.integers(1 << 30)), pad_tokens=2)
+    step = fp8_cache(step, 9)
+    for splits in (1, 4):
+        out, lse, g = run_gpu(step, num_splits=splits)
+        kp, vp = oracle_write(step)
+        ro, rl = oracle_attn(step, kp, vp)
+        check(step, out, lse, ro, rl, what=f"fp8 d={d} G={hq // hkv} S={splits}")
+        assert torch.isnan(out[-2:]).all()
+
+
+def test_fp8_full_long_decode():
+    # the full-size long single decode (1 x 32768) in the benchmark's launch
+    step = fp8_cache(config_step(2), 2)
+    out, lse, g = run_gpu(step)
+    kp, vp = oracle_write(step)
+    assert same_codes(g["k_pool"], kp) and same_codes(g["v_pool"], vp)
+    ro, rl = oracle_attn(step, kp, vp)
+    check(step, out, lse, ro, rl, what="fp8 full long decode")

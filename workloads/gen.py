@@ -63,6 +63,9 @@ class StepInputs:
     k_pool: torch.Tensor = None     # [NB, Hkv, 16, d] before the write
     v_pool: torch.Tensor = None     # [NB, Hkv, d, 16] before the write
     info: dict = field(default_factory=dict)
+    kv_cache: str = "same"          # "same" (pools in dtype) or "fp8" (E4M3 codes)
+    k_scale: torch.Tensor = None    # fp8: float32 [Hkv]
+    v_scale: torch.Tensor = None
 
     @property
     def num_seqs(self) -> int:
@@ -198,6 +201,54 @@ def _draw_values(step: StepInputs, requests, seed, device, fill) -> None:
         step.query[pad] = fv
         step.key[pad] = fv
         step.value[pad] = fv
+
+
+def fp8_cache(step: StepInputs, seed: int, device="cpu", fill="nan") -> StepInputs:
+    """The same step over an E4M3 cache: per-KV-head scales and pools of
+    codes drawn directly (no quantisation here).
+
+    Scales: k_scale[h] = 2^-5 (1 + h/4), v_scale[h] = 2^-4 (1 + h/8).  Every
+    prior-context code has a random sign, an exponent field uniform in
+    [3, 10] and a uniform mantissa (magnitudes 2^-4 .. 2^3.9 before scaling);
+    dead slots hold the NaN code 0x7F (``fill="nan"``) or 0.  The query and
+    the new tokens' K/V stay as drawn (they reach the cache through the
+    quantising write).  Codes come from ``torch.Generator(seed + 1000)``: K
+    pool, then V pool.
+    """
+    hkv = step.num_kv_heads
+    h = torch.arange(hkv, dtype=torch.float32)
+    k_scale = (2.0 ** -5) * (1.0 + h / 4.0)
+    v_scale = (2.0 ** -4) * (1.0 + h / 8.0)
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) + 1000)
+
+    def codes(shape):
+        sign = torch.randint(0, 2, shape, generator=g, device=device, dtype=torch.int32)
+        e = torch.randint(3, 11, shape, generator=g, device=device, dtype=torch.int32)
+        m = torch.randint(0, 8, shape, generator=g, device=device, dtype=torch.int32)
+        return ((sign << 7) | (e << 3) | m).to(torch.uint8)
+
+    NB, d = step.num_blocks, step.head_dim
+    kp = codes((NB, hkv, BLOCK, d))
+    vp = codes((NB, hkv, d, BLOCK))
+    # prior-context slots from the metadata: positions 0 .. seq_len - q_len - 1
+    chunks = []
+    q_lens = step.q_lens
+    for b in range(step.num_seqs):
+        prior = int(step.seq_lens[b]) - int(q_lens[b])
+        if prior <= 0:
+            continue
+        pos = np.arange(prior, dtype=np.int64)
+        chunks.append(step.block_tables[b, pos // BLOCK].astype(np.int64) * BLOCK + pos % BLOCK)
+    live = torch.zeros(NB * BLOCK, dtype=torch.bool, device=device)
+    if chunks:
+        live[torch.as_tensor(np.concatenate(chunks)).to(device)] = True
+    dead = ~live.view(NB, BLOCK)
+    fv = 0x7F if fill == "nan" else 0
+    kp.masked_fill_(dead.view(NB, 1, BLOCK, 1), fv)
+    vp.masked_fill_(dead.view(NB, 1, 1, BLOCK), fv)
+    return replace(step, k_pool=kp, v_pool=vp, info=dict(step.info), kv_cache="fp8",
+                   k_scale=k_scale.to(device), v_scale=v_scale.to(device))
 
 
 # ----------------------------------------------------------------------------
