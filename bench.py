@@ -84,8 +84,9 @@ def work_model(step):
     """
     import numpy as np
     es = 2 if step.dtype == "bf16" else 4
+    ec = 1 if step.kv_cache == "fp8" else es      # bytes per cached element
     hq, hkv, d = step.num_q_heads, step.num_kv_heads, step.head_dim
-    tok_bytes = 2 * hkv * d * es
+    tok_bytes = 2 * hkv * d * ec
     tokens_in_block = {}
     table_entries = 0
     pairs = 0
@@ -113,7 +114,7 @@ def work_model(step):
     nt = int(step.query_start_loc[-1])
     kv_bytes = ctx_tokens * tok_bytes
     io = nt * hq * d * es * 2 + nt * hq * 4 + table_entries * 4 + (2 * step.num_seqs + 1) * 4
-    write = nt * hkv * d * es * 2 * 2 + nt * 8
+    write = nt * hkv * d * (es + ec) * 2 + nt * 8
     return {
         "bytes": kv_bytes + io + write,
         "kv_bytes": kv_bytes,
@@ -132,6 +133,7 @@ def decode_kernel_bytes(step):
     """Algorithmic bytes of the decode kernel alone: K/V of the decode rows'
     context (unique blocks), their Q, output/partials excluded, table reads."""
     es = 2 if step.dtype == "bf16" else 4
+    ec = 1 if step.kv_cache == "fp8" else es
     hq, hkv, d = step.num_q_heads, step.num_kv_heads, step.head_dim
     dq = 16 // (hq // hkv)
     seen = {}
@@ -151,7 +153,7 @@ def decode_kernel_bytes(step):
             if cnt > seen.get(pb, 0):
                 seen[pb] = cnt
     toks = sum(seen.values())
-    return toks * 2 * hkv * d * es + rows * hq * d * es + entries * 4, toks
+    return toks * 2 * hkv * d * ec + rows * hq * d * es + entries * 4, toks
 
 
 # ----------------------------------------------------------------------------
@@ -194,22 +196,36 @@ class StepRunner:
         self.g = g
         code = _lib.PA_BF16 if step.dtype == "bf16" else _lib.PA_F32
         P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
-        self.kv_args = [P(g["key"]), P(g["value"]), P(g["kc"]), P(g["vc"]), P(g["sm"]), nt, hkv,
-                        d, 16, step.num_blocks, code]
-        self.attn_args = [P(g["query"]), P(g["kc"]), P(g["vc"]), P(g["qsl"]), P(g["sl"]),
-                          P(g["bt"]), step.num_seqs, nt, step.max_query_len, step.max_seq_len,
-                          hq, hkv, d, 16, g["bt"].shape[1], step.num_blocks,
-                          ctypes.c_float(step.scale), self.splits, P(g["out"]), P(g["lse"]),
-                          P(g["ws"]), ws, code]
+        self.fp8 = step.kv_cache == "fp8"
+        if self.fp8:
+            g["ks"] = step.k_scale.to(dev).contiguous()
+            g["vs"] = step.v_scale.to(dev).contiguous()
+            self.kv_args = [P(g["key"]), P(g["value"]), P(g["kc"]), P(g["vc"]), P(g["sm"]),
+                            P(g["ks"]), P(g["vs"]), nt, hkv, d, 16, step.num_blocks, code]
+            self.attn_args = [P(g["query"]), P(g["kc"]), P(g["vc"]), P(g["ks"]), P(g["vs"]),
+                              P(g["qsl"]), P(g["sl"]), P(g["bt"]), step.num_seqs, nt,
+                              step.max_query_len, step.max_seq_len, hq, hkv, d, 16,
+                              g["bt"].shape[1], step.num_blocks, ctypes.c_float(step.scale),
+                              self.splits, P(g["out"]), P(g["lse"]), P(g["ws"]), ws]
+            self.kv_fn, self.attn_fn = self.lib.pa_kv_write_fp8, self.lib.pa_attention_fwd_fp8
+        else:
+            self.kv_args = [P(g["key"]), P(g["value"]), P(g["kc"]), P(g["vc"]), P(g["sm"]), nt,
+                            hkv, d, 16, step.num_blocks, code]
+            self.attn_args = [P(g["query"]), P(g["kc"]), P(g["vc"]), P(g["qsl"]), P(g["sl"]),
+                              P(g["bt"]), step.num_seqs, nt, step.max_query_len,
+                              step.max_seq_len, hq, hkv, d, 16, g["bt"].shape[1],
+                              step.num_blocks, ctypes.c_float(step.scale), self.splits,
+                              P(g["out"]), P(g["lse"]), P(g["ws"]), ws, code]
+            self.kv_fn, self.attn_fn = self.lib.pa_kv_write, self.lib.pa_attention_fwd
 
     def __call__(self):
         s = self.ctypes.c_void_p(self.torch.cuda.current_stream().cuda_stream)
-        st = self.lib.pa_kv_write(*self.kv_args, s)
+        st = self.kv_fn(*self.kv_args, s)
         if st != 0:
-            raise RuntimeError(f"pa_kv_write failed: {st}")
-        st = self.lib.pa_attention_fwd(*self.attn_args, s)
+            raise RuntimeError(f"KV write failed: {st}")
+        st = self.attn_fn(*self.attn_args, s)
         if st != 0:
-            raise RuntimeError(f"pa_attention_fwd failed: {st}")
+            raise RuntimeError(f"attention failed: {st}")
 
 
 def busy_gpu(ms):
@@ -455,6 +471,50 @@ def achievable(log):
     return res
 
 
+def bench_fp8(args, log):
+    """The decode and prefill workloads over an E4M3 cache (per-KV-head
+    scales, codes drawn directly; the KV write quantises the new tokens).
+    Algorithmic bytes count one byte per cached element."""
+    import torch
+
+    from workloads import config_step, fp8_cache
+    dev = torch.device("cuda:0")
+    out = []
+    for cfg in (2, 3, 4):
+        step = fp8_cache(config_step(cfg, device=dev, fill="zero"), cfg, device=dev, fill="zero")
+        wm = work_model(step)
+        base = StepRunner(step, dev, 0)
+        runners = [base]
+        if cfg == 2:
+            for _ in range(args.replicas - 1):
+                runners.append(StepRunner(step, dev, base.splits,
+                                          pools=(step.k_pool.clone(), step.v_pool.clone())))
+            n = args.steps
+        else:
+            n = args.extra_steps
+        ms, mode = time_steps(runners, n, args.warmup if cfg == 2 else 3, not args.eager, log,
+                              per_graph=len(runners))
+        kt = kernel_times(runners, min(n, 200), log)
+        rec = {"workload": WORKLOAD_NAMES[cfg].split(" (")[0] + ", FP8 (E4M3) KV cache",
+               "ms_per_step": ms, "launch": mode, "num_splits": base.splits,
+               "step_GBps": wm["bytes"] / (ms * 1e-3) / 1e9,
+               "kernels_us": {k: round(v["avg_us"], 2) for k, v in kt.items()}}
+        name = "decode_split_partial" if "decode_split_partial" in kt else "decode"
+        if name in kt and cfg != 4:
+            kb, _ = decode_kernel_bytes(step)
+            gbs = kb / (kt[name]["avg_us"] * 1e-6) / 1e9
+            rec["decode_kernel"] = {"bytes": kb, "GBps": gbs, "frac_hbm": gbs / PEAK_HBM_GBS}
+        if "prefill_mfma" in kt:
+            tf = wm["prefill_flops"] / (kt["prefill_mfma"]["avg_us"] * 1e-6) / 1e12
+            rec["prefill_kernel"] = {"flops": wm["prefill_flops"], "TFLOPps": tf,
+                                     "frac_mfma": tf / PEAK_BF16_TFLOPS}
+        log(f"fp8 config{cfg}: {json.dumps(rec)}")
+        out.append(rec)
+        del runners, base, step
+        torch.cuda.empty_cache()
+    return out
+
+
 def bench_config1(args, log):
     """The tiny fp32 mixed step: GPU time per step and the oracle's
     CPU-seconds for the same step (correctness workload, no roofline)."""
@@ -584,11 +644,13 @@ def main():
     sweep = None
     ach = None
     cfg1 = None
+    fp8 = None
     if not args.only_main:
         sweep = split_sweep(args, log)
         for cfg in (3, 4, 5):
             log("extra workload: " + WORKLOAD_NAMES[cfg])
             extras.append(bench_extra(cfg, args, log))
+        fp8 = bench_fp8(args, log)
         cfg1 = bench_config1(args, log)
         ach = achievable(log)
     cpu = None
@@ -622,6 +684,7 @@ def main():
                         else round(res["eager_ms"] * 1e3, 2)},
         "split_sweep": sweep,
         "extra_workloads": extras,
+        "fp8_kv_cache": fp8,
         "correctness_workload": cfg1,
         "achievable": ach,
     }
