@@ -20,6 +20,8 @@ reference pages):
   same section as a self-check variant.
 * Same page, section "Prefill has a full grid; decode at batch 1 has almost
   none": the split-KV partials and their combine as a self-check variant.
+* ``rope``: rotary position embedding of Q and the new K fused with the
+  KV write (positions as in "Flattening a step").
 * ``fp8``: an FP8 (OCP E4M3) KV cache with per-KV-head scales -- the
   quantising write and attention over the dequantised pools.
 
@@ -41,6 +43,7 @@ from .paged_attention import (  # noqa: F401
     attention_split_partials,
     combine_partials,
 )
+from .rope import rope_table, rope, round_to, rope_kv_write  # noqa: F401
 from .fp8 import (  # noqa: F401
     E4M3_MAX,
     e4m3_decode,
