@@ -515,6 +515,65 @@ def bench_fp8(args, log):
     return out
 
 
+def bench_rope(args, log):
+    """The fused rotary embedding + KV write over the long-prefill step's
+    32768 new tokens, beside the plain KV write of the same tokens.  Bytes:
+    Q read and written, K and V read and written, one cos/sin row and the
+    slot and position per token."""
+    import torch
+
+    import paged_attention_flat_amd as pa
+    from workloads import config_step
+    dev = torch.device("cuda:0")
+    step = config_step(4, device=dev, fill="zero")
+    nt, hq, d = step.query.shape
+    hkv = step.num_kv_heads
+    qsl = step.query_start_loc
+    pos = torch.empty(nt, dtype=torch.int64)
+    for b in range(step.num_seqs):
+        n = int(qsl[b + 1] - qsl[b])
+        pos[int(qsl[b]):int(qsl[b + 1])] = int(step.seq_lens[b]) - n + torch.arange(n)
+    maxp = int(pos.max()) + 1
+    w = 10000.0 ** (-2.0 * torch.arange(d // 2, dtype=torch.float64) / d)
+    ang = torch.arange(maxp, dtype=torch.float64)[:, None] * w[None, :]
+    table = torch.cat([ang.cos(), ang.sin()], dim=1).to(torch.float32).to(dev)
+    pos = pos.to(dev)
+    sm = torch.as_tensor(step.slot_mapping).to(dev)
+    q = step.query.clone()
+    kc, vc = step.k_pool, step.v_pool
+    n = 20
+    for _ in range(3):
+        pa.rope_kv_write(q, step.key, step.value, kc, vc, sm, pos, table)
+        pa.kv_write(step.key, step.value, kc, vc, sm)
+    torch.cuda.synchronize()
+    pa.trace_begin(4 * n)
+    busy_gpu(20.0)
+    for _ in range(n):
+        pa.rope_kv_write(q, step.key, step.value, kc, vc, sm, pos, table)
+        pa.kv_write(step.key, step.value, kc, vc, sm)
+    pa.trace_end()
+    torch.cuda.synchronize()
+    agg = {}
+    for name, ms in pa.trace_read():
+        agg.setdefault(name, []).append(ms * 1e3)
+    es = 2
+    fused_bytes = nt * (2 * hq * d * es + 4 * hkv * d * es + d * 4 + 16)
+    plain_bytes = nt * (4 * hkv * d * es + 8)
+    f_us = sum(agg["rope_kv_write"]) / len(agg["rope_kv_write"])
+    p_us = sum(agg["kv_write"]) / len(agg["kv_write"])
+    out = {"workload": "rotary embedding + KV write of 4 x 8192 new tokens (Hq 32/Hkv 8, d 128, "
+                       "bf16)",
+           "fused_us": round(f_us, 2), "fused_bytes": fused_bytes,
+           "fused_GBps": round(fused_bytes / (f_us * 1e-6) / 1e9, 1),
+           "fused_frac_hbm": round(fused_bytes / (f_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+           "plain_kv_write_us": round(p_us, 2),
+           "plain_kv_write_GBps": round(plain_bytes / (p_us * 1e-6) / 1e9, 1)}
+    log(f"rope: {json.dumps(out)}")
+    del step, q
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_config1(args, log):
     """The tiny fp32 mixed step: GPU time per step and the oracle's
     CPU-seconds for the same step (correctness workload, no roofline)."""
@@ -645,12 +704,14 @@ def main():
     ach = None
     cfg1 = None
     fp8 = None
+    rope = None
     if not args.only_main:
         sweep = split_sweep(args, log)
         for cfg in (3, 4, 5):
             log("extra workload: " + WORKLOAD_NAMES[cfg])
             extras.append(bench_extra(cfg, args, log))
         fp8 = bench_fp8(args, log)
+        rope = bench_rope(args, log)
         cfg1 = bench_config1(args, log)
         ach = achievable(log)
     cpu = None
@@ -685,6 +746,7 @@ def main():
         "split_sweep": sweep,
         "extra_workloads": extras,
         "fp8_kv_cache": fp8,
+        "rope_kv_write": rope,
         "correctness_workload": cfg1,
         "achievable": ach,
     }

@@ -158,6 +158,31 @@ pa_status pa_attention_fwd(const void* query,
                            pa_dtype dtype, void* stream);
 
 /*
+ * pa_rope_kv_write -- rotary position embedding of the step's queries and new
+ * keys fused with the KV write (positions: "Model execution", section
+ * "Flattening a step", kept "for rotary embeddings" in "Inside the engine";
+ * the pages do not write the rotation out).  For every t < num_tokens whose
+ * p = positions[t] lies in [0, max_position), every head row x of length d
+ * (query[t][hq] for all query heads, key[t][hkv]) is rotated pairwise,
+ *   x'[i]       = x[i] c_i - x[i + d/2] s_i
+ *   x'[i + d/2] = x[i + d/2] c_i + x[i] s_i,     i < d/2,
+ * with c_i = cos_sin[p][i], s_i = cos_sin[p][d/2 + i] (fp32 table
+ * [max_position][head_dim], 16-byte aligned), computed in fp32 and rounded
+ * once to dtype.  query is rotated in place; the rotated key and the
+ * unchanged value are written at slot_mapping[t] exactly as pa_kv_write
+ * (slot < 0 or past the pool: nothing written).  Tokens whose position is
+ * outside the table are left alone (query unchanged, nothing written).
+ * Supported as pa_kv_write; num_q_heads a multiple of num_kv_heads.
+ */
+pa_status pa_rope_kv_write(void* query, const void* key, const void* value,
+                           void* key_cache, void* value_cache,
+                           const int64_t* slot_mapping, const int64_t* positions,
+                           const float* cos_sin, int32_t max_position,
+                           int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                           pa_dtype dtype, void* stream);
+
+/*
  * FP8 KV cache (E4M3).  The pages name an 8-bit cache as the way to halve the
  * bytes every decode step reads ("Anatomy of a serving engine", KV-cache
  * capacity; "Model execution", section "Attention backends") without fixing

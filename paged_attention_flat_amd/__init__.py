@@ -22,7 +22,7 @@ from ._lib import LIB, PA_BF16, PA_F32, PA_BLOCK_SIZE, PA_MAX_SPLITS  # noqa: F4
 
 __all__ = [
     "PaError", "kv_write", "attention", "split_combine", "workspace_size",
-    "kv_write_fp8", "attention_fp8", "alloc_cache_fp8",
+    "kv_write_fp8", "attention_fp8", "alloc_cache_fp8", "rope_kv_write",
     "choose_num_splits", "capture_size", "alloc_cache", "workspace", "trace_begin", "trace_end",
     "trace_read",
     "kernel_name", "version",
@@ -183,6 +183,36 @@ def attention_fp8(query, key_cache, value_cache, k_scale, v_scale, query_start_l
         _stream(stream))
     _check(st, "pa_attention_fwd_fp8")
     return out, lse
+
+
+def rope_kv_write(query, key, value, key_cache, value_cache, slot_mapping, positions, cos_sin,
+                  stream=None) -> None:
+    """Rotate query ([Nt, Hq, d], in place) and the new keys by each token's
+    position (cos_sin: float32 [max_position, d], cos then sin of the d/2
+    angles), writing the rotated K and V at their slots."""
+    nt, hkv, d = key.shape
+    hq = query.shape[1]
+    if value.shape != key.shape or value.dtype != key.dtype or query.dtype != key.dtype:
+        raise ValueError("query, key and value must share a dtype; key and value a shape")
+    if tuple(query.shape) != (nt, hq, d):
+        raise ValueError("query must be [num_tokens, num_q_heads, head_dim]")
+    nb = key_cache.shape[0]
+    if tuple(key_cache.shape) != (nb, hkv, PA_BLOCK_SIZE, d) or \
+            tuple(value_cache.shape) != (nb, hkv, d, PA_BLOCK_SIZE):
+        raise ValueError("cache shapes must be [NB, Hkv, 16, d] and [NB, Hkv, d, 16]")
+    if key_cache.dtype != key.dtype or value_cache.dtype != key.dtype:
+        raise ValueError("cache dtype must equal the K/V dtype")
+    for name, t in (("slot_mapping", slot_mapping), ("positions", positions)):
+        if t.dtype != torch.int64 or t.shape != (nt,):
+            raise ValueError(f"{name} must be int64 [num_tokens]")
+    if cos_sin.dtype != torch.float32 or cos_sin.dim() != 2 or cos_sin.shape[1] != d:
+        raise ValueError("cos_sin must be float32 [max_position, head_dim]")
+    st = LIB.pa_rope_kv_write(_dev(query, "query"), _dev(key, "key"), _dev(value, "value"),
+                              _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+                              _dev(slot_mapping, "slot_mapping"), _dev(positions, "positions"),
+                              _dev(cos_sin, "cos_sin"), cos_sin.shape[0], nt, hq, hkv, d,
+                              PA_BLOCK_SIZE, nb, _dtype_code(key), _stream(stream))
+    _check(st, "pa_rope_kv_write")
 
 
 def workspace_size(num_seqs: int, num_tokens: int, num_q_heads: int, head_dim: int,

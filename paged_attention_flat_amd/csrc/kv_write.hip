@@ -127,7 +127,161 @@ __global__ __launch_bounds__(256) void kv_write_fp8_kernel(
   }
 }
 
+// Rotary position embedding fused with the KV write.  Pairs are (i, i + d/2)
+// of each head; row p of the cos/sin table holds cos of the d/2 angles, then
+// their sin.  A work-group takes 16 tokens of one KV head: it rotates the new
+// keys on their way into the cache (one read and one write of K), rotates the
+// G query heads of that KV head in place, and writes V like kv_write.  Each
+// thread owns 4 consecutive pairs of one row (two 4-element pieces, one per
+// half of the head).  Arithmetic in fp32, one rounding to the element type.
+template <typename E>
+struct Piece4;  // four elements of E as one load / store
+template <>
+struct Piece4<uint16_t> {
+  typedef uint2 T;
+  static __device__ __forceinline__ void get(T v, float* f) {
+    f[0] = __uint_as_float(v.x << 16);
+    f[1] = __uint_as_float(v.x & 0xffff0000u);
+    f[2] = __uint_as_float(v.y << 16);
+    f[3] = __uint_as_float(v.y & 0xffff0000u);
+  }
+  static __device__ __forceinline__ T put(const float* f) {
+    return make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
+  }
+};
+template <>
+struct Piece4<uint32_t> {
+  typedef uint4 T;
+  static __device__ __forceinline__ void get(T v, float* f) {
+    f[0] = __uint_as_float(v.x);
+    f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z);
+    f[3] = __uint_as_float(v.w);
+  }
+  static __device__ __forceinline__ T put(const float* f) {
+    return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                      __float_as_uint(f[3]));
+  }
+};
+
+// rotate the 4 pairs (lo[j], hi[j]) by the angles in c[j], s[j]
+__device__ __forceinline__ void rotate4(float* lo, float* hi, const float4 c, const float4 s) {
+  const float cc[4] = {c.x, c.y, c.z, c.w}, ss[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float a = lo[j], b = hi[j];
+    lo[j] = a * cc[j] - b * ss[j];
+    hi[j] = b * cc[j] + a * ss[j];
+  }
+}
+
+template <typename E>
+__global__ __launch_bounds__(256) void rope_kv_write_kernel(
+    E* __restrict__ query, const E* __restrict__ key, const E* __restrict__ value,
+    E* __restrict__ kc, E* __restrict__ vc, const int64_t* __restrict__ slots,
+    const int64_t* __restrict__ positions, const float* __restrict__ cos_sin,
+    int32_t max_position, int32_t nt, int32_t hq, int32_t hkv, int32_t d, int64_t num_slots) {
+  typedef typename Piece4<E>::T P4;
+  constexpr int kPad = 16 / sizeof(E);
+  __shared__ __align__(16) E vrow[kTok][128 + kPad];
+  __shared__ int64_t sslot[kTok];
+  __shared__ int spos[kTok];
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * kTok;
+  const int h = blockIdx.y;
+  const int G = hq / hkv;
+  const int ntok = min(kTok, nt - t0);
+  if (tid < kTok) {
+    int64_t s = -1;
+    int p = -1;
+    if (tid < ntok) {
+      const int64_t pp = positions[t0 + tid];
+      p = (pp >= 0 && pp < max_position) ? (int)pp : -1;  // outside the table: untouched
+      s = slots[t0 + tid];
+      if (s >= num_slots || p < 0) s = -1;
+    }
+    sslot[tid] = s;
+    spos[tid] = p;
+  }
+  __syncthreads();
+  const int half = d / 2, qpr = half / 4;  // 4-pair pieces per head row
+  // K: rotate, write token-major into the cache
+  for (int c = tid; c < kTok * qpr; c += 256) {
+    const int ti = c / qpr, pc = c - ti * qpr;
+    const int p = spos[ti];
+    const int64_t s = sslot[ti];
+    if (ti >= ntok || p < 0) continue;
+    const size_t src = ((size_t)(t0 + ti) * hkv + h) * d + 4 * pc;
+    float lo[4], hi[4];
+    Piece4<E>::get(*reinterpret_cast<const P4*>(key + src), lo);
+    Piece4<E>::get(*reinterpret_cast<const P4*>(key + src + half), hi);
+    const float* row = cos_sin + (size_t)p * d + 4 * pc;
+    rotate4(lo, hi, *reinterpret_cast<const float4*>(row),
+            *reinterpret_cast<const float4*>(row + half));
+    if (s < 0) continue;
+    const size_t blk = (size_t)(s >> 4), off = (size_t)(s & 15);
+    E* kdst = kc + ((blk * hkv + h) * kTok + off) * d + 4 * pc;
+    *reinterpret_cast<P4*>(kdst) = Piece4<E>::put(lo);
+    *reinterpret_cast<P4*>(kdst + half) = Piece4<E>::put(hi);
+  }
+  // Q: the G query heads of this KV head, rotated in place
+  for (int c = tid; c < kTok * G * qpr; c += 256) {
+    const int ti = c / (G * qpr), rem = c - ti * (G * qpr);
+    const int g = rem / qpr, pc = rem - g * qpr;
+    const int p = spos[ti];
+    if (ti >= ntok || p < 0) continue;
+    E* qrow = query + ((size_t)(t0 + ti) * hq + h * G + g) * d + 4 * pc;
+    float lo[4], hi[4];
+    Piece4<E>::get(*reinterpret_cast<const P4*>(qrow), lo);
+    Piece4<E>::get(*reinterpret_cast<const P4*>(qrow + half), hi);
+    const float* row = cos_sin + (size_t)p * d + 4 * pc;
+    rotate4(lo, hi, *reinterpret_cast<const float4*>(row),
+            *reinterpret_cast<const float4*>(row + half));
+    *reinterpret_cast<P4*>(qrow) = Piece4<E>::put(lo);
+    *reinterpret_cast<P4*>(qrow + half) = Piece4<E>::put(hi);
+  }
+  // V: staged in LDS, written dim-major (as kv_write)
+  const int cpr = d * (int)sizeof(E) / 16;
+  for (int c = tid; c < kTok * cpr; c += 256) {
+    const int ti = c / cpr, part = c - ti * cpr;
+    if (ti >= ntok) break;
+    const size_t src = ((size_t)(t0 + ti) * hkv + h) * d;
+    reinterpret_cast<uint4*>(&vrow[ti][0])[part] = reinterpret_cast<const uint4*>(value + src)[part];
+  }
+  __syncthreads();
+  for (int e = tid; e < kTok * d; e += 256) {
+    const int ti = e & (kTok - 1), c = e >> 4;
+    if (ti >= ntok) continue;
+    const int64_t s = sslot[ti];
+    if (s < 0) continue;
+    const size_t blk = (size_t)(s >> 4), off = (size_t)(s & 15);
+    vc[((blk * hkv + h) * d + c) * kTok + off] = vrow[ti][c];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_rope_kv_write(void* query, const void* key, const void* value, void* kc,
+                                void* vc, const int64_t* slots, const int64_t* positions,
+                                const float* cos_sin, int32_t max_position, int32_t nt,
+                                int32_t hq, int32_t hkv, int32_t d, int32_t esize,
+                                int64_t num_blocks, hipStream_t stream) {
+  dim3 grid((nt + kTok - 1) / kTok, hkv);
+  trace_before(K_ROPE_KV_WRITE, stream);
+  if (esize == 2) {
+    hipLaunchKernelGGL(rope_kv_write_kernel<uint16_t>, grid, dim3(256), 0, stream,
+                       (uint16_t*)query, (const uint16_t*)key, (const uint16_t*)value,
+                       (uint16_t*)kc, (uint16_t*)vc, slots, positions, cos_sin, max_position, nt,
+                       hq, hkv, d, num_blocks * kTok);
+  } else {
+    hipLaunchKernelGGL(rope_kv_write_kernel<uint32_t>, grid, dim3(256), 0, stream,
+                       (uint32_t*)query, (const uint32_t*)key, (const uint32_t*)value,
+                       (uint32_t*)kc, (uint32_t*)vc, slots, positions, cos_sin, max_position, nt,
+                       hq, hkv, d, num_blocks * kTok);
+  }
+  trace_after(stream);
+  return hipGetLastError();
+}
 
 hipError_t launch_kv_write_fp8(const void* key, const void* value, void* kc, void* vc,
                                const int64_t* slots, const float* k_scale,

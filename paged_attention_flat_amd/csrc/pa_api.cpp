@@ -160,6 +160,7 @@ const char* pa_kernel_name(int32_t id) {
     case K_DECODE_ORDER: return "decode_order";
     case K_ZERO: return "workspace_zero";
     case K_KV_WRITE_FP8: return "kv_write_fp8";
+    case K_ROPE_KV_WRITE: return "rope_kv_write";
   }
   return "unknown";
 }
@@ -427,6 +428,34 @@ pa_status pa_attention_fwd_fp8(const void* query, const void* key_cache,
                         num_q_heads, num_kv_heads, head_dim, block_size, block_table_stride,
                         num_blocks, scale, num_splits, out, lse, workspace, workspace_bytes,
                         PA_BF16, true, stream);
+}
+
+pa_status pa_rope_kv_write(void* query, const void* key, const void* value, void* key_cache,
+                           void* value_cache, const int64_t* slot_mapping,
+                           const int64_t* positions, const float* cos_sin, int32_t max_position,
+                           int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                           pa_dtype dtype, void* stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_q_heads <= 0 || num_blocks <= 0 ||
+      max_position < 0)
+    return PA_ERR_INVALID;
+  if (num_q_heads % num_kv_heads != 0) return PA_ERR_INVALID;
+  if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_INVALID;
+  if (block_size != PA_BLOCK_SIZE) return PA_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (!query || !key || !value || !key_cache || !value_cache || !slot_mapping || !positions ||
+      !cos_sin)
+    return PA_ERR_NULL;
+  if (!aligned16(query) || !aligned16(key) || !aligned16(value) || !aligned16(key_cache) ||
+      !aligned16(value_cache) || !aligned16(cos_sin))
+    return PA_ERR_INVALID;
+  const int32_t esize = dtype == PA_BF16 ? 2 : 4;
+  hipError_t e = launch_rope_kv_write(query, key, value, key_cache, value_cache, slot_mapping,
+                                      positions, cos_sin, max_position, num_tokens, num_q_heads,
+                                      num_kv_heads, head_dim, esize, num_blocks,
+                                      (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 pa_status pa_kv_write_fp8(const void* key, const void* value, void* key_cache, void* value_cache,

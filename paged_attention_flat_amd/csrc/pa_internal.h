@@ -20,7 +20,8 @@ enum KernelId : int32_t {
   K_DECODE_ORDER = 8,
   K_ZERO = 9,
   K_KV_WRITE_FP8 = 10,
-  K_COUNT = 11
+  K_ROPE_KV_WRITE = 11,
+  K_COUNT = 12
 };
 
 // Tracing hooks (pa_api.cpp).  trace_before/after bracket one launch.
@@ -34,6 +35,12 @@ hipError_t launch_kv_write(const void* key, const void* value, void* kc, void* v
                            hipStream_t stream);
 // Quantising write into an E4M3 cache (one byte per element), per-KV-head
 // float scales: code = e4m3(clamp(x / scale[h], -448, 448)), ties to even.
+// Rotary embedding of Q (in place) and the new K, fused with the KV write.
+hipError_t launch_rope_kv_write(void* query, const void* key, const void* value, void* kc,
+                                void* vc, const int64_t* slots, const int64_t* positions,
+                                const float* cos_sin, int32_t max_position, int32_t nt,
+                                int32_t hq, int32_t hkv, int32_t d, int32_t esize,
+                                int64_t num_blocks, hipStream_t stream);
 hipError_t launch_kv_write_fp8(const void* key, const void* value, void* kc, void* vc,
                                const int64_t* slots, const float* k_scale,
                                const float* v_scale, int32_t nt, int32_t hkv, int32_t d,
