@@ -42,6 +42,7 @@ from .paged_attention import (  # noqa: F401
     attention_online,
     attention_split_partials,
     combine_partials,
+    attention_cascade,
 )
 from .rope import rope_table, rope, round_to, rope_kv_write  # noqa: F401
 from .fp8 import (  # noqa: F401

@@ -358,3 +358,56 @@ def combine_partials(partial_out, partial_lse):
     out = (coef[..., None] * np.where(np.isneginf(pl)[..., None], 0.0, po)).sum(axis=0)
     out = np.where(np.isfinite(LSE)[..., None], out, np.nan)
     return out, LSE
+
+
+def attention_cascade(query, k_pool, v_pool, query_start_loc, seq_lens, block_tables,
+                      scale: float, num_kv_heads: int, dtype: str, sharers, prefix_blocks,
+                      block_size: int = BLOCK_SIZE):
+    """Shared-prefix (cascade) attention: requests in ``sharers`` read their
+    first len(prefix_blocks) blocks from the one shared list ``prefix_blocks``
+    (the blocks several requests' tables point at: "Model execution",
+    "Flattening a step" -- block tables may share physical blocks; "Anatomy of
+    a serving engine" -- prefix caching) as a partial (o_A, lse_A) over those
+    keys, and the rest of their context through their own tables as (o_B,
+    lse_B); the two merge as split partials do.  Every other request is plain
+    attention.  Equals ``attention`` whenever each sharer's table starts with
+    ``prefix_blocks``.
+    """
+    out, lse = attention(query, k_pool, v_pool, query_start_loc, seq_lens, block_tables,
+                         scale, num_kv_heads, dtype)
+    q = to_f64(query, dtype)
+    Nt, Hq, d = q.shape
+    P = len(prefix_blocks)
+    pref_tab = np.asarray(prefix_blocks, dtype=np.int64)
+    for b in sharers:
+        q_len = int(query_start_loc[b + 1]) - int(query_start_loc[b])
+        if q_len == 0:
+            continue
+        seq_len = int(seq_lens[b])
+        ctx = seq_len - q_len
+        npre = min(P * block_size, seq_len)
+        Ka, Va = gather_context(k_pool, v_pool, pref_tab, npre, block_size)
+        Kall, Vall = gather_context(k_pool, v_pool, block_tables[b], seq_len, block_size)
+        Ka, Va = to_f64(Ka, dtype), to_f64(Va, dtype)
+        Kb, Vb = to_f64(Kall, dtype)[npre:], to_f64(Vall, dtype)[npre:]
+        for i in range(q_len):
+            t = int(query_start_loc[b]) + i
+            p = ctx + i
+            for h in range(Hq):
+                kvh = kv_head_of(h, Hq, num_kv_heads)
+                po, pl = [], []
+                for K, V, lo in ((Ka, Va, 0), (Kb, Vb, npre)):
+                    hi = min(K.shape[0], p + 1 - lo)
+                    if hi <= 0:
+                        po.append(np.zeros(d))
+                        pl.append(-np.inf)
+                        continue
+                    S = scale * (K[:hi, kvh, :] @ q[t, h, :])
+                    m = S.max()
+                    w = np.exp(S - m)
+                    po.append((w / w.sum()) @ V[:hi, kvh, :])
+                    pl.append(m + math.log(w.sum()))
+                o, L = combine_partials(np.array(po)[:, None, :], np.array(pl)[:, None])
+                out[t, h, :] = o[0]
+                lse[t, h] = L[0]
+    return out, lse

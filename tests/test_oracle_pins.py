@@ -526,3 +526,34 @@ def test_planted_strict_causal_mask_is_caught(monkeypatch):
     bad, _ = run_oracle(st, 0.5, fn=attention_strict)
     bf = brute_force(st, 0.5)
     assert any(not np.allclose(bad[t, h], o, atol=1e-9) for (t, h), (o, _) in bf.items())
+
+
+def test_cascade_equals_plain_attention():
+    # three decodes (one with 2 new tokens) and a prefill share a 2-block
+    # prefix; one decode's context is shorter than the prefix
+    rng = np.random.default_rng(27)
+    st = tiny_step(rng, [(40, 1), (50, 2), (20, 1), (0, 9), (70, 1)], 4, 2, 8, "bf16",
+                   num_blocks=24)
+    bt = st["block_tables"].copy()
+    prefix = list(bt[0, :2])
+    for b in (1, 2, 4):
+        bt[b, :2] = prefix
+    st = dict(st, block_tables=bt)
+    full, lf = run_oracle(st, 0.3)
+    casc, lc = run_oracle(st, 0.3, fn=oracle.attention_cascade, sharers=[0, 1, 2, 4],
+                          prefix_blocks=prefix)
+    np.testing.assert_allclose(casc, full, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lc, lf, rtol=0, atol=1e-12)
+    # planted: a sharer whose table does not start with the prefix reads the
+    # shared blocks instead (so the prefix list is what the cascade reads)
+    rng2 = np.random.default_rng(27)
+    orig = tiny_step(rng2, [(40, 1), (50, 2), (20, 1), (0, 9), (70, 1)], 4, 2, 8, "bf16",
+                     num_blocks=24)["block_tables"]
+    bt2 = bt.copy()
+    bt2[4, :2] = [orig[1, 0], prefix[1]]    # a fully written block of another request
+    st2 = dict(st, block_tables=bt2)
+    full2, _ = run_oracle(st2, 0.3)
+    casc2, _ = run_oracle(st2, 0.3, fn=oracle.attention_cascade, sharers=[4],
+                          prefix_blocks=prefix)
+    t4 = int(st["qsl"][4])
+    assert np.abs(casc2[t4] - full2[t4]).max() > 1e-3
