@@ -183,6 +183,44 @@ pa_status pa_rope_kv_write(void* query, const void* key, const void* value,
                            pa_dtype dtype, void* stream);
 
 /*
+ * pa_attention_fwd_cascade -- pa_attention_fwd (bf16) with a shared prefix
+ * read once.  Block tables may point several requests at the same physical
+ * blocks ("Model execution", "Flattening a step"; prefix caching in "Anatomy
+ * of a serving engine"); here `sharers` [num_sharers] are requests whose
+ * tables start with the num_prefix_blocks blocks `prefix_blocks` (device
+ * int32, caller's contract, unchecked).  The decode rows of the sharers are
+ * gathered and attend to the shared blocks in one matrix-core pass (each
+ * prefix tile staged once per 64-token tile of gathered rows, not once per
+ * request) as a partial (o, lse); the decode kernel then reads only each
+ * sharer's own later blocks and merges that partial with its splits.  The
+ * result is the attention of pa_attention_fwd (up to rounding): causality is
+ * kept per row, so a sharer whose context is shorter than the prefix is still
+ * exact.  Sharers with more new tokens than the decode kernel packs, or none,
+ * are computed as usual.  Workspace: pa_cascade_workspace_size (zeroed once
+ * like pa_attention_fwd's).  Every other argument and error as
+ * pa_attention_fwd with dtype PA_BF16.
+ */
+pa_status pa_attention_fwd_cascade(const void* query, const void* key_cache,
+                                   const void* value_cache,
+                                   const int32_t* query_start_loc, const int32_t* seq_lens,
+                                   const int32_t* block_tables,
+                                   int32_t num_seqs, int32_t num_tokens,
+                                   int32_t max_query_len, int32_t max_seq_len,
+                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t block_size, int32_t block_table_stride,
+                                   int64_t num_blocks, float scale, int32_t num_splits,
+                                   const int32_t* sharers, int32_t num_sharers,
+                                   const int32_t* prefix_blocks, int32_t num_prefix_blocks,
+                                   void* out, float* lse, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/* pa_cascade_workspace_size -- bytes of workspace for pa_attention_fwd_cascade
+ * (num_splits resolved, >= 1). */
+size_t pa_cascade_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t num_splits,
+                                 int32_t num_sharers, int32_t max_query_len);
+
+/*
  * FP8 KV cache (E4M3).  The pages name an 8-bit cache as the way to halve the
  * bytes every decode step reads ("Anatomy of a serving engine", KV-cache
  * capacity; "Model execution", section "Attention backends") without fixing

@@ -60,6 +60,12 @@ struct DecodeParams {
   float* lse;
   float* part_out;
   float* part_lse;
+  // shared-prefix attention: sharers skip the first pre_blocks blocks and
+  // merge the prefix partial (row pre_index[b] + token) with their splits
+  const int32_t* pre_index;  // nullable: [num_seqs], -1 for a non-sharer
+  const float* pre_out;
+  const float* pre_lse;
+  int32_t pre_blocks;
 };
 
 // Two launch shapes.  Many work units: 8 waves per work-group, one pair in
@@ -152,7 +158,8 @@ __global__ __launch_bounds__(64 * NW, (PIPE == 2 && NW < 8 ? 8 / NW : 1)) void d
   // the host-known max_seq_len, so the first 64 block-table entries can be
   // fetched together with query_start_loc / seq_lens (one round trip fewer
   // before the first K/V load).  Splits past a shorter request are empty.
-  const int blk_lo = split * p.split_blocks;
+  const int pv0 = p.pre_index != nullptr ? p.pre_index[b] : -1;
+  const int blk_lo = (pv0 >= 0 ? p.pre_blocks : 0) + split * p.split_blocks;
   const int32_t* table = p.tables + (size_t)b * p.table_stride;
   int tab = 0, tab_base = 0;
   {
@@ -369,8 +376,10 @@ __global__ __launch_bounds__(64 * NW, (PIPE == 2 && NW < 8 ? 8 / NW : 1)) void d
   // wave 0, lane (col, kg) holds dims 16*db + 4*kg .. +4 of column col
   const int t = q0 + qi;
   const int h = kvh * G + g;
+  // a sharer always merges (its splits and the prefix partial)
+  const bool merged = p.splits > 1 || pv0 >= 0;
   if (wave == 0 && col_valid) {
-    if (p.splits == 1) {
+    if (!merged) {
       const float inv = v_scale / l;
       uint16_t* dst = p.out + ((size_t)t * p.hq + h) * D + 4 * kg;
 #pragma unroll
@@ -398,7 +407,7 @@ __global__ __launch_bounds__(64 * NW, (PIPE == 2 && NW < 8 ? 8 / NW : 1)) void d
                            __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  if (p.splits == 1 || p.sem == nullptr) return;
+  if (!merged || p.sem == nullptr) return;
 
   // ---- merge of the split partials by the last split to finish ------------
   // ("combining the partials in a second reduction", here done by whichever
@@ -432,6 +441,7 @@ __global__ __launch_bounds__(64 * NW, (PIPE == 2 && NW < 8 ? 8 / NW : 1)) void d
   const int items = rows * QUADS;
   const int sg = items >= NT ? 1 : NT / items;
   const size_t split_rows = (size_t)p.nt * p.hq;
+  const int nparts = p.splits + (pv0 >= 0 ? 1 : 0);  // the prefix partial comes last
   float* s_m = &s_x[0][0][0];  // [6][NT] staging for the group merge
   static_assert(sizeof(s_x) >= 6 * NT * sizeof(float), "LDS staging too small");
   for (int base = 0; base < items * sg; base += NT) {
@@ -442,19 +452,25 @@ __global__ __launch_bounds__(64 * NW, (PIPE == 2 && NW < 8 ? 8 / NW : 1)) void d
     const int tt = q0 + r / G, hh = kvh * G + (r - (r / G) * G);
     const size_t rowi = (size_t)tt * p.hq + hh;
     const float* ob = p.part_out + rowi * D + quad * 4;
+    const size_t prer = (size_t)(pv0 + r / G) * p.hq + hh;  // row of the prefix partial
     float mm = -INFINITY, ll = 0.f;
     float4 ac = make_float4(0.f, 0.f, 0.f, 0.f);
     if (act) {
-      for (int s0 = grp; s0 < p.splits; s0 += CH * sg) {
+      for (int s0 = grp; s0 < nparts; s0 += CH * sg) {
         float x[CH];
         float4 v[CH];
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
           const int sp = s0 + c * sg;
-          const bool ok = sp < p.splits;
-          x[c] = ok ? p.part_lse[sp * split_rows + rowi] : -INFINITY;
-          v[c] = ok ? *reinterpret_cast<const float4*>(ob + sp * split_rows * D)
-                    : make_float4(0.f, 0.f, 0.f, 0.f);
+          x[c] = -INFINITY;
+          v[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (sp < p.splits) {
+            x[c] = p.part_lse[sp * split_rows + rowi];
+            v[c] = *reinterpret_cast<const float4*>(ob + sp * split_rows * D);
+          } else if (sp < nparts) {
+            x[c] = p.pre_lse[prer];
+            v[c] = *reinterpret_cast<const float4*>(p.pre_out + prer * D + quad * 4);
+          }
         }
         float mc = mm;
 #pragma unroll
@@ -545,6 +561,10 @@ void launch_dg(const AttnArgs& a, hipStream_t stream) {
   p.part_out = a.part_out;
   p.part_lse = a.part_lse;
   p.sem = a.sem;
+  p.pre_index = a.sharers != nullptr ? a.pre_index : nullptr;
+  p.pre_out = a.pre_out;
+  p.pre_lse = a.pre_lse;
+  p.pre_blocks = a.num_pre_blocks;
   if (a.decode_order != nullptr) {
     int shift = 0;
     const int max_blocks = (a.max_seq_len + 15) / 16;

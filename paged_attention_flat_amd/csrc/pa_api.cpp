@@ -76,13 +76,18 @@ size_t plan_capacity(int32_t num_seqs, int32_t num_tokens) {
 //   [plan: 1 + 2 * cap ints][plan_tmp: 2 * cap ints][decode order: 1 + num_seqs ints]
 //   [partial out: splits * nt * hq * d floats][partial lse: splits * nt * hq floats]
 struct WsLayout {
-  size_t sem, plan, plan_tmp, order, part_out, part_lse, total;
+  size_t sem, plan, plan_tmp, order, part_out, part_lse;
+  size_t pre_index, vtok, vpos, casc_count, pre_out, pre_lse;  // cascade only
+  size_t total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-WsLayout ws_layout(int32_t num_seqs, int32_t num_tokens, int32_t hq, int32_t d, int32_t splits) {
-  WsLayout w;
+// casc_rows > 0: room for the shared-prefix stage (gathered rows, their
+// partials) and split partials even at one split (sharers always merge).
+WsLayout ws_layout(int32_t num_seqs, int32_t num_tokens, int32_t hq, int32_t d, int32_t splits,
+                   int64_t casc_rows = 0) {
+  WsLayout w = {};
   const size_t cap = plan_capacity(num_seqs, num_tokens);
   // arrival counters of the split merge, one per (request, KV head <= Hq);
   // must be zero on entry and are left zero by every call
@@ -93,10 +98,20 @@ WsLayout ws_layout(int32_t num_seqs, int32_t num_tokens, int32_t hq, int32_t d, 
   w.part_out = align256(w.order + (1 + (size_t)num_seqs) * sizeof(int32_t));
   w.part_lse = w.part_out;
   w.total = w.part_out;
-  if (splits > 1) {
+  if (splits > 1 || casc_rows > 0) {
     const size_t rows = (size_t)splits * num_tokens * hq;
     w.part_lse = align256(w.part_out + rows * d * sizeof(float));
     w.total = align256(w.part_lse + rows * sizeof(float));
+  }
+  if (casc_rows > 0) {
+    const size_t R = (size_t)casc_rows;
+    w.pre_index = w.total;
+    w.vtok = align256(w.pre_index + (size_t)num_seqs * sizeof(int32_t));
+    w.vpos = align256(w.vtok + R * sizeof(int32_t));
+    w.casc_count = align256(w.vpos + R * sizeof(int32_t));
+    w.pre_out = align256(w.casc_count + sizeof(int32_t));
+    w.pre_lse = align256(w.pre_out + R * hq * d * sizeof(float));
+    w.total = align256(w.pre_lse + R * hq * sizeof(float));
   }
   return w;
 }
@@ -161,6 +176,8 @@ const char* pa_kernel_name(int32_t id) {
     case K_ZERO: return "workspace_zero";
     case K_KV_WRITE_FP8: return "kv_write_fp8";
     case K_ROPE_KV_WRITE: return "rope_kv_write";
+    case K_CASCADE_SETUP: return "cascade_setup";
+    case K_CASCADE_PREFIX: return "cascade_prefix";
   }
   return "unknown";
 }
@@ -301,7 +318,9 @@ pa_status attention_impl(const void* query, const void* key_cache, const void* v
                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                          int32_t block_table_stride, int64_t num_blocks, float scale,
                          int32_t num_splits, void* out, float* lse, void* workspace,
-                         size_t workspace_bytes, pa_dtype dtype, bool cache_fp8, void* stream) {
+                         size_t workspace_bytes, pa_dtype dtype, bool cache_fp8, void* stream,
+                         const int32_t* sharers = nullptr, int32_t num_sharers = 0,
+                         const int32_t* pre_blocks = nullptr, int32_t num_pre_blocks = 0) {
   if (num_seqs < 0 || num_tokens < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
       num_blocks <= 0 || num_splits < 0 || num_splits > PA_MAX_SPLITS || !std::isfinite(scale) ||
       !(scale > 0.f))
@@ -327,11 +346,15 @@ pa_status attention_impl(const void* query, const void* key_cache, const void* v
       num_splits == 0 ? pa_choose_num_splits(num_seqs, max_query_len, max_seq_len, num_q_heads,
                                              num_kv_heads, 0)
                       : num_splits;
-  const size_t need = workspace_bytes_for(num_seqs, num_tokens, num_q_heads, head_dim, splits);
+  const bool cascade = sharers != nullptr && num_sharers > 0 && num_pre_blocks > 0;
+  const int64_t casc_rows =
+      cascade ? (int64_t)num_sharers * std::min<int32_t>(max_query_len, decode_max_q(group)) : 0;
+  const size_t need =
+      ws_layout(num_seqs, num_tokens, num_q_heads, head_dim, splits, casc_rows).total;
   if (workspace == nullptr || workspace_bytes < need) return PA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return PA_ERR_INVALID;
 
-  AttnArgs a;
+  AttnArgs a = {};
   a.q = query;
   a.kc = key_cache;
   a.vc = value_cache;
@@ -351,7 +374,7 @@ pa_status attention_impl(const void* query, const void* key_cache, const void* v
   a.out = out;
   a.lse = lse;
   char* ws = static_cast<char*>(workspace);
-  const WsLayout lay = ws_layout(num_seqs, num_tokens, num_q_heads, head_dim, splits);
+  const WsLayout lay = ws_layout(num_seqs, num_tokens, num_q_heads, head_dim, splits, casc_rows);
   a.plan = reinterpret_cast<int32_t*>(ws + lay.plan);
   a.plan_tmp = reinterpret_cast<int32_t*>(ws + lay.plan_tmp);
   {
@@ -372,11 +395,22 @@ pa_status attention_impl(const void* query, const void* key_cache, const void* v
   a.part_out = nullptr;
   a.part_lse = nullptr;
   a.sem = nullptr;
-  if (splits > 1) {
+  if (splits > 1 || cascade) {
     a.part_out = reinterpret_cast<float*>(ws + lay.part_out);
     a.part_lse = reinterpret_cast<float*>(ws + lay.part_lse);
     a.sem = reinterpret_cast<int32_t*>(ws + lay.sem);
   }
+  a.sharers = cascade ? sharers : nullptr;
+  a.num_sharers = cascade ? num_sharers : 0;
+  a.pre_blocks = pre_blocks;
+  a.num_pre_blocks = cascade ? num_pre_blocks : 0;
+  a.casc_rows_max = (int32_t)casc_rows;
+  a.pre_index = cascade ? reinterpret_cast<int32_t*>(ws + lay.pre_index) : nullptr;
+  a.vtok = cascade ? reinterpret_cast<int32_t*>(ws + lay.vtok) : nullptr;
+  a.vpos = cascade ? reinterpret_cast<int32_t*>(ws + lay.vpos) : nullptr;
+  a.casc_count = cascade ? reinterpret_cast<int32_t*>(ws + lay.casc_count) : nullptr;
+  a.pre_out = cascade ? reinterpret_cast<float*>(ws + lay.pre_out) : nullptr;
+  a.pre_lse = cascade ? reinterpret_cast<float*>(ws + lay.pre_lse) : nullptr;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipSuccess;
   if (dtype == PA_F32) {
@@ -389,6 +423,7 @@ pa_status attention_impl(const void* query, const void* key_cache, const void* v
     // each request and KV head to finish does it)
     const int32_t dq = decode_max_q(group);
     if (max_query_len > dq) e = launch_prefill_bf16(a, s);
+    if (e == hipSuccess && cascade) e = launch_cascade_prefix(a, s);
     if (e == hipSuccess) e = launch_decode_bf16(a, s);
   }
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
@@ -411,6 +446,41 @@ pa_status pa_attention_fwd(const void* query, const void* key_cache, const void*
                         num_q_heads, num_kv_heads, head_dim, block_size, block_table_stride,
                         num_blocks, scale, num_splits, out, lse, workspace, workspace_bytes,
                         dtype, false, stream);
+}
+
+size_t pa_cascade_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t num_splits,
+                                 int32_t num_sharers, int32_t max_query_len) {
+  if (num_seqs < 0 || num_tokens < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      head_dim <= 0 || num_splits < 1 || num_sharers < 0 || max_query_len < 0 ||
+      num_q_heads % num_kv_heads != 0)
+    return 0;
+  const int32_t group = num_q_heads / num_kv_heads;
+  const int64_t rows =
+      (int64_t)num_sharers * std::min<int32_t>(max_query_len, decode_max_q(group));
+  return ws_layout(num_seqs, num_tokens, num_q_heads, head_dim, num_splits, rows).total;
+}
+
+pa_status pa_attention_fwd_cascade(const void* query, const void* key_cache,
+                                   const void* value_cache, const int32_t* query_start_loc,
+                                   const int32_t* seq_lens, const int32_t* block_tables,
+                                   int32_t num_seqs, int32_t num_tokens, int32_t max_query_len,
+                                   int32_t max_seq_len, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                   int32_t block_table_stride, int64_t num_blocks, float scale,
+                                   int32_t num_splits, const int32_t* sharers,
+                                   int32_t num_sharers, const int32_t* prefix_blocks,
+                                   int32_t num_prefix_blocks, void* out, float* lse,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_sharers < 0 || num_prefix_blocks < 0) return PA_ERR_INVALID;
+  if (num_sharers > 0 && num_prefix_blocks > 0 && (!sharers || !prefix_blocks))
+    return PA_ERR_NULL;
+  return attention_impl(query, key_cache, value_cache, nullptr, nullptr, query_start_loc,
+                        seq_lens, block_tables, num_seqs, num_tokens, max_query_len, max_seq_len,
+                        num_q_heads, num_kv_heads, head_dim, block_size, block_table_stride,
+                        num_blocks, scale, num_splits, out, lse, workspace, workspace_bytes,
+                        PA_BF16, false, stream, sharers, num_sharers, prefix_blocks,
+                        num_prefix_blocks);
 }
 
 pa_status pa_attention_fwd_fp8(const void* query, const void* key_cache,

@@ -21,7 +21,9 @@ enum KernelId : int32_t {
   K_ZERO = 9,
   K_KV_WRITE_FP8 = 10,
   K_ROPE_KV_WRITE = 11,
-  K_COUNT = 12
+  K_CASCADE_SETUP = 12,
+  K_CASCADE_PREFIX = 13,
+  K_COUNT = 14
 };
 
 // Tracing hooks (pa_api.cpp).  trace_before/after bracket one launch.
@@ -70,6 +72,18 @@ struct AttnArgs {
   int32_t cache_fp8;      // 1: kc / vc hold E4M3 codes (query and out bf16)
   const float* k_scale;   // [hkv] when cache_fp8: a cached K value is code * k_scale[h]
   const float* v_scale;   // [hkv] when cache_fp8
+  // shared-prefix (cascade) attention; sharers == nullptr: none
+  const int32_t* sharers;     // [num_sharers] request indices
+  int32_t num_sharers;
+  const int32_t* pre_blocks;  // [num_pre_blocks] the shared prefix's blocks
+  int32_t num_pre_blocks;
+  int32_t casc_rows_max;      // bound on gathered rows (grid of the prefix stage)
+  int32_t* pre_index;         // [num_seqs] first gathered row of each request, or -1
+  int32_t* vtok;              // [casc_rows_max]
+  int32_t* vpos;              // [casc_rows_max]
+  int32_t* casc_count;        // [1]
+  float* pre_out;             // [casc_rows_max][hq][d]
+  float* pre_lse;             // [casc_rows_max][hq]
 };
 
 // Largest number of new tokens per request that the decode kernel packs.
@@ -89,6 +103,9 @@ inline int32_t prefill_tile_tokens(int32_t group) {
 
 hipError_t launch_decode_bf16(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t stream);
+// shared-prefix stage: gather the sharers' decode rows, attend them to the
+// shared blocks (partials in pre_out / pre_lse); the decode kernel merges
+hipError_t launch_cascade_prefix(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_zero(void* ptr, size_t bytes, hipStream_t stream);
 hipError_t launch_combine(const float* po, const float* pl, int32_t splits,

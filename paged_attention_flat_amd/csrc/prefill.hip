@@ -58,6 +58,14 @@ struct PrefillParams {
   float scale_log2;
   uint16_t* out;
   float* lse;
+  // shared-prefix (cascade) stage: gathered decode rows of the sharers
+  const int32_t* casc_count;  // [1] rows gathered
+  const int32_t* vtok;        // [rows] flat token of each gathered row
+  const int32_t* vpos;        // [rows] its position
+  const int32_t* pre_blocks;  // the shared prefix's physical blocks
+  int32_t pre_tokens;         // 16 * number of prefix blocks
+  float* pre_out;             // [rows][hq][D] fp32 normalised partial
+  float* pre_lse;             // [rows][hq] natural-log lse of the partial
 };
 
 constexpr int kPlanBuckets = 4096;
@@ -153,7 +161,11 @@ __device__ __forceinline__ int vperm(int k) {
   return (k & 3) | ((k & 4) << 1) | ((k & 8) >> 1);
 }
 
-template <int D, int G, int NW, int RG, int kBK, bool F8>
+// CASC: the prefix stage of shared-prefix attention -- work-group tiles are
+// consecutive gathered rows (decode tokens of the sharers, each with its own
+// position), keys are the shared prefix blocks, and the result is a partial
+// (normalised fp32 output and lse) merged later by the decode kernel.
+template <int D, int G, int NW, int RG, int kBK, bool F8, bool CASC>
 __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
   typedef typename Frag8<F8>::elem CT;
   typedef typename Frag8<F8>::raw RT;
@@ -172,17 +184,26 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
 
   const int kvh = blockIdx.x % p.hkv;
   const int item = blockIdx.x / p.hkv;
-  if (item >= p.plan[0]) return;
-  const int b = p.plan[1 + 2 * item];
-  const int tile = p.plan[2 + 2 * item];
+  int b = 0, tile, q0, q_len, seq_len, ctx;
+  if constexpr (CASC) {
+    tile = item;
+    q_len = p.casc_count[0];  // rows gathered
+    if (tile * TQ >= q_len) return;
+    q0 = 0;
+    seq_len = p.pre_tokens;
+    ctx = 0;
+  } else {
+    if (item >= p.plan[0]) return;
+    b = p.plan[1 + 2 * item];
+    tile = p.plan[2 + 2 * item];
+    q0 = p.qsl[b];
+    q_len = p.qsl[b + 1] - q0;
+    seq_len = p.seq_lens[b];
+    ctx = seq_len - q_len;
+  }
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int row = lane & 31, kg = lane >> 5;
-
-  const int q0 = p.qsl[b];
-  const int q_len = p.qsl[b + 1] - q0;
-  const int seq_len = p.seq_lens[b];
-  const int ctx = seq_len - q_len;
   const int tok0 = tile * TQ;
 
   // row group rg of this wave: work-group rows WROWS*wave + 32*rg + row,
@@ -195,17 +216,21 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
     tokr[rg] = tok0 + r / G;
     gr[rg] = r - (r / G) * G;
     valid[rg] = tokr[rg] < q_len;
-    pos[rg] = ctx + min(tokr[rg], q_len - 1);
+    // CASC: a row sees the prefix up to its own position; keys past the
+    // prefix (zero-filled in the last tile) are masked like later positions
+    if constexpr (CASC) pos[rg] = min(p.vpos[min(tokr[rg], q_len - 1)], seq_len - 1);
+    else pos[rg] = ctx + min(tokr[rg], q_len - 1);
   }
-  const int wpos_lo = ctx + min(tok0 + (WROWS * wave) / G, q_len - 1);
-  const int kend = ctx + min(tok0 + TQ, q_len);  // one past the last visible key
+  // CASC: rows carry unrelated positions, so every tile is masked per row
+  const int wpos_lo = CASC ? -1 : ctx + min(tok0 + (WROWS * wave) / G, q_len - 1);
+  const int kend = CASC ? seq_len : ctx + min(tok0 + TQ, q_len);  // one past the last key
 
   bf16x8 qf[RG][QSTEPS];
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) {
     if (valid[rg]) {
-      const uint16_t* qrow =
-          p.q + ((size_t)(q0 + tokr[rg]) * p.hq + kvh * G + gr[rg]) * D + 8 * kg;
+      const size_t qtok = CASC ? (size_t)p.vtok[tokr[rg]] : (size_t)(q0 + tokr[rg]);
+      const uint16_t* qrow = p.q + (qtok * p.hq + kvh * G + gr[rg]) * D + 8 * kg;
 #pragma unroll
       for (int st = 0; st < QSTEPS; ++st)
         qf[rg][st] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 16 * st));
@@ -215,7 +240,7 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
     }
   }
 
-  const int32_t* table = p.tables + (size_t)b * p.table_stride;
+  const int32_t* table = CASC ? p.pre_blocks : p.tables + (size_t)b * p.table_stride;
   const size_t head_elems = 16 * D;
   const size_t block_elems = (size_t)p.hkv * head_elems;
   const CT* kbase = static_cast<const CT*>(p.kc) + kvh * head_elems;
@@ -509,8 +534,23 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
     const float lt = l[rg] + shfl_xor(l[rg], 32);
     if (!valid[rg]) continue;
     const float inv = v_scale / lt;
-    const int t = q0 + tokr[rg];
     const int h = kvh * G + gr[rg];
+    if constexpr (CASC) {
+      // the prefix partial of gathered row tokr: fp32, normalised
+      float* prow = p.pre_out + ((size_t)tokr[rg] * p.hq + h) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x16& a = acc[rg][db];
+          *reinterpret_cast<float4*>(prow + 32 * db + 8 * i + 4 * kg) =
+              make_float4(a[4 * i] * inv, a[4 * i + 1] * inv, a[4 * i + 2] * inv,
+                          a[4 * i + 3] * inv);
+        }
+      if (kg == 0) p.pre_lse[(size_t)tokr[rg] * p.hq + h] = (m[rg] + fast_log2(lt)) * kLn2;
+      continue;
+    }
+    const int t = q0 + tokr[rg];
     uint16_t* orow = p.out + ((size_t)t * p.hq + h) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -556,7 +596,91 @@ void launch_dg(const AttnArgs& a, hipStream_t stream) {
                      a.plan_cap);
   trace_after(stream);
   trace_before(K_PREFILL, stream);
-  hipLaunchKernelGGL((prefill_kernel<D, G, NW, RG, BK, F8>), dim3(a.plan_cap * a.hkv),
+  hipLaunchKernelGGL((prefill_kernel<D, G, NW, RG, BK, F8, false>), dim3(a.plan_cap * a.hkv),
+                     dim3(64 * NW), 0, stream, p);
+  trace_after(stream);
+}
+
+// Gathered decode rows of the sharers of a shared prefix: pre_index[b] = first
+// gathered row of request b (or -1), vtok / vpos = flat token and position of
+// every gathered row, count in casc_count[0].  Requests whose rows the decode
+// kernel handles (0 < q_len <= dq, dq also bounded by the host's
+// max_query_len, which sized the gathered-row buffers) take part; others keep
+// pre_index = -1 and read the prefix themselves.  One work-group.
+__global__ __launch_bounds__(1024) void cascade_setup_kernel(
+    const int32_t* __restrict__ sharers, int32_t num_sharers, const int32_t* __restrict__ qsl,
+    const int32_t* __restrict__ seq_lens, int32_t num_seqs, int32_t dq,
+    int32_t* __restrict__ pre_index, int32_t* __restrict__ vtok, int32_t* __restrict__ vpos,
+    int32_t* __restrict__ count) {
+  __shared__ int s_scan[1024];
+  __shared__ int s_base;
+  const int tid = threadIdx.x;
+  for (int b = tid; b < num_seqs; b += 1024) pre_index[b] = -1;
+  if (tid == 0) s_base = 0;
+  __syncthreads();
+  for (int c0 = 0; c0 < num_sharers; c0 += 1024) {
+    const int i = c0 + tid;
+    int b = -1, ql = 0;
+    if (i < num_sharers) {
+      b = sharers[i];
+      if (b >= 0 && b < num_seqs) {
+        ql = qsl[b + 1] - qsl[b];
+        if (ql <= 0 || ql > dq) ql = 0;
+      }
+    }
+    s_scan[tid] = ql;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int v = tid >= off ? s_scan[tid - off] : 0;
+      __syncthreads();
+      s_scan[tid] += v;
+      __syncthreads();
+    }
+    const int v0 = s_base + s_scan[tid] - ql;
+    if (ql > 0) {
+      pre_index[b] = v0;
+      const int ctx = seq_lens[b] - ql;
+      for (int j = 0; j < ql; ++j) {
+        vtok[v0 + j] = qsl[b] + j;
+        vpos[v0 + j] = ctx + j;
+      }
+    }
+    __syncthreads();
+    if (tid == 1023) s_base += s_scan[1023];
+    __syncthreads();
+  }
+  if (tid == 0) count[0] = s_base;
+}
+
+template <int D, int G>
+void launch_cascade_dg(const AttnArgs& a, hipStream_t stream) {
+  constexpr int NW = PA_PREFILL_WAVES;
+  constexpr int RG = PA_PREFILL_ROW_GROUPS;
+  constexpr int BK = PA_PREFILL_KEYS;
+  constexpr int TQ = 32 * RG * NW / G;
+  PrefillParams p = {};
+  p.q = (const uint16_t*)a.q;
+  p.kc = a.kc;
+  p.vc = a.vc;
+  p.hq = a.hq;
+  p.hkv = a.hkv;
+  p.scale_log2 = a.scale * kLog2e;
+  p.casc_count = a.casc_count;
+  p.vtok = a.vtok;
+  p.vpos = a.vpos;
+  p.pre_blocks = a.pre_blocks;
+  p.pre_tokens = 16 * a.num_pre_blocks;
+  p.pre_out = a.pre_out;
+  p.pre_lse = a.pre_lse;
+  trace_before(K_CASCADE_SETUP, stream);
+  hipLaunchKernelGGL(cascade_setup_kernel, dim3(1), dim3(1024), 0, stream, a.sharers,
+                     a.num_sharers, a.qsl, a.seq_lens, a.num_seqs,
+                     min(decode_max_q(G), a.max_query_len), a.pre_index,
+                     a.vtok, a.vpos, a.casc_count);
+  trace_after(stream);
+  const int tiles = (a.casc_rows_max + TQ - 1) / TQ;
+  trace_before(K_CASCADE_PREFIX, stream);
+  hipLaunchKernelGGL((prefill_kernel<D, G, NW, RG, BK, false, true>), dim3(tiles * a.hkv),
                      dim3(64 * NW), 0, stream, p);
   trace_after(stream);
 }
@@ -573,6 +697,27 @@ void launch_d(const AttnArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_cascade_prefix(const AttnArgs& a, hipStream_t stream) {
+  if (a.d == 64) {
+    switch (a.hq / a.hkv) {
+      case 1: launch_cascade_dg<64, 1>(a, stream); break;
+      case 2: launch_cascade_dg<64, 2>(a, stream); break;
+      case 4: launch_cascade_dg<64, 4>(a, stream); break;
+      case 8: launch_cascade_dg<64, 8>(a, stream); break;
+      default: launch_cascade_dg<64, 16>(a, stream); break;
+    }
+  } else {
+    switch (a.hq / a.hkv) {
+      case 1: launch_cascade_dg<128, 1>(a, stream); break;
+      case 2: launch_cascade_dg<128, 2>(a, stream); break;
+      case 4: launch_cascade_dg<128, 4>(a, stream); break;
+      case 8: launch_cascade_dg<128, 8>(a, stream); break;
+      default: launch_cascade_dg<128, 16>(a, stream); break;
+    }
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t stream) {
   if (a.cache_fp8) {
