@@ -164,7 +164,7 @@ class StepRunner:
     """Enqueues one step (KV write + attention) on the current stream, calling
     the C ABI directly with pre-marshalled arguments."""
 
-    def __init__(self, step, dev, num_splits, pools=None):
+    def __init__(self, step, dev, num_splits, pools=None, cascade=None):
         import ctypes
 
         import torch
@@ -217,6 +217,22 @@ class StepRunner:
                               step.num_blocks, ctypes.c_float(step.scale), self.splits,
                               P(g["out"]), P(g["lse"]), P(g["ws"]), ws, code]
             self.kv_fn, self.attn_fn = self.lib.pa_kv_write, self.lib.pa_attention_fwd
+        if cascade is not None:
+            # shared-prefix attention: (sharer request ids, prefix block ids)
+            sh, pb = cascade
+            g["sharers"] = torch.as_tensor(sh, dtype=torch.int32).to(dev)
+            g["prefix"] = torch.as_tensor(pb, dtype=torch.int32).to(dev)
+            need = self.lib.pa_cascade_workspace_size(step.num_seqs, nt, hq, hkv, d, self.splits,
+                                                      g["sharers"].numel(), step.max_query_len,
+                                                      g["prefix"].numel())
+            g["ws"] = torch.zeros(need, dtype=torch.uint8, device=dev)
+            self.attn_args = [P(g["query"]), P(g["kc"]), P(g["vc"]), P(g["qsl"]), P(g["sl"]),
+                              P(g["bt"]), step.num_seqs, nt, step.max_query_len,
+                              step.max_seq_len, hq, hkv, d, 16, g["bt"].shape[1],
+                              step.num_blocks, ctypes.c_float(step.scale), self.splits,
+                              P(g["sharers"]), g["sharers"].numel(), P(g["prefix"]),
+                              g["prefix"].numel(), P(g["out"]), P(g["lse"]), P(g["ws"]), need]
+            self.attn_fn = self.lib.pa_attention_fwd_cascade
 
     def __call__(self):
         s = self.ctypes.c_void_p(self.torch.cuda.current_stream().cuda_stream)
@@ -574,6 +590,33 @@ def bench_rope(args, log):
     return out
 
 
+def bench_shared_prefix(args, log):
+    """256 decodes sharing a 16384-token prefix (private suffixes of 0..512
+    tokens): plain attention re-reads the 64 MiB prefix per request, the
+    cascade reads it once per tile of gathered rows."""
+    import torch
+
+    from workloads import shared_prefix_step
+    dev = torch.device("cuda:0")
+    step = shared_prefix_step(256, 16384, 0, 512, 11, device=dev, fill="zero")
+    wm = work_model(step)
+    prefix = list(step.info["shared_blocks"])
+    r = StepRunner(step, dev, 0)
+    rc = StepRunner(step, dev, 0, pools=(r.g["kc"], r.g["vc"]),
+                    cascade=(list(range(step.num_seqs)), prefix))
+    res = {"workload": "256 decodes sharing a 16384-token prefix + 0..512 private tokens "
+                       "(Hq 32/Hkv 8, d 128, bf16)", "step_bytes_unique": wm["bytes"]}
+    for name, run in (("plain", r), ("shared_prefix_read_once", rc)):
+        ms, _ = time_steps([run], args.extra_steps, 3, not args.eager, log)
+        kt = kernel_times([run], min(args.extra_steps, 20), log)
+        res[name] = {"ms_per_step": ms, "step_GBps_unique": wm["bytes"] / (ms * 1e-3) / 1e9,
+                     "kernels_us": {k: round(v["avg_us"], 2) for k, v in kt.items()}}
+    log(f"shared prefix: {json.dumps(res)}")
+    del r, rc, step
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_config1(args, log):
     """The tiny fp32 mixed step: GPU time per step and the oracle's
     CPU-seconds for the same step (correctness workload, no roofline)."""
@@ -632,6 +675,19 @@ def bench_extra(cfg, args, log):
     if cfg == 5:
         t_roof = max(wm["bytes"] / (PEAK_HBM_GBS * 1e9), wm["flops"] / (PEAK_BF16_TFLOPS * 1e12))
         out["step_roofline_frac"] = t_roof / (ms * 1e-3)
+        # the same step with the shared 1024-token prefix read once
+        prefix = list(step.info["shared_blocks"])
+        P = len(prefix)
+        bt = step.block_tables
+        sharers = [b for b in range(step.num_seqs) if list(bt[b, :P]) == prefix]
+        rc = StepRunner(step, dev, 0, pools=(r.g["kc"], r.g["vc"]), cascade=(sharers, prefix))
+        cms, _ = time_steps([rc], args.extra_steps, 3, not args.eager, log)
+        ckt = kernel_times([rc], min(args.extra_steps, 20), log)
+        out["shared_prefix_read_once"] = {
+            "sharers": len(sharers), "prefix_blocks": P, "ms_per_step": cms,
+            "step_GBps": wm["bytes"] / (cms * 1e-3) / 1e9,
+            "kernels_us": {k: round(v["avg_us"], 2) for k, v in ckt.items()}}
+        del rc
     log(f"config{cfg}: {json.dumps(out)}")
     del r
     torch.cuda.empty_cache()
@@ -705,6 +761,7 @@ def main():
     cfg1 = None
     fp8 = None
     rope = None
+    shared = None
     if not args.only_main:
         sweep = split_sweep(args, log)
         for cfg in (3, 4, 5):
@@ -712,6 +769,7 @@ def main():
             extras.append(bench_extra(cfg, args, log))
         fp8 = bench_fp8(args, log)
         rope = bench_rope(args, log)
+        shared = bench_shared_prefix(args, log)
         cfg1 = bench_config1(args, log)
         ach = achievable(log)
     cpu = None
@@ -747,6 +805,7 @@ def main():
         "extra_workloads": extras,
         "fp8_kv_cache": fp8,
         "rope_kv_write": rope,
+        "shared_prefix": shared,
         "correctness_workload": cfg1,
         "achievable": ach,
     }

@@ -195,7 +195,8 @@ pa_status pa_rope_kv_write(void* query, const void* key, const void* value,
  * sharer's own later blocks and merges that partial with its splits.  The
  * result is the attention of pa_attention_fwd (up to rounding): causality is
  * kept per row, so a sharer whose context is shorter than the prefix is still
- * exact.  Sharers with more new tokens than the decode kernel packs, or none,
+ * exact.  The prefix keys are cut into ranges (one partial each) so that the
+ * stage fills the device even for few sharers.  Sharers with more new tokens than the decode kernel packs, or none,
  * are computed as usual.  Workspace: pa_cascade_workspace_size (zeroed once
  * like pa_attention_fwd's).  Every other argument and error as
  * pa_attention_fwd with dtype PA_BF16.
@@ -215,10 +216,11 @@ pa_status pa_attention_fwd_cascade(const void* query, const void* key_cache,
                                    size_t workspace_bytes, void* stream);
 
 /* pa_cascade_workspace_size -- bytes of workspace for pa_attention_fwd_cascade
- * (num_splits resolved, >= 1). */
+ * (num_splits resolved, >= 1; on the device the call will run on). */
 size_t pa_cascade_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
                                  int32_t num_kv_heads, int32_t head_dim, int32_t num_splits,
-                                 int32_t num_sharers, int32_t max_query_len);
+                                 int32_t num_sharers, int32_t max_query_len,
+                                 int32_t num_prefix_blocks);
 
 /*
  * FP8 KV cache (E4M3).  The pages name an 8-bit cache as the way to halve the

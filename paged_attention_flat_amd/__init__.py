@@ -217,7 +217,8 @@ def attention_cascade(query, key_cache, value_cache, query_start_loc, seq_lens, 
     if lse is None and want_lse:
         lse = torch.empty(nt, hq, dtype=torch.float32, device=query.device)
     need = int(LIB.pa_cascade_workspace_size(ns, nt, hq, hkv, d, max(1, splits),
-                                             sharers.numel(), int(max_query_len)))
+                                             sharers.numel(), int(max_query_len),
+                                             prefix_blocks.numel()))
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.zeros(need, dtype=torch.uint8, device=query.device)
     st = LIB.pa_attention_fwd_cascade(

@@ -63,9 +63,11 @@ struct DecodeParams {
   // shared-prefix attention: sharers skip the first pre_blocks blocks and
   // merge the prefix partial (row pre_index[b] + token) with their splits
   const int32_t* pre_index;  // nullable: [num_seqs], -1 for a non-sharer
-  const float* pre_out;
-  const float* pre_lse;
+  const float* pre_out;      // [pre_splits][pre_rows][hq][D]
+  const float* pre_lse;      // [pre_splits][pre_rows][hq]
   int32_t pre_blocks;
+  int32_t pre_splits;        // prefix partials per row (key ranges)
+  int32_t pre_rows;
 };
 
 // Two launch shapes.  Many work units: 8 waves per work-group, one pair in
@@ -388,6 +390,41 @@ __global__ __launch_bounds__(64 * NW, (PIPE == 2 && NW < 8 ? 8 / NW : 1)) void d
             make_uint2(pack_bf16x2(acc[db][0] * inv, acc[db][1] * inv),
                        pack_bf16x2(acc[db][2] * inv, acc[db][3] * inv));
       if (p.lse != nullptr && kg == 0) p.lse[(size_t)t * p.hq + h] = (m + fast_log2(l)) * kLn2;
+    } else if (p.splits == 1) {
+      // a sharer without a split: merge the prefix partials (written by the
+      // previous launch on this stream) with this work-group's own result
+      const size_t prer = (size_t)(pv0 + qi) * p.hq + h;
+      const size_t kstride = (size_t)p.pre_rows * p.hq;
+      const float lb = (l == 0.f) ? -INFINITY : (m + fast_log2(l)) * kLn2;
+      float M = lb;
+      for (int ks = 0; ks < p.pre_splits; ++ks) M = fmaxf(M, p.pre_lse[ks * kstride + prer]);
+      const float wb = (lb == -INFINITY) ? 0.f : fast_exp2((lb - M) * kLog2e);
+      float den = wb;
+      float4 o[DB];
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const float cb = (l == 0.f) ? 0.f : wb * v_scale / l;
+        o[db] = make_float4(cb * acc[db][0], cb * acc[db][1], cb * acc[db][2], cb * acc[db][3]);
+      }
+      for (int ks = 0; ks < p.pre_splits; ++ks) {
+        const float la = p.pre_lse[ks * kstride + prer];
+        const float wa = (la == -INFINITY) ? 0.f : fast_exp2((la - M) * kLog2e);
+        den += wa;
+        const float* src = p.pre_out + (ks * kstride + prer) * D + 4 * kg;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const float4 oa = *reinterpret_cast<const float4*>(src + 16 * db);
+          o[db].x += wa * oa.x; o[db].y += wa * oa.y; o[db].z += wa * oa.z; o[db].w += wa * oa.w;
+        }
+      }
+      const float inv = 1.f / den;
+      uint16_t* dst = p.out + ((size_t)t * p.hq + h) * D + 4 * kg;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        *reinterpret_cast<uint2*>(dst + 16 * db) =
+            make_uint2(pack_bf16x2(o[db].x * inv, o[db].y * inv),
+                       pack_bf16x2(o[db].z * inv, o[db].w * inv));
+      if (p.lse != nullptr && kg == 0) p.lse[(size_t)t * p.hq + h] = M + fast_log2(den) * kLn2;
     } else {
       const bool empty = (l == 0.f);
       const float inv = empty ? 0.f : v_scale / l;
@@ -407,7 +444,7 @@ __global__ __launch_bounds__(64 * NW, (PIPE == 2 && NW < 8 ? 8 / NW : 1)) void d
                            __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  if (!merged || p.sem == nullptr) return;
+  if (!merged || p.splits == 1 || p.sem == nullptr) return;
 
   // ---- merge of the split partials by the last split to finish ------------
   // ("combining the partials in a second reduction", here done by whichever
@@ -441,7 +478,9 @@ __global__ __launch_bounds__(64 * NW, (PIPE == 2 && NW < 8 ? 8 / NW : 1)) void d
   const int items = rows * QUADS;
   const int sg = items >= NT ? 1 : NT / items;
   const size_t split_rows = (size_t)p.nt * p.hq;
-  const int nparts = p.splits + (pv0 >= 0 ? 1 : 0);  // the prefix partial comes last
+  // the prefix partials (one per key range) come after the splits
+  const int nparts = p.splits + (pv0 >= 0 ? p.pre_splits : 0);
+  const size_t kstride = (size_t)p.pre_rows * p.hq;
   float* s_m = &s_x[0][0][0];  // [6][NT] staging for the group merge
   static_assert(sizeof(s_x) >= 6 * NT * sizeof(float), "LDS staging too small");
   for (int base = 0; base < items * sg; base += NT) {
@@ -468,8 +507,9 @@ __global__ __launch_bounds__(64 * NW, (PIPE == 2 && NW < 8 ? 8 / NW : 1)) void d
             x[c] = p.part_lse[sp * split_rows + rowi];
             v[c] = *reinterpret_cast<const float4*>(ob + sp * split_rows * D);
           } else if (sp < nparts) {
-            x[c] = p.pre_lse[prer];
-            v[c] = *reinterpret_cast<const float4*>(p.pre_out + prer * D + quad * 4);
+            const size_t pi = (size_t)(sp - p.splits) * kstride + prer;
+            x[c] = p.pre_lse[pi];
+            v[c] = *reinterpret_cast<const float4*>(p.pre_out + pi * D + quad * 4);
           }
         }
         float mc = mm;
@@ -565,6 +605,8 @@ void launch_dg(const AttnArgs& a, hipStream_t stream) {
   p.pre_out = a.pre_out;
   p.pre_lse = a.pre_lse;
   p.pre_blocks = a.num_pre_blocks;
+  p.pre_splits = a.casc_ksplits;
+  p.pre_rows = a.casc_rows_max;
   if (a.decode_order != nullptr) {
     int shift = 0;
     const int max_blocks = (a.max_seq_len + 15) / 16;

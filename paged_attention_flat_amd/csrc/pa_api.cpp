@@ -86,7 +86,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // casc_rows > 0: room for the shared-prefix stage (gathered rows, their
 // partials) and split partials even at one split (sharers always merge).
 WsLayout ws_layout(int32_t num_seqs, int32_t num_tokens, int32_t hq, int32_t d, int32_t splits,
-                   int64_t casc_rows = 0) {
+                   int64_t casc_rows = 0, int32_t casc_ksplits = 1) {
   WsLayout w = {};
   const size_t cap = plan_capacity(num_seqs, num_tokens);
   // arrival counters of the split merge, one per (request, KV head <= Hq);
@@ -109,11 +109,27 @@ WsLayout ws_layout(int32_t num_seqs, int32_t num_tokens, int32_t hq, int32_t d, 
     w.vtok = align256(w.pre_index + (size_t)num_seqs * sizeof(int32_t));
     w.vpos = align256(w.vtok + R * sizeof(int32_t));
     w.casc_count = align256(w.vpos + R * sizeof(int32_t));
+    const size_t KR = (size_t)casc_ksplits * R;
     w.pre_out = align256(w.casc_count + sizeof(int32_t));
-    w.pre_lse = align256(w.pre_out + R * hq * d * sizeof(float));
-    w.total = align256(w.pre_lse + R * hq * sizeof(float));
+    w.pre_lse = align256(w.pre_out + KR * hq * d * sizeof(float));
+    w.total = align256(w.pre_lse + KR * hq * sizeof(float));
   }
   return w;
+}
+
+// Key ranges of the shared-prefix stage: enough work-groups for about two
+// per compute unit, each range a whole number of 64-key tiles.
+void cascade_key_split(int32_t num_pre_blocks, int64_t casc_rows, int32_t group, int32_t hkv,
+                       int32_t num_cus, int32_t* ksplits, int32_t* kchunk) {
+  const int64_t tq = prefill_tile_tokens(group);
+  const int64_t tiles = std::max<int64_t>(1, (casc_rows + tq - 1) / tq);
+  const int64_t units = tiles * hkv;
+  const int64_t ktiles = std::max<int64_t>(1, (num_pre_blocks + 3) / 4);  // 64-key tiles
+  int64_t ks = std::max<int64_t>(1, (2 * (int64_t)num_cus + units - 1) / units);
+  ks = std::min<int64_t>(ks, std::min<int64_t>(ktiles, 64));
+  const int64_t per = (ktiles + ks - 1) / ks;                  // tiles per range
+  *ksplits = (int32_t)((ktiles + per - 1) / per);              // no empty range
+  *kchunk = (int32_t)(per * 64);
 }
 
 size_t workspace_bytes_for(int32_t num_seqs, int32_t num_tokens, int32_t hq, int32_t d,
@@ -349,8 +365,12 @@ pa_status attention_impl(const void* query, const void* key_cache, const void* v
   const bool cascade = sharers != nullptr && num_sharers > 0 && num_pre_blocks > 0;
   const int64_t casc_rows =
       cascade ? (int64_t)num_sharers * std::min<int32_t>(max_query_len, decode_max_q(group)) : 0;
+  int32_t ksplits = 1, kchunk = 0;
+  if (cascade)
+    cascade_key_split(num_pre_blocks, casc_rows, group, num_kv_heads, device_cu_count(), &ksplits,
+                      &kchunk);
   const size_t need =
-      ws_layout(num_seqs, num_tokens, num_q_heads, head_dim, splits, casc_rows).total;
+      ws_layout(num_seqs, num_tokens, num_q_heads, head_dim, splits, casc_rows, ksplits).total;
   if (workspace == nullptr || workspace_bytes < need) return PA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return PA_ERR_INVALID;
 
@@ -374,7 +394,8 @@ pa_status attention_impl(const void* query, const void* key_cache, const void* v
   a.out = out;
   a.lse = lse;
   char* ws = static_cast<char*>(workspace);
-  const WsLayout lay = ws_layout(num_seqs, num_tokens, num_q_heads, head_dim, splits, casc_rows);
+  const WsLayout lay =
+      ws_layout(num_seqs, num_tokens, num_q_heads, head_dim, splits, casc_rows, ksplits);
   a.plan = reinterpret_cast<int32_t*>(ws + lay.plan);
   a.plan_tmp = reinterpret_cast<int32_t*>(ws + lay.plan_tmp);
   {
@@ -405,6 +426,8 @@ pa_status attention_impl(const void* query, const void* key_cache, const void* v
   a.pre_blocks = pre_blocks;
   a.num_pre_blocks = cascade ? num_pre_blocks : 0;
   a.casc_rows_max = (int32_t)casc_rows;
+  a.casc_ksplits = ksplits;
+  a.casc_kchunk = kchunk;
   a.pre_index = cascade ? reinterpret_cast<int32_t*>(ws + lay.pre_index) : nullptr;
   a.vtok = cascade ? reinterpret_cast<int32_t*>(ws + lay.vtok) : nullptr;
   a.vpos = cascade ? reinterpret_cast<int32_t*>(ws + lay.vpos) : nullptr;
@@ -450,15 +473,21 @@ pa_status pa_attention_fwd(const void* query, const void* key_cache, const void*
 
 size_t pa_cascade_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
                                  int32_t num_kv_heads, int32_t head_dim, int32_t num_splits,
-                                 int32_t num_sharers, int32_t max_query_len) {
+                                 int32_t num_sharers, int32_t max_query_len,
+                                 int32_t num_prefix_blocks) {
   if (num_seqs < 0 || num_tokens < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
       head_dim <= 0 || num_splits < 1 || num_sharers < 0 || max_query_len < 0 ||
-      num_q_heads % num_kv_heads != 0)
+      num_prefix_blocks < 0 || num_q_heads % num_kv_heads != 0)
     return 0;
   const int32_t group = num_q_heads / num_kv_heads;
-  const int64_t rows =
-      (int64_t)num_sharers * std::min<int32_t>(max_query_len, decode_max_q(group));
-  return ws_layout(num_seqs, num_tokens, num_q_heads, head_dim, num_splits, rows).total;
+  const int64_t rows = num_prefix_blocks > 0 ? (int64_t)num_sharers *
+                                                   std::min<int32_t>(max_query_len,
+                                                                     decode_max_q(group))
+                                             : 0;
+  int32_t ks = 1, kc = 0;
+  if (rows > 0)
+    cascade_key_split(num_prefix_blocks, rows, group, num_kv_heads, device_cu_count(), &ks, &kc);
+  return ws_layout(num_seqs, num_tokens, num_q_heads, head_dim, num_splits, rows, ks).total;
 }
 
 pa_status pa_attention_fwd_cascade(const void* query, const void* key_cache,

@@ -78,12 +78,14 @@ struct AttnArgs {
   const int32_t* pre_blocks;  // [num_pre_blocks] the shared prefix's blocks
   int32_t num_pre_blocks;
   int32_t casc_rows_max;      // bound on gathered rows (grid of the prefix stage)
+  int32_t casc_ksplits;       // key ranges of the prefix stage (partials per row)
+  int32_t casc_kchunk;        // keys per range, a multiple of 64
   int32_t* pre_index;         // [num_seqs] first gathered row of each request, or -1
   int32_t* vtok;              // [casc_rows_max]
   int32_t* vpos;              // [casc_rows_max]
   int32_t* casc_count;        // [1]
-  float* pre_out;             // [casc_rows_max][hq][d]
-  float* pre_lse;             // [casc_rows_max][hq]
+  float* pre_out;             // [casc_ksplits][casc_rows_max][hq][d]
+  float* pre_lse;             // [casc_ksplits][casc_rows_max][hq]
 };
 
 // Largest number of new tokens per request that the decode kernel packs.

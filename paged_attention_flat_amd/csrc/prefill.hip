@@ -64,8 +64,11 @@ struct PrefillParams {
   const int32_t* vpos;        // [rows] its position
   const int32_t* pre_blocks;  // the shared prefix's physical blocks
   int32_t pre_tokens;         // 16 * number of prefix blocks
-  float* pre_out;             // [rows][hq][D] fp32 normalised partial
-  float* pre_lse;             // [rows][hq] natural-log lse of the partial
+  int32_t pre_splits;         // key ranges of the prefix (one partial each)
+  int32_t pre_chunk;          // keys per range (a multiple of the key tile)
+  int32_t pre_rows;           // row capacity of one range's partial arrays
+  float* pre_out;             // [splits][rows][hq][D] fp32 normalised partials
+  float* pre_lse;             // [splits][rows][hq] natural-log lse (-inf: no key)
 };
 
 constexpr int kPlanBuckets = 4096;
@@ -185,8 +188,12 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
   const int kvh = blockIdx.x % p.hkv;
   const int item = blockIdx.x / p.hkv;
   int b = 0, tile, q0, q_len, seq_len, ctx;
+  int kbeg = 0, ksplit = 0;
   if constexpr (CASC) {
-    tile = item;
+    // work-group = (row tile, prefix key range, KV head)
+    ksplit = item % p.pre_splits;
+    tile = item / p.pre_splits;
+    kbeg = ksplit * p.pre_chunk;
     q_len = p.casc_count[0];  // rows gathered
     if (tile * TQ >= q_len) return;
     q0 = 0;
@@ -223,7 +230,8 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
   }
   // CASC: rows carry unrelated positions, so every tile is masked per row
   const int wpos_lo = CASC ? -1 : ctx + min(tok0 + (WROWS * wave) / G, q_len - 1);
-  const int kend = CASC ? seq_len : ctx + min(tok0 + TQ, q_len);  // one past the last key
+  const int kend = CASC ? min(seq_len, kbeg + p.pre_chunk)
+                        : ctx + min(tok0 + TQ, q_len);  // one past the last key
 
   bf16x8 qf[RG][QSTEPS];
 #pragma unroll
@@ -275,7 +283,7 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
     v_key[i] = bi * 16 + half * 8;
     v_dst[i] = d * (kBK + kVPad) + bi * 16;
   }
-  int tab_base = 0;
+  int tab_base = (kbeg >> 4) / kTabWin * kTabWin;
   RT kr[KCH], vr[VCH];
   auto gload = [&](int k0) {
     const int tb = (k0 >> 4) - tab_base;
@@ -367,9 +375,9 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
   auto load_tab = [&](int base) {
     for (int i = tid; i < kTabWin; i += NT) s_tab[i] = (base + i < nblk) ? table[base + i] : 0;
   };
-  load_tab(0);
+  load_tab(tab_base);
   __syncthreads();
-  gload(0);
+  gload(kbeg);
   lstore(0, 0);
   __syncthreads();
 
@@ -407,7 +415,7 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
     for (int ps = 0; ps < PS; ++ps) pprev[rg][ps] = as_bf16x8(make_uint4(0, 0, 0, 0));
   int vprev = 0;
   int it = 0;
-  for (int k0 = 0; k0 < kend; k0 += kBK, ++it) {
+  for (int k0 = kbeg; k0 < kend; k0 += kBK, ++it) {
     const int kbuf = it & 1, vbuf = it % 3;
     const bool more = k0 + kBK < kend;
     // a moved max of the previous tile: acc now holds every P.V up to two
@@ -486,6 +494,12 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
       // finite once the wave has met key 0, which every row sees
       m_new[rg] = move[rg] ? fmaxf(m[rg], mt) : m[rg];
     }
+    // exponent reference: CASC rows that have seen no key yet (m = -inf)
+    // take 0, so their masked scores give P = 0 rather than NaN
+    float m_ref[RG];
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+      m_ref[rg] = (CASC && m_new[rg] == -INFINITY) ? 0.f : m_new[rg];
 
     // ---- P.V of the previous tile, interleaved with this tile's softmax -----
     pv(vprev, pprev);
@@ -496,7 +510,7 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          s[rg][kb][j] = fast_exp2(__builtin_fmaf(s[rg][kb][j], scale_log2, -m_new[rg]));
+          s[rg][kb][j] = fast_exp2(__builtin_fmaf(s[rg][kb][j], scale_log2, -m_ref[rg]));
           ps4[j & 3] += s[rg][kb][j];
         }
       const float rs = (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
@@ -510,7 +524,8 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
       }
       // a moved max rescales l now and acc at the top of the next iteration,
       // after the previous tile's P.V (accumulated at the old max) is in
-      alpha[rg] = fast_exp2(m[rg] - m_new[rg]);  // 1 when the max stays
+      // 1 when the max stays (CASC: also while a row has seen no key yet)
+      alpha[rg] = (CASC && m_new[rg] == -INFINITY) ? 1.f : fast_exp2(m[rg] - m_new[rg]);
       rescale[rg] = move[rg];
       l[rg] = l[rg] * alpha[rg] + rs;
       m[rg] = m_new[rg];
@@ -536,18 +551,21 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
     const float inv = v_scale / lt;
     const int h = kvh * G + gr[rg];
     if constexpr (CASC) {
-      // the prefix partial of gathered row tokr: fp32, normalised
-      float* prow = p.pre_out + ((size_t)tokr[rg] * p.hq + h) * D;
+      // the partial of gathered row tokr over this key range: fp32,
+      // normalised; a row that saw no key here gives o = 0, lse = -inf
+      const size_t prow_i = ((size_t)ksplit * p.pre_rows + tokr[rg]) * p.hq + h;
+      const float cinv = lt > 0.f ? inv : 0.f;
+      float* prow = p.pre_out + prow_i * D;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const f32x16& a = acc[rg][db];
           *reinterpret_cast<float4*>(prow + 32 * db + 8 * i + 4 * kg) =
-              make_float4(a[4 * i] * inv, a[4 * i + 1] * inv, a[4 * i + 2] * inv,
-                          a[4 * i + 3] * inv);
+              make_float4(a[4 * i] * cinv, a[4 * i + 1] * cinv, a[4 * i + 2] * cinv,
+                          a[4 * i + 3] * cinv);
         }
-      if (kg == 0) p.pre_lse[(size_t)tokr[rg] * p.hq + h] = (m[rg] + fast_log2(lt)) * kLn2;
+      if (kg == 0) p.pre_lse[prow_i] = lt > 0.f ? (m[rg] + fast_log2(lt)) * kLn2 : -INFINITY;
       continue;
     }
     const int t = q0 + tokr[rg];
@@ -670,6 +688,9 @@ void launch_cascade_dg(const AttnArgs& a, hipStream_t stream) {
   p.vpos = a.vpos;
   p.pre_blocks = a.pre_blocks;
   p.pre_tokens = 16 * a.num_pre_blocks;
+  p.pre_splits = a.casc_ksplits;
+  p.pre_chunk = a.casc_kchunk;
+  p.pre_rows = a.casc_rows_max;
   p.pre_out = a.pre_out;
   p.pre_lse = a.pre_lse;
   trace_before(K_CASCADE_SETUP, stream);
@@ -680,8 +701,8 @@ void launch_cascade_dg(const AttnArgs& a, hipStream_t stream) {
   trace_after(stream);
   const int tiles = (a.casc_rows_max + TQ - 1) / TQ;
   trace_before(K_CASCADE_PREFIX, stream);
-  hipLaunchKernelGGL((prefill_kernel<D, G, NW, RG, BK, false, true>), dim3(tiles * a.hkv),
-                     dim3(64 * NW), 0, stream, p);
+  hipLaunchKernelGGL((prefill_kernel<D, G, NW, RG, BK, false, true>),
+                     dim3(tiles * a.casc_ksplits * a.hkv), dim3(64 * NW), 0, stream, p);
   trace_after(stream);
 }
 

@@ -128,3 +128,40 @@ def test_cascade_full_mixed_step_sampled():
     assert float(np.abs(o - ref).max()) <= 2e-2
     assert float(np.linalg.norm(o - ref) / np.linalg.norm(ref)) <= 2e-2
     assert float(np.abs(lse.cpu().double().numpy()[rows] - rl[o_rows]).max()) <= 1e-3
+
+
+@pytest.mark.parametrize("splits", [0, 1, 5])
+def test_cascade_long_shared_prefix(splits):
+    # 16 decodes sharing a 2048-token prefix, private suffixes of 10..300 tokens
+    from workloads import shared_prefix_step
+    step = shared_prefix_step(16, 2048, 10, 300, 7, num_q_heads=16, num_kv_heads=4)
+    prefix = list(step.info["shared_blocks"])
+    out, lse = run_cascade(step, list(range(16)), prefix, num_splits=splits)
+    ro, rl = oracle_plain(step)
+    check(out, lse, ro, rl, np.arange(16), f"long shared prefix S={splits}")
+
+
+def test_cascade_key_ranges_with_short_sharers():
+    # a 2048-token prefix cut into many key ranges; two sharers end early
+    # inside it (100 and 700 tokens), so they see no key in most ranges
+    rng = np.random.default_rng(12)
+    P = 128
+    nb = 400
+    perm = [int(x) for x in rng.permutation(nb)]
+    prefix = perm[:P]
+    k = P
+    reqs = []
+    for prior in (2048 + 40, 2048 + 333, 100, 700, 2048 + 7, 2048 + 250):
+        need = -(-(prior + 1) // 16)
+        if need <= P:
+            table = prefix[:need]
+        else:
+            table = prefix + perm[k:k + need - P]
+            k += need - P
+        reqs.append(Request(prior, 1, table))
+    step = build_step("short-sharers", reqs, dtype="bf16", num_q_heads=16, num_kv_heads=4,
+                      head_dim=128, num_blocks=nb, seed=12)
+    for splits in (1, 4):
+        out, lse = run_cascade(step, list(range(6)), prefix, num_splits=splits)
+        ro, rl = oracle_plain(step)
+        check(out, lse, ro, rl, np.arange(6), f"short sharers S={splits}")

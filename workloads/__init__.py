@@ -17,4 +17,5 @@ from .gen import (  # noqa: F401
     extract_requests,
     unique_block_count,
     fp8_cache,
+    shared_prefix_step,
 )

@@ -203,6 +203,34 @@ def _draw_values(step: StepInputs, requests, seed, device, fill) -> None:
         step.value[pad] = fv
 
 
+def shared_prefix_step(num_requests: int, prefix_tokens: int, suffix_lo: int, suffix_hi: int,
+                       seed: int, *, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                       dtype="bf16", device="cpu", fill="nan", with_values=True) -> StepInputs:
+    """Decode requests that all share one prefix of ``prefix_tokens`` tokens
+    (a multiple of 16; its blocks appear at the head of every table) followed
+    by a private suffix of U[suffix_lo, suffix_hi] tokens; one new token each.
+    Placement: numpy ``default_rng(seed)``; block ids a permutation of the pool
+    (prefix blocks first).  info["shared_blocks"] lists the prefix blocks."""
+    assert prefix_tokens % BLOCK == 0
+    rng = np.random.default_rng(seed)
+    P = prefix_tokens // BLOCK
+    suffix = rng.integers(suffix_lo, suffix_hi + 1, size=num_requests)
+    need = [-(-(prefix_tokens + int(x) + 1) // BLOCK) - P for x in suffix]
+    nb = P + sum(need)
+    perm = rng.permutation(nb)
+    prefix = [int(x) for x in perm[:P]]
+    reqs, k = [], P
+    for i in range(num_requests):
+        reqs.append(Request(prefix_tokens + int(suffix[i]), 1,
+                            prefix + [int(x) for x in perm[k:k + need[i]]]))
+        k += need[i]
+    return build_step(f"shared-prefix {num_requests} x {prefix_tokens}", reqs, dtype=dtype,
+                      num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
+                      num_blocks=nb, seed=seed, device=device, fill=fill,
+                      info={"shared_blocks": prefix, "num_sharers": num_requests},
+                      with_values=with_values)
+
+
 def fp8_cache(step: StepInputs, seed: int, device="cpu", fill="nan") -> StepInputs:
     """The same step over an E4M3 cache: per-KV-head scales and pools of
     codes drawn directly (no quantisation here).
