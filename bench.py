@@ -65,6 +65,11 @@ def parse_args():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--skip-main", action="store_true",
+                    help="profiling aid: run only --sections and print them (no headline line)")
+    ap.add_argument("--sections", default="sweep,extra,fp8,rope,shared,tiny,achievable",
+                    help="comma list of the reports after the headline (profiling runs pick "
+                         "a subset): sweep, extra, fp8, rope, shared, tiny, achievable")
     return ap.parse_args()
 
 
@@ -519,11 +524,15 @@ def bench_fp8(args, log):
         if name in kt and cfg != 4:
             kb, _ = decode_kernel_bytes(step)
             gbs = kb / (kt[name]["avg_us"] * 1e-6) / 1e9
-            rec["decode_kernel"] = {"bytes": kb, "GBps": gbs, "frac_hbm": gbs / PEAK_HBM_GBS}
+            rec["decode_kernel"] = {"bytes": kb, "GBps": gbs, "frac_hbm": gbs / PEAK_HBM_GBS,
+                                    "traffic": measured_traffic(PROFILE_NAMES[cfg] + "_fp8",
+                                                                "decode")}
         if "prefill_mfma" in kt:
             tf = wm["prefill_flops"] / (kt["prefill_mfma"]["avg_us"] * 1e-6) / 1e12
             rec["prefill_kernel"] = {"flops": wm["prefill_flops"], "TFLOPps": tf,
-                                     "frac_mfma": tf / PEAK_BF16_TFLOPS}
+                                     "frac_mfma": tf / PEAK_BF16_TFLOPS,
+                                     "traffic": measured_traffic(PROFILE_NAMES[cfg] + "_fp8",
+                                                                 "prefill_mfma")}
         log(f"fp8 config{cfg}: {json.dumps(rec)}")
         out.append(rec)
         del runners, base, step
@@ -748,6 +757,19 @@ def main():
         torch.cuda.synchronize()
         log("copy calibration: 3 copies of 1073741824 bytes")
         del src, dst
+    if args.skip_main:
+        sec = set(x.strip() for x in args.sections.split(",") if x.strip())
+        part = {}
+        if "fp8" in sec:
+            part["fp8_kv_cache"] = bench_fp8(args, log)
+        if "rope" in sec:
+            part["rope_kv_write"] = bench_rope(args, log)
+        if "shared" in sec:
+            part["shared_prefix"] = bench_shared_prefix(args, log)
+        if "extra" in sec:
+            part["extra_workloads"] = [bench_extra(c, args, log) for c in (3, 4, 5)]
+        print(json.dumps(part, default=str), flush=True)
+        return
     log("main workload: " + WORKLOAD_NAMES[2])
     res = bench_main(args, log)
     wm = res["work"]
@@ -763,15 +785,23 @@ def main():
     rope = None
     shared = None
     if not args.only_main:
-        sweep = split_sweep(args, log)
-        for cfg in (3, 4, 5):
-            log("extra workload: " + WORKLOAD_NAMES[cfg])
-            extras.append(bench_extra(cfg, args, log))
-        fp8 = bench_fp8(args, log)
-        rope = bench_rope(args, log)
-        shared = bench_shared_prefix(args, log)
-        cfg1 = bench_config1(args, log)
-        ach = achievable(log)
+        sec = set(x.strip() for x in args.sections.split(",") if x.strip())
+        if "sweep" in sec:
+            sweep = split_sweep(args, log)
+        if "extra" in sec:
+            for cfg in (3, 4, 5):
+                log("extra workload: " + WORKLOAD_NAMES[cfg])
+                extras.append(bench_extra(cfg, args, log))
+        if "fp8" in sec:
+            fp8 = bench_fp8(args, log)
+        if "rope" in sec:
+            rope = bench_rope(args, log)
+        if "shared" in sec:
+            shared = bench_shared_prefix(args, log)
+        if "tiny" in sec:
+            cfg1 = bench_config1(args, log)
+        if "achievable" in sec:
+            ach = achievable(log)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args, log)
