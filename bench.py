@@ -5,7 +5,9 @@ A step is the whole hot path over one batch of synthetic input: the KV write
 of the step's new tokens through slot_mapping, then causal attention of
 every scheduled row through the block tables (decode kernel with split-KV
 partials merged by the last split to finish, and/or the matrix-core prefill
-kernel).
+kernel).  The headline decode step goes through pa_decode_step, where the
+decode launch performs the KV write itself; the two-call time is reported
+beside it.
 
 Headline workload: long-context single decode (1 request, 1 new token,
 context 32768, 32 query / 8 KV heads, head_dim 128, bf16, 16-token blocks
@@ -169,7 +171,7 @@ class StepRunner:
     """Enqueues one step (KV write + attention) on the current stream, calling
     the C ABI directly with pre-marshalled arguments."""
 
-    def __init__(self, step, dev, num_splits, pools=None, cascade=None):
+    def __init__(self, step, dev, num_splits, pools=None, cascade=None, fused=False):
         import ctypes
 
         import torch
@@ -222,6 +224,12 @@ class StepRunner:
                               step.num_blocks, ctypes.c_float(step.scale), self.splits,
                               P(g["out"]), P(g["lse"]), P(g["ws"]), ws, code]
             self.kv_fn, self.attn_fn = self.lib.pa_kv_write, self.lib.pa_attention_fwd
+        self.fused = fused and not self.fp8 and cascade is None
+        if self.fused:
+            # one call: KV write + attention (pa_decode_step)
+            # (key, value, caches, slots) + attention's arguments without its caches
+            self.step_args = ([P(g["key"]), P(g["value"]), P(g["kc"]), P(g["vc"]), P(g["sm"])] +
+                              self.attn_args[:1] + self.attn_args[3:])
         if cascade is not None:
             # shared-prefix attention: (sharer request ids, prefix block ids)
             sh, pb = cascade
@@ -241,6 +249,11 @@ class StepRunner:
 
     def __call__(self):
         s = self.ctypes.c_void_p(self.torch.cuda.current_stream().cuda_stream)
+        if self.fused:
+            st = self.lib.pa_decode_step(*self.step_args, s)
+            if st != 0:
+                raise RuntimeError(f"decode step failed: {st}")
+            return
         st = self.kv_fn(*self.kv_args, s)
         if st != 0:
             raise RuntimeError(f"KV write failed: {st}")
@@ -316,10 +329,16 @@ def time_steps(runners, steps, warmup, use_graph, log, per_graph=1):
 
     run(warmup)
     torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    ev0.record()
     run(steps)
+    ev1.record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    # HIP events on the stream the steps run on, bracketing the timed region
+    time_steps.last_event_ms = ev0.elapsed_time(ev1) / steps
     return (t1 - t0) * 1e3 / steps, mode
 
 
@@ -394,28 +413,39 @@ def bench_main(args, log):
     from workloads import config_step
     dev = torch.device("cuda:0")
     step = config_step(2, device=dev, fill="zero")
-    base = StepRunner(step, dev, 0)
+    # the step through pa_decode_step: KV write fused into the decode launch
+    base = StepRunner(step, dev, 0, fused=True)
     runners = [base]
     for _ in range(args.replicas - 1):
         kc = step.k_pool.to(dev).clone()
         vc = step.v_pool.to(dev).clone()
-        runners.append(StepRunner(step, dev, base.splits, pools=(kc, vc)))
+        runners.append(StepRunner(step, dev, base.splits, pools=(kc, vc), fused=True))
     wm = work_model(step)
     # one graph holds one step on each replica in turn (R steps per replay)
     ms, mode = time_steps(runners, args.steps, args.warmup, not args.eager, log,
                           per_graph=len(runners))
-    eager_ms = None
+    ev_ms = time_steps.last_event_ms   # one decode launch per step
+    eager_ms = sep_ms = None
     if not args.eager:
         # the same steps launched one call at a time from the host (no graph)
         eager_ms, _ = time_steps(runners, min(args.steps, 200), args.warmup, False, log)
+        # and as two calls (pa_kv_write, pa_attention_fwd), from graphs
+        sep = [StepRunner(step, dev, base.splits, pools=(r.g["kc"], r.g["vc"]))
+               for r in runners]
+        sep_ms, _ = time_steps(sep, args.steps, args.warmup, True, log, per_graph=len(sep))
+        del sep
     kt = kernel_times(runners, min(args.steps, 200), log)
     kbytes, ktoks = decode_kernel_bytes(step)
     dom = "decode_split_partial" if base.splits > 1 else "decode"
-    dur_us = kt[dom]["avg_us"]
+    # each step is exactly one launch of the dominant kernel (the KV write is
+    # fused into it), so its average launch duration is the event-timed
+    # region over the steps; the per-launch events of kernel_times (which
+    # include launch gaps) are reported in kernels_us
+    dur_us = ev_ms * 1e3
     achieved = kbytes / (dur_us * 1e-6) / 1e9
     res = {
         "step": step, "ms": ms, "mode": mode, "splits": base.splits, "work": wm,
-        "eager_ms": eager_ms,
+        "eager_ms": eager_ms, "sep_ms": sep_ms,
         "kernels": kt,
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
@@ -423,7 +453,8 @@ def bench_main(args, log):
                      "bytes_per_launch": kbytes, "units_per_launch": ktoks,
                      "unit_def": "one context token of one request: K and V for 8 KV heads "
                                  "x 128 dims x 2 B = 4096 B (plus Q and table reads)",
-                     "avg_launch_us": dur_us},
+                     "avg_launch_us": dur_us,
+                     "timing": "HIP events around the timed graph replays, / launches"},
     }
     del runners, base
     torch.cuda.empty_cache()
@@ -444,7 +475,7 @@ def split_sweep(args, log, splits=(1, 8, 16, 32, 64, 128)):
     wm = work_model(step)
     out = []
     for S in splits:
-        runners = [StepRunner(step, dev, S, pools=pl) for pl in pools]
+        runners = [StepRunner(step, dev, S, pools=pl, fused=True) for pl in pools]
         n = args.replicas * (4 if S == 1 else 10)
         ms, _ = time_steps(runners, n, args.replicas, not args.eager, log,
                            per_graph=len(runners))
@@ -830,7 +861,9 @@ def main():
                        for k, v in res["kernels"].items()},
         "launch_path": {"graph_us_per_step": round(ms * 1e3, 2),
                         "eager_us_per_step": None if res["eager_ms"] is None
-                        else round(res["eager_ms"] * 1e3, 2)},
+                        else round(res["eager_ms"] * 1e3, 2),
+                        "two_calls_graph_us_per_step": None if res["sep_ms"] is None
+                        else round(res["sep_ms"] * 1e3, 2)},
         "split_sweep": sweep,
         "extra_workloads": extras,
         "fp8_kv_cache": fp8,

@@ -183,6 +183,30 @@ pa_status pa_rope_kv_write(void* query, const void* key, const void* value,
                            pa_dtype dtype, void* stream);
 
 /*
+ * pa_decode_step -- pa_kv_write followed by pa_attention_fwd, as one call
+ * (arguments as those two; key/value/slot_mapping for the write, the rest
+ * for attention).  When every request has at most 16 / group new tokens
+ * (max_query_len) and dtype is bf16, the decode kernel performs the write
+ * itself, in one launch: the work-group whose block range holds a request's
+ * new token writes that token's K/V for its KV head before it reads any
+ * block, and one work-group writes tokens after the last request's rows.
+ * This relies on the definition of the flat batch ("Model execution",
+ * "Flattening a step"): the slot of position p of request b is
+ * block_tables[b][p / 16] * 16 + p % 16, so no other work-group reads a
+ * new token's entry.  Otherwise (prefill rows, fp32) the two calls run in
+ * order.  Results (pool bytes, out, lse) are those of the two calls.
+ */
+pa_status pa_decode_step(const void* key, const void* value, void* key_cache, void* value_cache,
+                         const int64_t* slot_mapping, const void* query,
+                         const int32_t* query_start_loc, const int32_t* seq_lens,
+                         const int32_t* block_tables, int32_t num_seqs, int32_t num_tokens,
+                         int32_t max_query_len, int32_t max_seq_len, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         int32_t block_table_stride, int64_t num_blocks, float scale,
+                         int32_t num_splits, void* out, float* lse, void* workspace,
+                         size_t workspace_bytes, pa_dtype dtype, void* stream);
+
+/*
  * pa_attention_fwd_cascade -- pa_attention_fwd (bf16) with a shared prefix
  * read once.  Block tables may point several requests at the same physical
  * blocks ("Model execution", "Flattening a step"; prefix caching in "Anatomy

@@ -23,6 +23,7 @@ from ._lib import LIB, PA_BF16, PA_F32, PA_BLOCK_SIZE, PA_MAX_SPLITS  # noqa: F4
 __all__ = [
     "PaError", "kv_write", "attention", "split_combine", "workspace_size",
     "kv_write_fp8", "attention_fp8", "alloc_cache_fp8", "rope_kv_write", "attention_cascade",
+    "decode_step",
     "choose_num_splits", "capture_size", "alloc_cache", "workspace", "trace_begin", "trace_end",
     "trace_read",
     "kernel_name", "version",
@@ -182,6 +183,54 @@ def attention_fp8(query, key_cache, value_cache, k_scale, v_scale, query_start_l
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _stream(stream))
     _check(st, "pa_attention_fwd_fp8")
+    return out, lse
+
+
+def decode_step(key, value, key_cache, value_cache, slot_mapping, query, query_start_loc,
+                seq_lens, block_tables, max_query_len: int, max_seq_len: int, scale: float,
+                num_splits: int = 0, out=None, lse=None, want_lse: bool = True, workspace=None,
+                stream=None):
+    """kv_write then attention as one call (one launch for bf16 decode steps).
+    Returns (out, lse)."""
+    nt, hq, d = query.shape
+    nb, hkv = key_cache.shape[0], key_cache.shape[1]
+    if key.shape != (nt, hkv, d) or value.shape != key.shape:
+        raise ValueError("key / value must be [num_tokens, num_kv_heads, head_dim]")
+    if len({t.dtype for t in (query, key, value, key_cache, value_cache)}) != 1:
+        raise ValueError("query, key, value and the cache must share a dtype")
+    if tuple(key_cache.shape) != (nb, hkv, PA_BLOCK_SIZE, d) or \
+            tuple(value_cache.shape) != (nb, hkv, d, PA_BLOCK_SIZE):
+        raise ValueError("cache shapes must be [NB, Hkv, 16, d] and [NB, Hkv, d, 16]")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (nt,):
+        raise ValueError("slot_mapping must be int64 [num_tokens]")
+    for name, t in (("query_start_loc", query_start_loc), ("seq_lens", seq_lens),
+                    ("block_tables", block_tables)):
+        if t.dtype != torch.int32:
+            raise ValueError(f"{name} must be int32")
+    ns = seq_lens.shape[0]
+    if query_start_loc.shape != (ns + 1,) or block_tables.dim() != 2 or \
+            block_tables.shape[0] != ns:
+        raise ValueError("metadata shapes disagree")
+    splits = num_splits
+    if splits == 0:
+        splits = choose_num_splits(ns, max_query_len, max_seq_len, hq, hkv)
+    if out is None:
+        out = torch.empty_like(query)
+    if lse is None and want_lse:
+        lse = torch.empty(nt, hq, dtype=torch.float32, device=query.device)
+    need = workspace_size(ns, nt, hq, d, splits)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=query.device)
+    st = LIB.pa_decode_step(
+        _dev(key, "key"), _dev(value, "value"), _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), _dev(slot_mapping, "slot_mapping"),
+        _dev(query, "query"), _dev(query_start_loc, "query_start_loc"),
+        _dev(seq_lens, "seq_lens"), _dev(block_tables, "block_tables"), ns, nt,
+        int(max_query_len), int(max_seq_len), hq, hkv, d, PA_BLOCK_SIZE, block_tables.shape[1],
+        nb, float(scale), splits, _dev(out, "out"), None if lse is None else _dev(lse, "lse"),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _dtype_code(query), _stream(stream))
+    _check(st, "pa_decode_step")
     return out, lse
 
 

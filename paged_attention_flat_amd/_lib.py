@@ -36,6 +36,9 @@ PROTOTYPES = {
     "pa_attention_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                 _i32, _i32, _i32, _i32, _i64, _f32, _i32, _vp, _vp, _vp, _sz,
                                 _i32, _vp]),
+    "pa_decode_step": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                              _i32, _i32, _i32, _i32, _i32, _i32, _i64, _f32, _i32, _vp, _vp,
+                              _vp, _sz, _i32, _vp]),
     "pa_attention_fwd_cascade": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                         _i32, _i32, _i32, _i32, _i32, _i64, _f32, _i32, _vp,
                                         _i32, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),

@@ -68,6 +68,12 @@ struct DecodeParams {
   int32_t pre_blocks;
   int32_t pre_splits;        // prefix partials per row (key ranges)
   int32_t pre_rows;
+  // fused KV write (nullable): the step's new K/V rows [nt][hkv][D] and their
+  // slots; the work-group whose block range holds a new token writes it
+  const uint16_t* knew;
+  const uint16_t* vnew;
+  const int64_t* slots;
+  int64_t num_slots;
 };
 
 // Two launch shapes.  Many work units: 8 waves per work-group, one pair in
@@ -151,6 +157,27 @@ __global__ __launch_bounds__(64 * NW, (PIPE == 2 && NW < 8 ? 8 / NW : 1)) void d
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, kg = lane >> 4;
 
+  if constexpr (!F8) {
+    if (p.knew != nullptr && blockIdx.x == 0 && blockIdx.y == 0) {
+      // fused KV write of tokens after the last request's rows (no row reads
+      // them; written for the pool's sake, every KV head)
+      const int t_end = p.qsl[p.num_seqs];
+      uint16_t* kc = const_cast<uint16_t*>(static_cast<const uint16_t*>(p.kc));
+      uint16_t* vc = const_cast<uint16_t*>(static_cast<const uint16_t*>(p.vc));
+      for (int t = t_end; t < p.nt; ++t) {
+        const int64_t sl = p.slots[t];
+        if (sl < 0 || sl >= p.num_slots) continue;
+        const size_t cb = (size_t)(sl >> 4), off = (size_t)(sl & 15);
+        for (int e = threadIdx.x; e < p.hkv * D; e += 64 * NW) {
+          const int hh = e / D, dd = e - hh * D;
+          const size_t head = (cb * p.hkv + hh) * 16 * D;
+          const size_t src = ((size_t)t * p.hkv + hh) * D + dd;
+          kc[head + off * D + dd] = p.knew[src];
+          vc[head + (size_t)dd * 16 + off] = p.vnew[src];
+        }
+      }
+    }
+  }
   int b = rank;
   if (p.order != nullptr) {
     if (rank >= p.order[0]) return;
@@ -177,8 +204,35 @@ __global__ __launch_bounds__(64 * NW, (PIPE == 2 && NW < 8 ? 8 / NW : 1)) void d
   const int blk_hi = min(nblocks, blk_lo + p.split_blocks);
 
   const int qi = col / G, g = col - (col / G) * G;
-  const bool col_valid = qi < q_len;
   const int qpos = ctx + min(qi, q_len - 1);
+  const bool col_valid = qi < q_len;
+
+  if constexpr (!F8) {
+    if (p.knew != nullptr) {
+      // Fused KV write: this request's new tokens whose blocks fall in this
+      // split's range are written here (head kvh) before any K/V is read;
+      // the slot of position p is table[p / 16] * 16 + p % 16 by definition,
+      // so no other work-group reads these entries.
+      bool wrote = false;
+      for (int i = 0; i < q_len; ++i) {
+        const int blk = (ctx + i) >> 4;
+        if (blk < blk_lo || blk >= blk_hi) continue;
+        const int64_t sl = p.slots[q0 + i];
+        if (sl < 0 || sl >= p.num_slots) continue;
+        wrote = true;
+        const size_t src = ((size_t)(q0 + i) * p.hkv + kvh) * D;
+        const size_t cb = (size_t)(sl >> 4), off = (size_t)(sl & 15);
+        const size_t head = (cb * p.hkv + kvh) * 16 * D;
+        uint16_t* kc = const_cast<uint16_t*>(static_cast<const uint16_t*>(p.kc));
+        uint16_t* vc = const_cast<uint16_t*>(static_cast<const uint16_t*>(p.vc));
+        for (int e = threadIdx.x; e < D / 8; e += 64 * NW)
+          *reinterpret_cast<uint4*>(kc + head + off * D + 8 * e) =
+              *reinterpret_cast<const uint4*>(p.knew + src + 8 * e);
+        for (int e = threadIdx.x; e < D; e += 64 * NW) vc[head + (size_t)e * 16 + off] = p.vnew[src + e];
+      }
+      if (wrote) __syncthreads();  // stores complete before any wave reads the block
+    }
+  }
 
   // Q as the B operand: lane (col, kg) holds d = 32*st + 8*kg .. +8
   bf16x8 qf[KSTEPS];
@@ -607,6 +661,10 @@ void launch_dg(const AttnArgs& a, hipStream_t stream) {
   p.pre_blocks = a.num_pre_blocks;
   p.pre_splits = a.casc_ksplits;
   p.pre_rows = a.casc_rows_max;
+  p.knew = (const uint16_t*)a.knew;
+  p.vnew = (const uint16_t*)a.vnew;
+  p.slots = a.slots;
+  p.num_slots = a.num_blocks * 16;
   if (a.decode_order != nullptr) {
     int shift = 0;
     const int max_blocks = (a.max_seq_len + 15) / 16;

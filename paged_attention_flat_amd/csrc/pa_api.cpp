@@ -336,7 +336,9 @@ pa_status attention_impl(const void* query, const void* key_cache, const void* v
                          int32_t num_splits, void* out, float* lse, void* workspace,
                          size_t workspace_bytes, pa_dtype dtype, bool cache_fp8, void* stream,
                          const int32_t* sharers = nullptr, int32_t num_sharers = 0,
-                         const int32_t* pre_blocks = nullptr, int32_t num_pre_blocks = 0) {
+                         const int32_t* pre_blocks = nullptr, int32_t num_pre_blocks = 0,
+                         const void* knew = nullptr, const void* vnew = nullptr,
+                         const int64_t* slots = nullptr) {
   if (num_seqs < 0 || num_tokens < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
       num_blocks <= 0 || num_splits < 0 || num_splits > PA_MAX_SPLITS || !std::isfinite(scale) ||
       !(scale > 0.f))
@@ -425,6 +427,10 @@ pa_status attention_impl(const void* query, const void* key_cache, const void* v
   a.num_sharers = cascade ? num_sharers : 0;
   a.pre_blocks = pre_blocks;
   a.num_pre_blocks = cascade ? num_pre_blocks : 0;
+  a.knew = knew;
+  a.vnew = vnew;
+  a.slots = slots;
+  a.num_blocks = num_blocks;
   a.casc_rows_max = (int32_t)casc_rows;
   a.casc_ksplits = ksplits;
   a.casc_kchunk = kchunk;
@@ -510,6 +516,40 @@ pa_status pa_attention_fwd_cascade(const void* query, const void* key_cache,
                         num_blocks, scale, num_splits, out, lse, workspace, workspace_bytes,
                         PA_BF16, false, stream, sharers, num_sharers, prefix_blocks,
                         num_prefix_blocks);
+}
+
+pa_status pa_decode_step(const void* key, const void* value, void* key_cache, void* value_cache,
+                         const int64_t* slot_mapping, const void* query,
+                         const int32_t* query_start_loc, const int32_t* seq_lens,
+                         const int32_t* block_tables, int32_t num_seqs, int32_t num_tokens,
+                         int32_t max_query_len, int32_t max_seq_len, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         int32_t block_table_stride, int64_t num_blocks, float scale,
+                         int32_t num_splits, void* out, float* lse, void* workspace,
+                         size_t workspace_bytes, pa_dtype dtype, void* stream) {
+  if (num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return PA_ERR_INVALID;
+  const int32_t group = num_q_heads / num_kv_heads;
+  const bool fuse = dtype == PA_BF16 && is_pow2_group(group) && num_seqs > 0 &&
+                    num_tokens > 0 && max_query_len >= 1 && max_query_len <= decode_max_q(group);
+  if (!fuse) {
+    // the two calls in order (same results, two launches)
+    pa_status st = pa_kv_write(key, value, key_cache, value_cache, slot_mapping, num_tokens,
+                               num_kv_heads, head_dim, block_size, num_blocks, dtype, stream);
+    if (st != PA_OK) return st;
+    return pa_attention_fwd(query, key_cache, value_cache, query_start_loc, seq_lens,
+                            block_tables, num_seqs, num_tokens, max_query_len, max_seq_len,
+                            num_q_heads, num_kv_heads, head_dim, block_size, block_table_stride,
+                            num_blocks, scale, num_splits, out, lse, workspace, workspace_bytes,
+                            dtype, stream);
+  }
+  if (!key || !value || !slot_mapping) return PA_ERR_NULL;
+  if (!aligned16(key) || !aligned16(value)) return PA_ERR_INVALID;
+  return attention_impl(query, key_cache, value_cache, nullptr, nullptr, query_start_loc,
+                        seq_lens, block_tables, num_seqs, num_tokens, max_query_len, max_seq_len,
+                        num_q_heads, num_kv_heads, head_dim, block_size, block_table_stride,
+                        num_blocks, scale, num_splits, out, lse, workspace, workspace_bytes,
+                        dtype, false, stream, nullptr, 0, nullptr, 0, key, value, slot_mapping);
 }
 
 pa_status pa_attention_fwd_fp8(const void* query, const void* key_cache,

@@ -86,6 +86,11 @@ struct AttnArgs {
   int32_t* casc_count;        // [1]
   float* pre_out;             // [casc_ksplits][casc_rows_max][hq][d]
   float* pre_lse;             // [casc_ksplits][casc_rows_max][hq]
+  // fused decode step (bf16): new K/V and slots written by the decode kernel
+  const void* knew;           // nullable
+  const void* vnew;
+  const int64_t* slots;
+  int64_t num_blocks;
 };
 
 // Largest number of new tokens per request that the decode kernel packs.
