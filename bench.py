@@ -224,12 +224,20 @@ class StepRunner:
                               step.num_blocks, ctypes.c_float(step.scale), self.splits,
                               P(g["out"]), P(g["lse"]), P(g["ws"]), ws, code]
             self.kv_fn, self.attn_fn = self.lib.pa_kv_write, self.lib.pa_attention_fwd
-        self.fused = fused and not self.fp8 and cascade is None
-        if self.fused:
-            # one call: KV write + attention (pa_decode_step)
+        self.fused = fused and cascade is None
+        if self.fused and self.fp8:
+            # one call: quantising KV write + attention (pa_decode_step_fp8):
+            # (key, value, caches, slots, scales, query) + attention's metadata on
+            self.step_args = ([P(g["key"]), P(g["value"]), P(g["kc"]), P(g["vc"]), P(g["sm"]),
+                               P(g["ks"]), P(g["vs"]), P(g["query"])] + self.attn_args[5:] +
+                              [code])
+            self.step_fn = self.lib.pa_decode_step_fp8
+        elif self.fused:
+            # one call: KV write + attention (pa_decode_step):
             # (key, value, caches, slots) + attention's arguments without its caches
             self.step_args = ([P(g["key"]), P(g["value"]), P(g["kc"]), P(g["vc"]), P(g["sm"])] +
                               self.attn_args[:1] + self.attn_args[3:])
+            self.step_fn = self.lib.pa_decode_step
         if cascade is not None:
             # shared-prefix attention: (sharer request ids, prefix block ids)
             sh, pb = cascade
@@ -250,7 +258,7 @@ class StepRunner:
     def __call__(self):
         s = self.ctypes.c_void_p(self.torch.cuda.current_stream().cuda_stream)
         if self.fused:
-            st = self.lib.pa_decode_step(*self.step_args, s)
+            st = self.step_fn(*self.step_args, s)
             if st != 0:
                 raise RuntimeError(f"decode step failed: {st}")
             return
@@ -535,11 +543,11 @@ def bench_fp8(args, log):
     for cfg in (2, 3, 4):
         step = fp8_cache(config_step(cfg, device=dev, fill="zero"), cfg, device=dev, fill="zero")
         wm = work_model(step)
-        base = StepRunner(step, dev, 0)
+        base = StepRunner(step, dev, 0, fused=True)
         runners = [base]
         if cfg == 2:
             for _ in range(args.replicas - 1):
-                runners.append(StepRunner(step, dev, base.splits,
+                runners.append(StepRunner(step, dev, base.splits, fused=True,
                                           pools=(step.k_pool.clone(), step.v_pool.clone())))
             n = args.steps
         else:

@@ -300,6 +300,24 @@ pa_status pa_attention_fwd_fp8(const void* query, const void* key_cache,
                                void* stream);
 
 /*
+ * pa_decode_step_fp8 -- pa_kv_write_fp8 followed by pa_attention_fwd_fp8 as
+ * one call, fused into the decode launch under the conditions of
+ * pa_decode_step (bf16 key / value / query; decode rows only), where the
+ * decode kernel quantises each new token exactly as pa_kv_write_fp8 does.
+ * dtype: of key / value (the query is bf16); PA_F32 runs the two calls.
+ */
+pa_status pa_decode_step_fp8(const void* key, const void* value, void* key_cache,
+                             void* value_cache, const int64_t* slot_mapping,
+                             const float* k_scale, const float* v_scale, const void* query,
+                             const int32_t* query_start_loc, const int32_t* seq_lens,
+                             const int32_t* block_tables, int32_t num_seqs, int32_t num_tokens,
+                             int32_t max_query_len, int32_t max_seq_len, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             int32_t block_table_stride, int64_t num_blocks, float scale,
+                             int32_t num_splits, void* out, float* lse, void* workspace,
+                             size_t workspace_bytes, pa_dtype dtype, void* stream);
+
+/*
  * pa_attention_workspace_init -- zero `workspace_bytes` of a workspace on
  * `stream` with a kernel (no memset node, so it may be captured in a HIP
  * graph).  Needed once for a new workspace whose memory is not already zero.

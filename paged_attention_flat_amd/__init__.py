@@ -23,7 +23,7 @@ from ._lib import LIB, PA_BF16, PA_F32, PA_BLOCK_SIZE, PA_MAX_SPLITS  # noqa: F4
 __all__ = [
     "PaError", "kv_write", "attention", "split_combine", "workspace_size",
     "kv_write_fp8", "attention_fp8", "alloc_cache_fp8", "rope_kv_write", "attention_cascade",
-    "decode_step",
+    "decode_step", "decode_step_fp8",
     "choose_num_splits", "capture_size", "alloc_cache", "workspace", "trace_begin", "trace_end",
     "trace_read",
     "kernel_name", "version",
@@ -231,6 +231,50 @@ def decode_step(key, value, key_cache, value_cache, slot_mapping, query, query_s
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _dtype_code(query), _stream(stream))
     _check(st, "pa_decode_step")
+    return out, lse
+
+
+def decode_step_fp8(key, value, key_cache, value_cache, slot_mapping, k_scale, v_scale, query,
+                    query_start_loc, seq_lens, block_tables, max_query_len: int,
+                    max_seq_len: int, scale: float, num_splits: int = 0, out=None, lse=None,
+                    want_lse: bool = True, workspace=None, stream=None):
+    """kv_write_fp8 then attention_fp8 as one call (one launch for decode
+    steps with bf16 inputs).  Returns (out, lse)."""
+    nt, hq, d = query.shape
+    hkv = key_cache.shape[1]
+    if query.dtype != torch.bfloat16:
+        raise ValueError("an FP8 cache is read with a bf16 query")
+    if key.shape != (nt, hkv, d) or value.shape != key.shape or value.dtype != key.dtype:
+        raise ValueError("key / value must be [num_tokens, num_kv_heads, head_dim], one dtype")
+    nb = _check_fp8_cache(key_cache, value_cache, hkv, d)
+    _check_scales(k_scale, v_scale, hkv)
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (nt,):
+        raise ValueError("slot_mapping must be int64 [num_tokens]")
+    for name, t in (("query_start_loc", query_start_loc), ("seq_lens", seq_lens),
+                    ("block_tables", block_tables)):
+        if t.dtype != torch.int32:
+            raise ValueError(f"{name} must be int32")
+    ns = seq_lens.shape[0]
+    splits = num_splits
+    if splits == 0:
+        splits = choose_num_splits(ns, max_query_len, max_seq_len, hq, hkv)
+    if out is None:
+        out = torch.empty_like(query)
+    if lse is None and want_lse:
+        lse = torch.empty(nt, hq, dtype=torch.float32, device=query.device)
+    need = workspace_size(ns, nt, hq, d, splits)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=query.device)
+    st = LIB.pa_decode_step_fp8(
+        _dev(key, "key"), _dev(value, "value"), _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), _dev(slot_mapping, "slot_mapping"),
+        _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"), _dev(query, "query"),
+        _dev(query_start_loc, "query_start_loc"), _dev(seq_lens, "seq_lens"),
+        _dev(block_tables, "block_tables"), ns, nt, int(max_query_len), int(max_seq_len), hq,
+        hkv, d, PA_BLOCK_SIZE, block_tables.shape[1], nb, float(scale), splits,
+        _dev(out, "out"), None if lse is None else _dev(lse, "lse"), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _dtype_code(key), _stream(stream))
+    _check(st, "pa_decode_step_fp8")
     return out, lse
 
 

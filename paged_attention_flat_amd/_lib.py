@@ -50,6 +50,9 @@ PROTOTYPES = {
     "pa_attention_fwd_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
                                     _i32, _i32, _i32, _i32, _i32, _i32, _i64, _f32, _i32, _vp,
                                     _vp, _vp, _sz, _vp]),
+    "pa_decode_step_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
+                                  _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i64, _f32,
+                                  _i32, _vp, _vp, _vp, _sz, _i32, _vp]),
     "pa_attention_workspace_init": (_i32, [_vp, _sz, _vp]),
     "pa_split_combine": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp]),
     "pa_attention_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),

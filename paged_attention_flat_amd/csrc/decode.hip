@@ -157,21 +157,25 @@ __global__ __launch_bounds__(64 * NW, (PIPE == 2 && NW < 8 ? 8 / NW : 1)) void d
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, kg = lane >> 4;
 
-  if constexpr (!F8) {
-    if (p.knew != nullptr && blockIdx.x == 0 && blockIdx.y == 0) {
-      // fused KV write of tokens after the last request's rows (no row reads
-      // them; written for the pool's sake, every KV head)
-      const int t_end = p.qsl[p.num_seqs];
-      uint16_t* kc = const_cast<uint16_t*>(static_cast<const uint16_t*>(p.kc));
-      uint16_t* vc = const_cast<uint16_t*>(static_cast<const uint16_t*>(p.vc));
-      for (int t = t_end; t < p.nt; ++t) {
-        const int64_t sl = p.slots[t];
-        if (sl < 0 || sl >= p.num_slots) continue;
-        const size_t cb = (size_t)(sl >> 4), off = (size_t)(sl & 15);
-        for (int e = threadIdx.x; e < p.hkv * D; e += 64 * NW) {
-          const int hh = e / D, dd = e - hh * D;
-          const size_t head = (cb * p.hkv + hh) * 16 * D;
-          const size_t src = ((size_t)t * p.hkv + hh) * D + dd;
+  if (p.knew != nullptr && blockIdx.x == 0 && blockIdx.y == 0) {
+    // fused KV write of tokens after the last request's rows (no row reads
+    // them; written for the pool's sake, every KV head)
+    const int t_end = p.qsl[p.num_seqs];
+    CT* kc = const_cast<CT*>(static_cast<const CT*>(p.kc));
+    CT* vc = const_cast<CT*>(static_cast<const CT*>(p.vc));
+    for (int t = t_end; t < p.nt; ++t) {
+      const int64_t sl = p.slots[t];
+      if (sl < 0 || sl >= p.num_slots) continue;
+      const size_t cb = (size_t)(sl >> 4), off = (size_t)(sl & 15);
+      for (int e = threadIdx.x; e < p.hkv * D; e += 64 * NW) {
+        const int hh = e / D, dd = e - hh * D;
+        const size_t head = (cb * p.hkv + hh) * 16 * D;
+        const size_t src = ((size_t)t * p.hkv + hh) * D + dd;
+        if constexpr (F8) {
+          kc[head + off * D + dd] = e4m3_code(bf16_bits_to_f32(p.knew[src]) / p.k_scale[hh]);
+          vc[head + (size_t)dd * 16 + off] =
+              e4m3_code(bf16_bits_to_f32(p.vnew[src]) / p.v_scale[hh]);
+        } else {
           kc[head + off * D + dd] = p.knew[src];
           vc[head + (size_t)dd * 16 + off] = p.vnew[src];
         }
@@ -207,31 +211,50 @@ __global__ __launch_bounds__(64 * NW, (PIPE == 2 && NW < 8 ? 8 / NW : 1)) void d
   const int qpos = ctx + min(qi, q_len - 1);
   const bool col_valid = qi < q_len;
 
-  if constexpr (!F8) {
-    if (p.knew != nullptr) {
-      // Fused KV write: this request's new tokens whose blocks fall in this
-      // split's range are written here (head kvh) before any K/V is read;
-      // the slot of position p is table[p / 16] * 16 + p % 16 by definition,
-      // so no other work-group reads these entries.
-      bool wrote = false;
-      for (int i = 0; i < q_len; ++i) {
-        const int blk = (ctx + i) >> 4;
-        if (blk < blk_lo || blk >= blk_hi) continue;
-        const int64_t sl = p.slots[q0 + i];
-        if (sl < 0 || sl >= p.num_slots) continue;
-        wrote = true;
-        const size_t src = ((size_t)(q0 + i) * p.hkv + kvh) * D;
-        const size_t cb = (size_t)(sl >> 4), off = (size_t)(sl & 15);
-        const size_t head = (cb * p.hkv + kvh) * 16 * D;
-        uint16_t* kc = const_cast<uint16_t*>(static_cast<const uint16_t*>(p.kc));
-        uint16_t* vc = const_cast<uint16_t*>(static_cast<const uint16_t*>(p.vc));
-        for (int e = threadIdx.x; e < D / 8; e += 64 * NW)
-          *reinterpret_cast<uint4*>(kc + head + off * D + 8 * e) =
-              *reinterpret_cast<const uint4*>(p.knew + src + 8 * e);
-        for (int e = threadIdx.x; e < D; e += 64 * NW) vc[head + (size_t)e * 16 + off] = p.vnew[src + e];
+  if (p.knew != nullptr) {
+    // Fused KV write: this request's new tokens whose blocks fall in this
+    // split's range are written here (head kvh) before any K/V is read; the
+    // slot of position p is table[p / 16] * 16 + p % 16 by definition, so no
+    // other work-group reads these entries.  E4M3 cache: quantised exactly
+    // as pa_kv_write_fp8 does.
+    bool wrote = false;
+    CT* kc = const_cast<CT*>(static_cast<const CT*>(p.kc));
+    CT* vc = const_cast<CT*>(static_cast<const CT*>(p.vc));
+    for (int i = 0; i < q_len; ++i) {
+      const int blk = (ctx + i) >> 4;
+      if (blk < blk_lo || blk >= blk_hi) continue;
+      const int64_t sl = p.slots[q0 + i];
+      if (sl < 0 || sl >= p.num_slots) continue;
+      wrote = true;
+      const size_t src = ((size_t)(q0 + i) * p.hkv + kvh) * D;
+      const size_t cb = (size_t)(sl >> 4), off = (size_t)(sl & 15);
+      const size_t head = (cb * p.hkv + kvh) * 16 * D;
+      for (int e = threadIdx.x; e < D / 8; e += 64 * NW) {
+        const uint4 k8 = *reinterpret_cast<const uint4*>(p.knew + src + 8 * e);
+        if constexpr (F8) {
+          const float ks = p.k_scale[kvh];
+          const uint32_t w[4] = {k8.x, k8.y, k8.z, k8.w};
+          float f[8];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            f[2 * j] = __uint_as_float(w[j] << 16) / ks;
+            f[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u) / ks;
+          }
+          *reinterpret_cast<uint2*>(kc + head + off * D + 8 * e) =
+              make_uint2(e4m3_pack4(f[0], f[1], f[2], f[3]), e4m3_pack4(f[4], f[5], f[6], f[7]));
+        } else {
+          *reinterpret_cast<uint4*>(kc + head + off * D + 8 * e) = k8;
+        }
       }
-      if (wrote) __syncthreads();  // stores complete before any wave reads the block
+      for (int e = threadIdx.x; e < D; e += 64 * NW) {
+        if constexpr (F8)
+          vc[head + (size_t)e * 16 + off] =
+              e4m3_code(bf16_bits_to_f32(p.vnew[src + e]) / p.v_scale[kvh]);
+        else
+          vc[head + (size_t)e * 16 + off] = p.vnew[src + e];
+      }
     }
+    if (wrote) __syncthreads();  // stores complete before any wave reads the block
   }
 
   // Q as the B operand: lane (col, kg) holds d = 32*st + 8*kg .. +8

@@ -52,6 +52,21 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint2 v) {
   return bf16x8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
+// E4M3 codes of four values already divided by their scale: clamped to the
+// largest finite magnitude (448; the conversion gives NaN past it), then
+// rounded to nearest even by the hardware conversion.  NaN stays NaN.
+__device__ __forceinline__ float e4m3_sat(float y) {
+  return y > 448.f ? 448.f : (y < -448.f ? -448.f : y);
+}
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_sat(a), e4m3_sat(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_sat(c), e4m3_sat(d), w, true);
+  return (uint32_t)w;
+}
+__device__ __forceinline__ uint8_t e4m3_code(float y) {
+  return (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_sat(y), 0.f, 0, false) & 0xff);
+}
+
 // Cache fragments of eight elements: raw bits as loaded (16 bytes of bf16 or
 // 8 bytes of E4M3 codes) and their bf16 operand form.
 template <bool F8>

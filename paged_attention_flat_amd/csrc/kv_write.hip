@@ -66,12 +66,6 @@ __global__ __launch_bounds__(256) void kv_write_kernel(
 // it) and converted with round-to-nearest-even by the hardware instruction.
 // Each thread quantises 8 consecutive dims of one token (one 8-byte K store);
 // the V codes are staged in LDS and written dim-major like the 16-bit path.
-__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
-  auto sat = [](float y) { return y > 448.f ? 448.f : (y < -448.f ? -448.f : y); };
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(a), sat(b), 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(c), sat(d), w, true);
-  return (uint32_t)w;
-}
 
 template <typename E>
 __device__ __forceinline__ float widen(E v);

@@ -552,6 +552,41 @@ pa_status pa_decode_step(const void* key, const void* value, void* key_cache, vo
                         dtype, false, stream, nullptr, 0, nullptr, 0, key, value, slot_mapping);
 }
 
+pa_status pa_decode_step_fp8(const void* key, const void* value, void* key_cache,
+                             void* value_cache, const int64_t* slot_mapping,
+                             const float* k_scale, const float* v_scale, const void* query,
+                             const int32_t* query_start_loc, const int32_t* seq_lens,
+                             const int32_t* block_tables, int32_t num_seqs, int32_t num_tokens,
+                             int32_t max_query_len, int32_t max_seq_len, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             int32_t block_table_stride, int64_t num_blocks, float scale,
+                             int32_t num_splits, void* out, float* lse, void* workspace,
+                             size_t workspace_bytes, pa_dtype dtype, void* stream) {
+  if (num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return PA_ERR_INVALID;
+  const int32_t group = num_q_heads / num_kv_heads;
+  const bool fuse = dtype == PA_BF16 && is_pow2_group(group) && num_seqs > 0 &&
+                    num_tokens > 0 && max_query_len >= 1 && max_query_len <= decode_max_q(group);
+  if (!fuse) {
+    pa_status st = pa_kv_write_fp8(key, value, key_cache, value_cache, slot_mapping, k_scale,
+                                   v_scale, num_tokens, num_kv_heads, head_dim, block_size,
+                                   num_blocks, dtype, stream);
+    if (st != PA_OK) return st;
+    return pa_attention_fwd_fp8(query, key_cache, value_cache, k_scale, v_scale,
+                                query_start_loc, seq_lens, block_tables, num_seqs, num_tokens,
+                                max_query_len, max_seq_len, num_q_heads, num_kv_heads, head_dim,
+                                block_size, block_table_stride, num_blocks, scale, num_splits,
+                                out, lse, workspace, workspace_bytes, stream);
+  }
+  if (!key || !value || !slot_mapping) return PA_ERR_NULL;
+  if (!aligned16(key) || !aligned16(value)) return PA_ERR_INVALID;
+  return attention_impl(query, key_cache, value_cache, k_scale, v_scale, query_start_loc,
+                        seq_lens, block_tables, num_seqs, num_tokens, max_query_len, max_seq_len,
+                        num_q_heads, num_kv_heads, head_dim, block_size, block_table_stride,
+                        num_blocks, scale, num_splits, out, lse, workspace, workspace_bytes,
+                        PA_BF16, true, stream, nullptr, 0, nullptr, 0, key, value, slot_mapping);
+}
+
 pa_status pa_attention_fwd_fp8(const void* query, const void* key_cache,
                                const void* value_cache, const float* k_scale,
                                const float* v_scale, const int32_t* query_start_loc,

@@ -4,7 +4,8 @@
 sizes and a step replays the graph of the smallest size that holds it, with
 the extra rows padded; "Inside the engine", section "Record the launch stream
 once, replay it as one operation".  A graph here holds one step of the path:
-the KV write of the step's new tokens, then attention for every row.
+the KV write of the step's new tokens and attention for every row, which
+pa_decode_step performs in a single decode launch.
 
 Each ladder size gets its own fixed device buffers (inputs, outputs,
 workspace), allocated and captured on first use.  A step is copied into the
@@ -19,7 +20,8 @@ from __future__ import annotations
 
 import torch
 
-from . import PA_BLOCK_SIZE, attention, capture_size, choose_num_splits, kv_write, workspace
+from . import (PA_BLOCK_SIZE, attention, capture_size, choose_num_splits, decode_step, kv_write,
+               workspace)
 
 
 class DecodeGraphs:
@@ -58,10 +60,11 @@ class DecodeGraphs:
         return b
 
     def _launch(self, b, P: int):
-        kv_write(b["k"], b["v"], self.kc, self.vc, b["slots"])
-        attention(b["q"], self.kc, self.vc, b["qsl"], b["seq_lens"], b["tables"], 1,
-                  self.max_seq_len, self.scale, num_splits=b["splits"], out=b["out"],
-                  lse=b["lse"], want_lse=self.want_lse, workspace=b["ws"])
+        # one launch: the decode kernel performs the KV write (pa_decode_step)
+        decode_step(b["k"], b["v"], self.kc, self.vc, b["slots"], b["q"], b["qsl"],
+                    b["seq_lens"], b["tables"], 1, self.max_seq_len, self.scale,
+                    num_splits=b["splits"], out=b["out"], lse=b["lse"], want_lse=self.want_lse,
+                    workspace=b["ws"])
 
     def _graph(self, P: int):
         g = self.graphs.get(P)

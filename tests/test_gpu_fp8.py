@@ -180,3 +180,56 @@ def test_fp8_full_long_decode():
     assert same_codes(g["k_pool"], kp) and same_codes(g["v_pool"], vp)
     ro, rl = oracle_attn(step, kp, vp)
     check(step, out, lse, ro, rl, what="fp8 full long decode")
+
+
+def run_step_fp8(step, num_splits=0):
+    import paged_attention_flat_amd as pa
+    g = upload(step)
+    out = torch.full_like(g["query"], float("nan"))
+    out, lse = pa.decode_step_fp8(g["key"], g["value"], g["k_pool"], g["v_pool"], g["slots"],
+                                  g["k_scale"], g["v_scale"], g["query"], g["qsl"],
+                                  g["seq_lens"], g["tables"], step.max_query_len,
+                                  step.max_seq_len, step.scale, num_splits=num_splits, out=out)
+    torch.cuda.synchronize()
+    return out, lse, g
+
+
+@pytest.mark.parametrize("cfg,splits", [(2, 0), (2, 5), (3, 0), (5, 0)])
+def test_fp8_decode_step(cfg, splits):
+    # one call: fused quantising write + attention for decode steps (config
+    # 5 has prefill rows: the two calls run instead)
+    step = fp8_cache(config_step(cfg, scale_down=SMALL[cfg]), cfg)
+    out, lse, g = run_step_fp8(step, splits)
+    kp, vp = oracle_write(step)
+    assert same_codes(g["k_pool"], kp) and same_codes(g["v_pool"], vp)
+    ro, rl = oracle_attn(step, kp, vp)
+    check(step, out, lse, ro, rl, what=f"fp8 decode step config{cfg} S={splits}")
+
+
+def test_fp8_decode_step_tokens_across_blocks():
+    rng = np.random.default_rng(6)
+    shapes = [(30, 4), (14, 3), (1000, 2), (0, 4)]
+    need = [-(-(p + n) // 16) for p, n in shapes]
+    nb = sum(need) + 4
+    perm = [int(x) for x in rng.permutation(nb)]
+    tables, k = [], 0
+    for n in need:
+        tables.append(perm[k:k + n])
+        k += n
+    step = build_step("straddle8", [Request(p, n, t) for (p, n), t in zip(shapes, tables)],
+                      dtype="bf16", num_q_heads=16, num_kv_heads=4, head_dim=128,
+                      num_blocks=nb, seed=78, pad_tokens=2)
+    sm = step.slot_mapping.copy()
+    sm[-1] = perm[k] * 16 + 9          # a trailing token written to a free block
+    step.slot_mapping = sm
+    # padded tokens carry NaN poison; this one is written, so give it values
+    # (a NaN's code sign is left open by the write's contract)
+    step.key[-1] = step.key[0]
+    step.value[-1] = step.value[1]
+    step = fp8_cache(step, 78)
+    for splits in (0, 32):
+        out, lse, g = run_step_fp8(step, splits)
+        kp, vp = oracle_write(step)
+        assert same_codes(g["k_pool"], kp) and same_codes(g["v_pool"], vp)
+        ro, rl = oracle_attn(step, kp, vp)
+        check(step, out, lse, ro, rl, what=f"fp8 straddle S={splits}")
