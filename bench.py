@@ -72,6 +72,8 @@ def parse_args():
     ap.add_argument("--sections", default="sweep,extra,fp8,rope,shared,tiny,achievable",
                     help="comma list of the reports after the headline (profiling runs pick "
                          "a subset): sweep, extra, fp8, rope, shared, tiny, achievable")
+    ap.add_argument("--profile", choices=WORKLOADS, default=None,
+                    help="profiling aid: warm up and time one workload, nothing else")
     return ap.parse_args()
 
 
@@ -381,6 +383,100 @@ def kernel_times(runners, steps, log):
     return out
 
 
+class RopeRunner:
+    """One rotary-embedding KV write of the long-prefill step's new tokens
+    followed by the plain KV write of the same tokens (for comparison)."""
+
+    def __init__(self, step, dev):
+        import torch
+
+        import paged_attention_flat_amd as pa
+        self.pa = pa
+        nt, hq, d = step.query.shape
+        qsl = step.query_start_loc
+        pos = torch.empty(nt, dtype=torch.int64)
+        for b in range(step.num_seqs):
+            n = int(qsl[b + 1] - qsl[b])
+            pos[int(qsl[b]):int(qsl[b + 1])] = int(step.seq_lens[b]) - n + torch.arange(n)
+        maxp = int(pos.max()) + 1
+        w = 10000.0 ** (-2.0 * torch.arange(d // 2, dtype=torch.float64) / d)
+        ang = torch.arange(maxp, dtype=torch.float64)[:, None] * w[None, :]
+        self.table = torch.cat([ang.cos(), ang.sin()], dim=1).to(torch.float32).to(dev)
+        self.pos = pos.to(dev)
+        self.sm = torch.as_tensor(step.slot_mapping).to(dev)
+        self.q = step.query.to(dev).clone()
+        self.k, self.v = step.key.to(dev), step.value.to(dev)
+        self.kc, self.vc = step.k_pool.to(dev), step.v_pool.to(dev)
+
+    def __call__(self):
+        self.pa.rope_kv_write(self.q, self.k, self.v, self.kc, self.vc, self.sm, self.pos,
+                              self.table)
+        self.pa.kv_write(self.k, self.v, self.kc, self.vc, self.sm)
+
+
+# every workload a report times, by the name of its profile summary
+WORKLOADS = ("long_context_decode", "large_batch_decode", "long_prefill",
+             "mixed_chunked_prefill_step", "mixed_chunked_prefill_step_shared_prefix",
+             "long_context_decode_fp8", "large_batch_decode_fp8", "long_prefill_fp8",
+             "rope_kv_write", "shared_prefix_plain", "shared_prefix_read_once")
+
+
+def workload_runners(name, dev, args, pools=None):
+    """The runners of one workload exactly as its report times them.
+
+    Returns (step, runners, per_graph, steps, warmup).  The long single decode
+    cycles `args.replicas` pool replicas, one graph holding one step on each;
+    the others run one step per graph.  Every plain step goes through
+    pa_decode_step(_fp8), which performs the KV write inside the decode
+    launch where it can and falls back to the two calls otherwise."""
+    from workloads import config_step, fp8_cache, shared_prefix_step
+    cfg_of = {v: k for k, v in PROFILE_NAMES.items()}
+    base = name[:-4] if name.endswith("_fp8") else name
+    if name.startswith("shared_prefix"):
+        step = shared_prefix_step(256, 16384, 0, 512, 11, device=dev, fill="zero")
+        casc = None
+        if name == "shared_prefix_read_once":
+            casc = (list(range(step.num_seqs)), list(step.info["shared_blocks"]))
+        r = StepRunner(step, dev, 0, pools=pools, cascade=casc, fused=casc is None)
+        return step, [r], 1, args.extra_steps, 3
+    if name == "rope_kv_write":
+        step = config_step(4, device=dev, fill="zero")
+        return step, [RopeRunner(step, dev)], 1, 20, 3
+    casc = base.endswith("_shared_prefix")
+    cfg = cfg_of[base[:-len("_shared_prefix")] if casc else base]
+    step = config_step(cfg, device=dev, fill="zero")
+    if name.endswith("_fp8"):
+        step = fp8_cache(step, cfg, device=dev, fill="zero")
+    if casc:
+        prefix = list(step.info["shared_blocks"])
+        P = len(prefix)
+        bt = step.block_tables
+        sharers = [b for b in range(step.num_seqs) if list(bt[b, :P]) == prefix]
+        r = StepRunner(step, dev, 0, pools=pools, cascade=(sharers, prefix))
+        return step, [r], 1, args.extra_steps, 3
+    first = StepRunner(step, dev, 0, pools=pools, fused=True)
+    if cfg != 2:
+        return step, [first], 1, args.extra_steps, 3
+    runners = [first]
+    for _ in range(args.replicas - 1):
+        runners.append(StepRunner(step, dev, first.splits, fused=True,
+                                  pools=(step.k_pool.to(dev).clone(),
+                                         step.v_pool.to(dev).clone())))
+    return step, runners, len(runners), args.steps, args.warmup
+
+
+def profile_workload(name, args, log):
+    """Warm-up plus the timed steps of one workload, nothing else (one
+    rocprofv3 run per workload keeps every kernel record attributable)."""
+    import torch
+    dev = torch.device("cuda:0")
+    step, runners, per_graph, n, warm = workload_runners(name, dev, args)
+    ms, mode = time_steps(runners, n, warm, not args.eager, log, per_graph=per_graph)
+    log(f"profile {name}: {ms * 1e3:.2f} us/step ({mode})")
+    return {"profile": name, "ms_per_step": ms, "launch": mode, "steps": n, "warmup": warm,
+            "event_ms_per_step": time_steps.last_event_ms}
+
+
 def kernel_sources_sha256():
     """Hash of the kernel sources (and the ABI header) of this tree."""
     import hashlib
@@ -418,20 +514,13 @@ def measured_traffic(workload, kernel):
 def bench_main(args, log):
     import torch
 
-    from workloads import config_step
     dev = torch.device("cuda:0")
-    step = config_step(2, device=dev, fill="zero")
-    # the step through pa_decode_step: KV write fused into the decode launch
-    base = StepRunner(step, dev, 0, fused=True)
-    runners = [base]
-    for _ in range(args.replicas - 1):
-        kc = step.k_pool.to(dev).clone()
-        vc = step.v_pool.to(dev).clone()
-        runners.append(StepRunner(step, dev, base.splits, pools=(kc, vc), fused=True))
-    wm = work_model(step)
+    # the step through pa_decode_step: KV write fused into the decode launch;
     # one graph holds one step on each replica in turn (R steps per replay)
-    ms, mode = time_steps(runners, args.steps, args.warmup, not args.eager, log,
-                          per_graph=len(runners))
+    step, runners, per_graph, n, warm = workload_runners("long_context_decode", dev, args)
+    base = runners[0]
+    wm = work_model(step)
+    ms, mode = time_steps(runners, n, warm, not args.eager, log, per_graph=per_graph)
     ev_ms = time_steps.last_event_ms   # one decode launch per step
     eager_ms = sep_ms = None
     if not args.eager:
@@ -536,27 +625,16 @@ def bench_fp8(args, log):
     scales, codes drawn directly; the KV write quantises the new tokens).
     Algorithmic bytes count one byte per cached element."""
     import torch
-
-    from workloads import config_step, fp8_cache
     dev = torch.device("cuda:0")
     out = []
     for cfg in (2, 3, 4):
-        step = fp8_cache(config_step(cfg, device=dev, fill="zero"), cfg, device=dev, fill="zero")
+        step, runners, per_graph, n, warm = workload_runners(PROFILE_NAMES[cfg] + "_fp8", dev,
+                                                             args)
         wm = work_model(step)
-        base = StepRunner(step, dev, 0, fused=True)
-        runners = [base]
-        if cfg == 2:
-            for _ in range(args.replicas - 1):
-                runners.append(StepRunner(step, dev, base.splits, fused=True,
-                                          pools=(step.k_pool.clone(), step.v_pool.clone())))
-            n = args.steps
-        else:
-            n = args.extra_steps
-        ms, mode = time_steps(runners, n, args.warmup if cfg == 2 else 3, not args.eager, log,
-                              per_graph=len(runners))
+        ms, mode = time_steps(runners, n, warm, not args.eager, log, per_graph=per_graph)
         kt = kernel_times(runners, min(n, 200), log)
         rec = {"workload": WORKLOAD_NAMES[cfg].split(" (")[0] + ", FP8 (E4M3) KV cache",
-               "ms_per_step": ms, "launch": mode, "num_splits": base.splits,
+               "ms_per_step": ms, "launch": mode, "num_splits": runners[0].splits,
                "step_GBps": wm["bytes"] / (ms * 1e-3) / 1e9,
                "kernels_us": {k: round(v["avg_us"], 2) for k, v in kt.items()}}
         name = "decode_split_partial" if "decode_split_partial" in kt else "decode"
@@ -574,7 +652,7 @@ def bench_fp8(args, log):
                                                                  "prefill_mfma")}
         log(f"fp8 config{cfg}: {json.dumps(rec)}")
         out.append(rec)
-        del runners, base, step
+        del runners, step
         torch.cuda.empty_cache()
     return out
 
@@ -587,34 +665,18 @@ def bench_rope(args, log):
     import torch
 
     import paged_attention_flat_amd as pa
-    from workloads import config_step
     dev = torch.device("cuda:0")
-    step = config_step(4, device=dev, fill="zero")
+    step, runners, _, n, warm = workload_runners("rope_kv_write", dev, args)
+    r = runners[0]
     nt, hq, d = step.query.shape
     hkv = step.num_kv_heads
-    qsl = step.query_start_loc
-    pos = torch.empty(nt, dtype=torch.int64)
-    for b in range(step.num_seqs):
-        n = int(qsl[b + 1] - qsl[b])
-        pos[int(qsl[b]):int(qsl[b + 1])] = int(step.seq_lens[b]) - n + torch.arange(n)
-    maxp = int(pos.max()) + 1
-    w = 10000.0 ** (-2.0 * torch.arange(d // 2, dtype=torch.float64) / d)
-    ang = torch.arange(maxp, dtype=torch.float64)[:, None] * w[None, :]
-    table = torch.cat([ang.cos(), ang.sin()], dim=1).to(torch.float32).to(dev)
-    pos = pos.to(dev)
-    sm = torch.as_tensor(step.slot_mapping).to(dev)
-    q = step.query.clone()
-    kc, vc = step.k_pool, step.v_pool
-    n = 20
-    for _ in range(3):
-        pa.rope_kv_write(q, step.key, step.value, kc, vc, sm, pos, table)
-        pa.kv_write(step.key, step.value, kc, vc, sm)
+    for _ in range(warm):
+        r()
     torch.cuda.synchronize()
     pa.trace_begin(4 * n)
     busy_gpu(20.0)
     for _ in range(n):
-        pa.rope_kv_write(q, step.key, step.value, kc, vc, sm, pos, table)
-        pa.kv_write(step.key, step.value, kc, vc, sm)
+        r()
     pa.trace_end()
     torch.cuda.synchronize()
     agg = {}
@@ -633,7 +695,7 @@ def bench_rope(args, log):
            "plain_kv_write_us": round(p_us, 2),
            "plain_kv_write_GBps": round(plain_bytes / (p_us * 1e-6) / 1e9, 1)}
     log(f"rope: {json.dumps(out)}")
-    del step, q
+    del step, runners, r
     torch.cuda.empty_cache()
     return out
 
@@ -643,20 +705,16 @@ def bench_shared_prefix(args, log):
     tokens): plain attention re-reads the 64 MiB prefix per request, the
     cascade reads it once per tile of gathered rows."""
     import torch
-
-    from workloads import shared_prefix_step
     dev = torch.device("cuda:0")
-    step = shared_prefix_step(256, 16384, 0, 512, 11, device=dev, fill="zero")
+    step, (r,), _, n, warm = workload_runners("shared_prefix_plain", dev, args)
+    _, (rc,), _, _, _ = workload_runners("shared_prefix_read_once", dev, args,
+                                         pools=(r.g["kc"], r.g["vc"]))
     wm = work_model(step)
-    prefix = list(step.info["shared_blocks"])
-    r = StepRunner(step, dev, 0)
-    rc = StepRunner(step, dev, 0, pools=(r.g["kc"], r.g["vc"]),
-                    cascade=(list(range(step.num_seqs)), prefix))
     res = {"workload": "256 decodes sharing a 16384-token prefix + 0..512 private tokens "
                        "(Hq 32/Hkv 8, d 128, bf16)", "step_bytes_unique": wm["bytes"]}
     for name, run in (("plain", r), ("shared_prefix_read_once", rc)):
-        ms, _ = time_steps([run], args.extra_steps, 3, not args.eager, log)
-        kt = kernel_times([run], min(args.extra_steps, 20), log)
+        ms, _ = time_steps([run], n, warm, not args.eager, log)
+        kt = kernel_times([run], min(n, 20), log)
         res[name] = {"ms_per_step": ms, "step_GBps_unique": wm["bytes"] / (ms * 1e-3) / 1e9,
                      "kernels_us": {k: round(v["avg_us"], 2) for k, v in kt.items()}}
     log(f"shared prefix: {json.dumps(res)}")
@@ -696,13 +754,11 @@ def bench_config1(args, log):
 def bench_extra(cfg, args, log):
     import torch
 
-    from workloads import config_step
     dev = torch.device("cuda:0")
-    step = config_step(cfg, device=dev, fill="zero")
-    r = StepRunner(step, dev, 0)
+    step, (r,), _, n, warm = workload_runners(PROFILE_NAMES[cfg], dev, args)
     wm = work_model(step)
-    ms, mode = time_steps([r], args.extra_steps, 3, not args.eager, log)
-    kt = kernel_times([r], min(args.extra_steps, 20), log)
+    ms, mode = time_steps([r], n, warm, not args.eager, log)
+    kt = kernel_times([r], min(n, 20), log)
     out = {"workload": WORKLOAD_NAMES[cfg], "ms_per_step": ms, "launch": mode,
            "num_splits": r.splits, "tokens_per_s": step.num_tokens / (ms * 1e-3),
            "step_GBps": wm["bytes"] / (ms * 1e-3) / 1e9,
@@ -724,15 +780,13 @@ def bench_extra(cfg, args, log):
         t_roof = max(wm["bytes"] / (PEAK_HBM_GBS * 1e9), wm["flops"] / (PEAK_BF16_TFLOPS * 1e12))
         out["step_roofline_frac"] = t_roof / (ms * 1e-3)
         # the same step with the shared 1024-token prefix read once
-        prefix = list(step.info["shared_blocks"])
-        P = len(prefix)
-        bt = step.block_tables
-        sharers = [b for b in range(step.num_seqs) if list(bt[b, :P]) == prefix]
-        rc = StepRunner(step, dev, 0, pools=(r.g["kc"], r.g["vc"]), cascade=(sharers, prefix))
-        cms, _ = time_steps([rc], args.extra_steps, 3, not args.eager, log)
-        ckt = kernel_times([rc], min(args.extra_steps, 20), log)
+        _, (rc,), _, _, _ = workload_runners(PROFILE_NAMES[cfg] + "_shared_prefix", dev, args,
+                                             pools=(r.g["kc"], r.g["vc"]))
+        cms, _ = time_steps([rc], n, warm, not args.eager, log)
+        ckt = kernel_times([rc], min(n, 20), log)
         out["shared_prefix_read_once"] = {
-            "sharers": len(sharers), "prefix_blocks": P, "ms_per_step": cms,
+            "sharers": int(rc.g["sharers"].numel()), "prefix_blocks": int(rc.g["prefix"].numel()),
+            "ms_per_step": cms,
             "step_GBps": wm["bytes"] / (cms * 1e-3) / 1e9,
             "kernels_us": {k: round(v["avg_us"], 2) for k, v in ckt.items()}}
         del rc
@@ -796,6 +850,9 @@ def main():
         torch.cuda.synchronize()
         log("copy calibration: 3 copies of 1073741824 bytes")
         del src, dst
+    if args.profile:
+        print(json.dumps(profile_workload(args.profile, args, log)), flush=True)
+        return
     if args.skip_main:
         sec = set(x.strip() for x in args.sections.split(",") if x.strip())
         part = {}
