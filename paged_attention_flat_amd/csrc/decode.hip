@@ -157,13 +157,22 @@ __global__ __launch_bounds__(64 * NW, (PIPE == 2 && NW < 8 ? 8 / NW : 1)) void d
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, kg = lane >> 4;
 
-  if (p.knew != nullptr && blockIdx.x == 0 && blockIdx.y == 0) {
+  CT* const kc_w = const_cast<CT*>(static_cast<const CT*>(p.kc));
+  CT* const vc_w = const_cast<CT*>(static_cast<const CT*>(p.vc));
+  // First-level metadata, issued together (each serialised scalar round trip
+  // here delays every work-group's first K/V load).  order[1 + rank] is in
+  // bounds for every rank (rank < num_seqs).
+  const bool tail_wg = p.knew != nullptr && blockIdx.x == 0 && blockIdx.y == 0;
+  int b = rank;
+  int live = 1;
+  if (p.order != nullptr) {
+    live = rank < p.order[0];
+    b = p.order[1 + rank];
+  }
+  if (tail_wg) {
     // fused KV write of tokens after the last request's rows (no row reads
     // them; written for the pool's sake, every KV head)
-    const int t_end = p.qsl[p.num_seqs];
-    CT* kc = const_cast<CT*>(static_cast<const CT*>(p.kc));
-    CT* vc = const_cast<CT*>(static_cast<const CT*>(p.vc));
-    for (int t = t_end; t < p.nt; ++t) {
+    for (int t = p.qsl[p.num_seqs]; t < p.nt; ++t) {
       const int64_t sl = p.slots[t];
       if (sl < 0 || sl >= p.num_slots) continue;
       const size_t cb = (size_t)(sl >> 4), off = (size_t)(sl & 15);
@@ -172,26 +181,25 @@ __global__ __launch_bounds__(64 * NW, (PIPE == 2 && NW < 8 ? 8 / NW : 1)) void d
         const size_t head = (cb * p.hkv + hh) * 16 * D;
         const size_t src = ((size_t)t * p.hkv + hh) * D + dd;
         if constexpr (F8) {
-          kc[head + off * D + dd] = e4m3_code(bf16_bits_to_f32(p.knew[src]) / p.k_scale[hh]);
-          vc[head + (size_t)dd * 16 + off] =
+          kc_w[head + off * D + dd] = e4m3_code(bf16_bits_to_f32(p.knew[src]) / p.k_scale[hh]);
+          vc_w[head + (size_t)dd * 16 + off] =
               e4m3_code(bf16_bits_to_f32(p.vnew[src]) / p.v_scale[hh]);
         } else {
-          kc[head + off * D + dd] = p.knew[src];
-          vc[head + (size_t)dd * 16 + off] = p.vnew[src];
+          kc_w[head + off * D + dd] = p.knew[src];
+          vc_w[head + (size_t)dd * 16 + off] = p.vnew[src];
         }
       }
     }
   }
-  int b = rank;
-  if (p.order != nullptr) {
-    if (rank >= p.order[0]) return;
-    b = p.order[1 + rank];
-  }
+  if (!live) return;
   // Split s covers blocks [s * bps, (s + 1) * bps) of every request, bps from
   // the host-known max_seq_len, so the first 64 block-table entries can be
   // fetched together with query_start_loc / seq_lens (one round trip fewer
   // before the first K/V load).  Splits past a shorter request are empty.
   const int pv0 = p.pre_index != nullptr ? p.pre_index[b] : -1;
+  const int q0 = p.qsl[b];
+  const int q1 = p.qsl[b + 1];
+  const int seq_len = p.seq_lens[b];
   const int blk_lo = (pv0 >= 0 ? p.pre_blocks : 0) + split * p.split_blocks;
   const int32_t* table = p.tables + (size_t)b * p.table_stride;
   int tab = 0, tab_base = 0;
@@ -199,10 +207,10 @@ __global__ __launch_bounds__(64 * NW, (PIPE == 2 && NW < 8 ? 8 / NW : 1)) void d
     const int j = blk_lo + lane;
     tab = j < p.table_stride ? table[j] : 0;
   }
-  const int q0 = p.qsl[b];
-  const int q_len = p.qsl[b + 1] - q0;
-  if (q_len <= 0 || q_len > DQ) return;  // empty request or a prefill row set
-  const int seq_len = p.seq_lens[b];
+  const int q_len = q1 - q0;
+  // empty request, a prefill row set, or (invalid) fewer cached than new
+  // tokens; seq_len in the test keeps its load in the same round trip
+  if (q_len <= 0 || q_len > DQ || seq_len < q_len) return;
   const int ctx = seq_len - q_len;
   const int nblocks = (seq_len + 15) >> 4;
   const int blk_hi = min(nblocks, blk_lo + p.split_blocks);
@@ -211,51 +219,90 @@ __global__ __launch_bounds__(64 * NW, (PIPE == 2 && NW < 8 ? 8 / NW : 1)) void d
   const int qpos = ctx + min(qi, q_len - 1);
   const bool col_valid = qi < q_len;
 
+  // Fused KV write.  The slot of position p is table[p / 16] * 16 + p % 16
+  // ("Model execution", "Flattening a step"), so the only reader of a new
+  // token's entry (for this KV head) is the wave of this work-group that
+  // processes the pair of blocks holding it: that wave writes the token (K
+  // row and V column; E4M3 cache: quantised exactly as pa_kv_write_fp8 does)
+  // and waits for its own stores before it loads that pair.  No barrier: the
+  // other waves never read these entries, and the kernel starts with a clean
+  // vector L1, so the load after the acknowledged store reads the new bytes.
+  // The first token a wave writes is fetched before its first K/V loads are
+  // issued, so the write costs no round trip of its own.
+  auto own_tok = [&](int i) {
+    const int blk = (ctx + i) >> 4;
+    return blk >= blk_lo && blk < blk_hi && (((blk - blk_lo) >> 1) % NW) == wave;
+  };
+  int own0 = -1;
   if (p.knew != nullptr) {
-    // Fused KV write: this request's new tokens whose blocks fall in this
-    // split's range are written here (head kvh) before any K/V is read; the
-    // slot of position p is table[p / 16] * 16 + p % 16 by definition, so no
-    // other work-group reads these entries.  E4M3 cache: quantised exactly
-    // as pa_kv_write_fp8 does.
-    bool wrote = false;
-    CT* kc = const_cast<CT*>(static_cast<const CT*>(p.kc));
-    CT* vc = const_cast<CT*>(static_cast<const CT*>(p.vc));
-    for (int i = 0; i < q_len; ++i) {
-      const int blk = (ctx + i) >> 4;
-      if (blk < blk_lo || blk >= blk_hi) continue;
-      const int64_t sl = p.slots[q0 + i];
-      if (sl < 0 || sl >= p.num_slots) continue;
-      wrote = true;
-      const size_t src = ((size_t)(q0 + i) * p.hkv + kvh) * D;
-      const size_t cb = (size_t)(sl >> 4), off = (size_t)(sl & 15);
-      const size_t head = (cb * p.hkv + kvh) * 16 * D;
-      for (int e = threadIdx.x; e < D / 8; e += 64 * NW) {
-        const uint4 k8 = *reinterpret_cast<const uint4*>(p.knew + src + 8 * e);
-        if constexpr (F8) {
-          const float ks = p.k_scale[kvh];
-          const uint32_t w[4] = {k8.x, k8.y, k8.z, k8.w};
-          float f[8];
+    for (int i = q_len - 1; i >= 0; --i)
+      if (own_tok(i)) own0 = i;
+  }
+  const bool own_any = own0 >= 0;
+  auto pair_new = [&](int pr) {  // pair pr of this wave holds a token it wrote
+    const int k0 = 16 * (blk_lo + 2 * pr);
+    return own_any && k0 + 32 > ctx && k0 < seq_len;
+  };
+  struct NewTok {
+    int64_t slot;
+    uint4 k;             // lanes < D / 8: 8 elements of the K row
+    uint16_t v[D / 64];  // elements lane + 64 j of the V row
+  };
+  auto fetch_tok = [&](int i, NewTok& t) {
+    const size_t src = ((size_t)(q0 + i) * p.hkv + kvh) * D;
+    t.slot = p.slots[q0 + i];
+    t.k = lane < D / 8 ? *reinterpret_cast<const uint4*>(p.knew + src + 8 * lane)
+                       : make_uint4(0, 0, 0, 0);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            f[2 * j] = __uint_as_float(w[j] << 16) / ks;
-            f[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u) / ks;
-          }
-          *reinterpret_cast<uint2*>(kc + head + off * D + 8 * e) =
-              make_uint2(e4m3_pack4(f[0], f[1], f[2], f[3]), e4m3_pack4(f[4], f[5], f[6], f[7]));
-        } else {
-          *reinterpret_cast<uint4*>(kc + head + off * D + 8 * e) = k8;
+    for (int j = 0; j < D / 64; ++j) t.v[j] = p.vnew[src + lane + 64 * j];
+  };
+  auto put_tok = [&](const NewTok& t) {
+    if (t.slot < 0 || t.slot >= p.num_slots) return;
+    const size_t cb = (size_t)(t.slot >> 4), off = (size_t)(t.slot & 15);
+    const size_t head = (cb * p.hkv + kvh) * 16 * D;
+    if (lane < D / 8) {
+      if constexpr (F8) {
+        const float ks = p.k_scale[kvh];
+        const uint32_t w[4] = {t.k.x, t.k.y, t.k.z, t.k.w};
+        float f[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f[2 * j] = __uint_as_float(w[j] << 16) / ks;
+          f[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u) / ks;
         }
-      }
-      for (int e = threadIdx.x; e < D; e += 64 * NW) {
-        if constexpr (F8)
-          vc[head + (size_t)e * 16 + off] =
-              e4m3_code(bf16_bits_to_f32(p.vnew[src + e]) / p.v_scale[kvh]);
-        else
-          vc[head + (size_t)e * 16 + off] = p.vnew[src + e];
+        *reinterpret_cast<uint2*>(kc_w + head + off * D + 8 * lane) =
+            make_uint2(e4m3_pack4(f[0], f[1], f[2], f[3]), e4m3_pack4(f[4], f[5], f[6], f[7]));
+      } else {
+        *reinterpret_cast<uint4*>(kc_w + head + off * D + 8 * lane) = t.k;
       }
     }
-    if (wrote) __syncthreads();  // stores complete before any wave reads the block
-  }
+#pragma unroll
+    for (int j = 0; j < D / 64; ++j) {
+      const size_t dd = lane + 64 * j;
+      if constexpr (F8)
+        vc_w[head + dd * 16 + off] = e4m3_code(bf16_bits_to_f32(t.v[j]) / p.v_scale[kvh]);
+      else
+        vc_w[head + dd * 16 + off] = t.v[j];
+    }
+  };
+  // (G = 16, bf16: the early fetch would cost a register spill in the
+  // two-set loop, so the token is fetched when it is written)
+  constexpr bool kEarly = !(G >= 16 && !F8 && D == 128);
+  NewTok tok0;
+  if (kEarly && own_any) fetch_tok(own0, tok0);
+  // called once this wave's first loads are issued: its stores, then (rare)
+  // the further tokens it owns, each fetched and stored in turn
+  auto write_own = [&]() {
+    if (!own_any) return;
+    if (!kEarly) fetch_tok(own0, tok0);
+    put_tok(tok0);
+    for (int i = own0 + 1; i < q_len; ++i) {
+      if (!own_tok(i)) continue;
+      NewTok t;
+      fetch_tok(i, t);
+      put_tok(t);
+    }
+  };
 
   // Q as the B operand: lane (col, kg) holds d = 32*st + 8*kg .. +8
   bf16x8 qf[KSTEPS];
@@ -395,25 +442,35 @@ __global__ __launch_bounds__(64 * NW, (PIPE == 2 && NW < 8 ? 8 / NW : 1)) void d
     }
   };
 
+  // waits for this wave's KV-write stores before it loads a pair they hit
+  auto load_after_write = [&](Frag& f, int pr) {
+    if (pair_new(pr)) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    load(f, pr);
+  };
   if constexpr (PIPE == 1) {
+    // many work-groups per CU: the write's round trip hides behind the others
+    write_own();
     for (int pr = wave; pr < npairs; pr += NW) {
       Frag f;
-      load(f, pr);
+      load_after_write(f, pr);
       compute(f, pr);
     }
   } else {
     // two fragment sets: the next pair's loads are in flight during compute
     Frag fa, fb;
     int pr = wave;
-    if (pr < npairs) load(fa, pr);
+    const bool d0 = pair_new(pr);
+    if (pr < npairs && !d0) load(fa, pr);
+    write_own();
+    if (pr < npairs && d0) load_after_write(fa, pr);
     while (pr < npairs) {
       int pn = pr + NW;
-      if (pn < npairs) load(fb, pn);
+      if (pn < npairs) load_after_write(fb, pn);
       compute(fa, pr);
       pr = pn;
       if (pr >= npairs) break;
       pn = pr + NW;
-      if (pn < npairs) load(fa, pn);
+      if (pn < npairs) load_after_write(fa, pn);
       compute(fb, pr);
       pr = pn;
     }

@@ -84,6 +84,29 @@ def test_decode_step_tokens_across_blocks_and_splits():
         check_all(step, out, lse, g, f"straddle S={splits}")
 
 
+@pytest.mark.parametrize("group,head_dim", [(1, 128), (2, 64), (8, 128), (16, 128), (16, 64)])
+def test_decode_step_group_sizes(group, head_dim):
+    # every group size the decode kernel packs (16 / G new tokens per
+    # request), new tokens in a wave's first pair, in two pairs owned by
+    # different waves, and across split boundaries; both launch shapes
+    dq = 16 // group
+    rng = np.random.default_rng(11 + group)
+    shapes = [(0, dq), (30, dq), (17, max(1, dq // 2)), (600, 1), (63, dq), (5, 0)]
+    need = [max(1, -(-(p + n) // 16)) for p, n in shapes]
+    nb = sum(need) + 4
+    perm = [int(x) for x in rng.permutation(nb)]
+    tables, k = [], 0
+    for n in need:
+        tables.append(perm[k:k + n])
+        k += n
+    step = build_step(f"groups{group}", [Request(p, n, t) for (p, n), t in zip(shapes, tables)],
+                      dtype="bf16", num_q_heads=2 * group, num_kv_heads=2, head_dim=head_dim,
+                      num_blocks=nb, seed=90 + group, pad_tokens=2)
+    for splits in (0, 3, 40):
+        out, lse, g = run_step(step, splits)
+        check_all(step, out, lse, g, f"G={group} d={head_dim} S={splits}")
+
+
 def test_decode_step_falls_back_for_prefill_rows_and_fp32():
     step = config_step(5, scale_down=SMALL[5])
     out, lse, g = run_step(step)
