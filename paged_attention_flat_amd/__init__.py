@@ -19,6 +19,7 @@ import torch
 
 from . import _lib
 from ._lib import LIB, PA_BF16, PA_F32, PA_BLOCK_SIZE, PA_MAX_SPLITS  # noqa: F401
+from .validate import step_problems, validate_step  # noqa: F401
 
 __all__ = [
     "PaError", "kv_write", "attention", "split_combine", "workspace_size",
@@ -26,7 +27,7 @@ __all__ = [
     "decode_step", "decode_step_fp8",
     "choose_num_splits", "capture_size", "alloc_cache", "workspace", "trace_begin", "trace_end",
     "trace_read",
-    "kernel_name", "version",
+    "kernel_name", "version", "validate_step", "step_problems",
 ]
 
 
