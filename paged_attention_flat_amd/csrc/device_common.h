@@ -91,6 +91,21 @@ __device__ __forceinline__ float shfl_xor(float v, int mask) {
   return __shfl_xor(v, mask, 64);
 }
 
+// max / sum of v over lanes i and i ^ 32 with one VALU lane-half swap
+// (v_permlane32_swap exchanges the upper half of its first operand with the
+// lower half of its second; given v twice, the two results hold v of lane i
+// and of lane i ^ 32 in some order)
+__device__ __forceinline__ float max_xor32(float v) {
+  const uint32_t b = __float_as_uint(v);
+  const auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  const uint32_t b = __float_as_uint(v);
+  const auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) {
   return __builtin_amdgcn_exp2f(x);
 }

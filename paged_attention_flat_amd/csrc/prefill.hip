@@ -489,7 +489,7 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
 #pragma unroll
         for (int u = 0; u < w / 2; ++u) mx[u] = fmaxf(mx[u], mx[u + w / 2]);
       float mt = mx[0];
-      mt = fmaxf(mt, shfl_xor(mt, 32)) * scale_log2;  // scale > 0 commutes with max
+      mt = max_xor32(mt) * scale_log2;  // scale > 0 commutes with max
       move[rg] = __ballot(mt > m[rg] + kLazy) != 0;
       // finite once the wave has met key 0, which every row sees
       m_new[rg] = move[rg] ? fmaxf(m[rg], mt) : m[rg];
@@ -546,7 +546,7 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
 
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) {
-    const float lt = l[rg] + shfl_xor(l[rg], 32);
+    const float lt = sum_xor32(l[rg]);
     if (!valid[rg]) continue;
     const float inv = v_scale / lt;
     const int h = kvh * G + gr[rg];
