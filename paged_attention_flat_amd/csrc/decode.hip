@@ -417,8 +417,7 @@ __global__ __launch_bounds__(64 * NW, (PIPE == 2 && NW < 8 ? 8 / NW : 1)) void d
     }
     float mt = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
                      fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-    mt = fmaxf(mt, shfl_xor(mt, 16));
-    mt = fmaxf(mt, shfl_xor(mt, 32));
+    mt = max_xor32(max_xor16(mt));
     mt *= scale_log2;  // scale > 0 commutes with max
     const float m_new = fmaxf(m, mt);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
@@ -477,8 +476,7 @@ __global__ __launch_bounds__(64 * NW, (PIPE == 2 && NW < 8 ? 8 / NW : 1)) void d
   }
 
   // per-column denominator: sum the four key groups of the wave
-  l += shfl_xor(l, 16);
-  l += shfl_xor(l, 32);
+  l = sum_xor32(sum_xor16(l));
 
   // tree merge of the waves; every wave holds the same (column, dim) layout,
   // so the merge is lane-local
