@@ -435,29 +435,46 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
     }
     if (more) gload(k0 + kBK);
     // ---- S^T = K Q^T: every K fragment feeds all row groups ------------------
+    // The K fragments of the next group of MFMAs are read from LDS while the
+    // current group runs (the fences keep the compiler from pairing each read
+    // with the MFMA right after it, which exposes the LDS latency every time).
     f32x16 s[RG][KB];
-#pragma unroll
-    for (int rg = 0; rg < RG; ++rg)
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) s[rg][kb][j] = 0.f;
-#pragma unroll
-    for (int s0 = 0; s0 < QSTEPS; s0 += 4) {
-      uint4 fk[KB][4];
+    constexpr int SG = 2;                    // k-steps per group
+    constexpr int NG = QSTEPS / SG;          // groups per tile
+    static_assert(QSTEPS % SG == 0, "k-steps split into groups");
+    uint4 fka[KB][SG], fkb[KB][SG];
+    auto kfrag = [&](uint4 (&f)[KB][SG], int g) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          fk[kb][u] = *reinterpret_cast<const uint4*>(&sK[kbuf][32 * kb + row][8 * kg + 16 * (s0 + u)]);
+        for (int u = 0; u < SG; ++u)
+          f[kb][u] = *reinterpret_cast<const uint4*>(
+              &sK[kbuf][32 * kb + row][8 * kg + 16 * (SG * g + u)]);
+    };
+    auto kmfma = [&](const uint4 (&f)[KB][SG], int g) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < SG; ++u)
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int rg = 0; rg < RG; ++rg)
-            s[rg][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fk[kb][u]), qf[rg][s0 + u],
-                                                                s[rg][kb], 0, 0, 0);
+            s[rg][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                as_bf16x8(f[kb][u]), qf[rg][SG * g + u],
+                (g == 0 && u == 0) ? f32x16{} : s[rg][kb], 0, 0, 0);
+    };
+    kfrag(fka, 0);
+#pragma unroll
+    for (int g = 0; g < NG; g += 2) {
+      if (g + 1 < NG) kfrag(fkb, g + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      kmfma(fka, g);
+      __builtin_amdgcn_sched_barrier(0);
+      if (g + 1 < NG) {
+        if (g + 2 < NG) kfrag(fka, g + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        kmfma(fkb, g + 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     if (k0 + kBK - 1 > wpos_lo) {
 #pragma unroll
