@@ -134,3 +134,112 @@ def test_capture_size_matches_printed_ladder(lib):
     assert lib.pa_capture_size(0, 512) == -1 and lib.pa_capture_size(-3, 512) == -1
     # a smaller top size cuts the ladder there
     assert lib.pa_capture_size(200, 128) == -1 and lib.pa_capture_size(128, 128) == 128
+
+
+# ---- the entry points beyond the core three: host validation and empty steps ----
+
+P = ctypes.c_void_p(256)
+
+
+def test_kv_write_fp8_validation(lib):
+    f = lib.pa_kv_write_fp8
+    assert f(P, P, P, P, P, P, P, 4, 2, 96, 16, 8, 1, None) == 3        # head_dim
+    assert f(P, P, P, P, P, P, P, 4, 2, 128, 32, 8, 1, None) == 3       # block size
+    assert f(P, P, P, P, P, P, P, 4, 2, 128, 16, 8, 9, None) == 2       # dtype
+    assert f(P, P, P, P, P, None, P, 4, 2, 128, 16, 8, 1, None) == 1    # no K scales
+    assert f(P, P, P, P, P, P, P, 4, 0, 128, 16, 8, 1, None) == 2       # no KV heads
+    assert f(None, None, None, None, None, None, None, 0, 2, 128, 16, 8, 1, None) == 0
+
+
+def test_rope_kv_write_validation(lib):
+    def rope(**kw):
+        a = dict(q=P, k=P, v=P, kc=P, vc=P, sm=P, pos=P, cs=P, maxp=64, nt=4, hq=8, hkv=2,
+                 d=128, bs=16, nb=8, dtype=1)
+        a.update(kw)
+        return lib.pa_rope_kv_write(a["q"], a["k"], a["v"], a["kc"], a["vc"], a["sm"], a["pos"],
+                                    a["cs"], a["maxp"], a["nt"], a["hq"], a["hkv"], a["d"],
+                                    a["bs"], a["nb"], a["dtype"], None)
+    assert rope(hq=6, hkv=4) == 2
+    assert rope(d=96) == 3
+    assert rope(bs=8) == 3
+    assert rope(dtype=4) == 2
+    assert rope(pos=None) == 1
+    assert rope(cs=None) == 1
+    assert rope(q=None, k=None, v=None, kc=None, vc=None, sm=None, pos=None, cs=None, nt=0) == 0
+
+
+def _fwd_fp8(lib, **kw):
+    a = dict(q=P, kc=P, vc=P, ks=P, vs=P, qsl=P, sl=P, bt=P, ns=2, nt=3, mq=2, ms=40, hq=8,
+             hkv=2, d=128, bs=16, stride=3, nb=10, scale=0.1, splits=1, out=P, lse=None, ws=P,
+             wsb=1 << 20)
+    a.update(kw)
+    return lib.pa_attention_fwd_fp8(a["q"], a["kc"], a["vc"], a["ks"], a["vs"], a["qsl"],
+                                    a["sl"], a["bt"], a["ns"], a["nt"], a["mq"], a["ms"],
+                                    a["hq"], a["hkv"], a["d"], a["bs"], a["stride"], a["nb"],
+                                    a["scale"], a["splits"], a["out"], a["lse"], a["ws"],
+                                    a["wsb"], None)
+
+
+def test_attention_fp8_validation(lib):
+    assert _fwd_fp8(lib, hq=6, hkv=2) == 3
+    assert _fwd_fp8(lib, d=80) == 3
+    assert _fwd_fp8(lib, scale=0.0) == 2
+    assert _fwd_fp8(lib, ks=None) == 1
+    assert _fwd_fp8(lib, vs=None) == 1
+    assert _fwd_fp8(lib, ws=None) == 4
+    assert _fwd_fp8(lib, ns=0) == 0 and _fwd_fp8(lib, nt=0) == 0
+
+
+def _cascade(lib, **kw):
+    a = dict(q=P, kc=P, vc=P, qsl=P, sl=P, bt=P, ns=2, nt=2, mq=1, ms=40, hq=8, hkv=2, d=128,
+             bs=16, stride=3, nb=10, scale=0.1, splits=1, sh=P, nsh=2, pb=P, npb=2, out=P,
+             lse=None, ws=P, wsb=1 << 20)
+    a.update(kw)
+    return lib.pa_attention_fwd_cascade(a["q"], a["kc"], a["vc"], a["qsl"], a["sl"], a["bt"],
+                                        a["ns"], a["nt"], a["mq"], a["ms"], a["hq"], a["hkv"],
+                                        a["d"], a["bs"], a["stride"], a["nb"], a["scale"],
+                                        a["splits"], a["sh"], a["nsh"], a["pb"], a["npb"],
+                                        a["out"], a["lse"], a["ws"], a["wsb"], None)
+
+
+def test_cascade_validation(lib):
+    assert _cascade(lib, nsh=-1) == 2
+    assert _cascade(lib, npb=-3) == 2
+    assert _cascade(lib, sh=None) == 1
+    assert _cascade(lib, pb=None) == 1
+    assert _cascade(lib, d=96) == 3
+    assert _cascade(lib, hq=6, hkv=4) == 2
+    assert _cascade(lib, ns=0) == 0
+
+
+def _step(lib, fp8=False, **kw):
+    a = dict(k=P, v=P, kc=P, vc=P, sm=P, ks=P, vs=P, q=P, qsl=P, sl=P, bt=P, ns=2, nt=2, mq=1,
+             ms=40, hq=8, hkv=2, d=128, bs=16, stride=3, nb=10, scale=0.1, splits=1, out=P,
+             lse=None, ws=P, wsb=1 << 20, dtype=1)
+    a.update(kw)
+    head = [a["k"], a["v"], a["kc"], a["vc"], a["sm"]]
+    if fp8:
+        head += [a["ks"], a["vs"]]
+    rest = [a["q"], a["qsl"], a["sl"], a["bt"], a["ns"], a["nt"], a["mq"], a["ms"], a["hq"],
+            a["hkv"], a["d"], a["bs"], a["stride"], a["nb"], a["scale"], a["splits"], a["out"],
+            a["lse"], a["ws"], a["wsb"], a["dtype"], None]
+    f = lib.pa_decode_step_fp8 if fp8 else lib.pa_decode_step
+    return f(*head, *rest)
+
+
+def test_decode_step_validation(lib):
+    for fp8 in (False, True):
+        assert _step(lib, fp8, hq=6, hkv=4) == 2          # heads
+        assert _step(lib, fp8, d=96) == 3                 # one launch: the kernel's check
+        assert _step(lib, fp8, k=None) == 1               # one launch needs the new K
+        assert _step(lib, fp8, k=ctypes.c_void_p(258)) == 2   # misaligned new K
+        assert _step(lib, fp8, mq=5, nt=5, d=96) == 3     # two calls: the KV write's check
+        assert _step(lib, fp8, dtype=0, d=96) == 3        # fp32: two calls as well
+        assert _step(lib, fp8, nt=0) == 0                 # empty step
+    assert _step(lib, True, ks=None) == 1
+
+
+def test_workspace_init_validation(lib):
+    assert lib.pa_attention_workspace_init(None, 0, None) == 0
+    assert lib.pa_attention_workspace_init(None, 64, None) == 1
+    assert lib.pa_attention_workspace_init(ctypes.c_void_p(260), 64, None) == 2
