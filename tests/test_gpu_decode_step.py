@@ -79,7 +79,7 @@ def test_decode_step_tokens_across_blocks_and_splits():
     sm = step.slot_mapping.copy()
     sm[-2] = perm[k] * 16 + 5          # a trailing token written to a free block
     step.slot_mapping = sm
-    for splits in (0, 32, 63):
+    for splits in (0, 32, 63, 256):
         out, lse, g = run_step(step, splits)
         check_all(step, out, lse, g, f"straddle S={splits}")
 

@@ -206,7 +206,7 @@ def test_small_configs_bf16(cfg):
     check(step, out, lse, ro, rl, what=f"config{cfg} small")
 
 
-@pytest.mark.parametrize("splits", [1, 2, 7, 64, 128])
+@pytest.mark.parametrize("splits", [1, 2, 7, 64, 128, 256])
 def test_split_sweep_small_decode(splits):
     step = config_step(2, scale_down=SMALL[2])
     out, lse, _ = run_gpu(step, num_splits=splits)
