@@ -91,6 +91,13 @@ __device__ __forceinline__ float shfl_xor(float v, int mask) {
   return __shfl_xor(v, mask, 64);
 }
 
+// 16-byte load with the non-temporal cache policy (data read once per step)
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream16(const uint4* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // max / sum of v over lanes i and i ^ 32 with one VALU lane-half swap
 // (v_permlane32_swap exchanges the upper half of its first operand with the
 // lower half of its second; given v twice, the two results hold v of lane i
