@@ -251,6 +251,10 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
   const int32_t* table = CASC ? p.pre_blocks : p.tables + (size_t)b * p.table_stride;
   const size_t head_elems = 16 * D;
   const size_t block_elems = (size_t)p.hkv * head_elems;
+  // block ids are non-negative and a block holds < 2^32 elements: one
+  // 32 x 32 -> 64-bit multiply-add per block instead of a signed 64-bit product
+  const uint32_t block_elems32 = (uint32_t)block_elems;
+  auto blk_off = [&](int id) -> uint64_t { return (uint64_t)(uint32_t)id * block_elems32; };
   const CT* kbase = static_cast<const CT*>(p.kc) + kvh * head_elems;
   const CT* vbase = static_cast<const CT*>(p.vc) + kvh * head_elems;
   // E4M3 cache: K's scale folds into the score scale, V's into the output;
@@ -291,11 +295,11 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
       // whole tile inside the context: no per-key checks
 #pragma unroll
       for (int i = 0; i < KCH; ++i)
-        kr[i] = *reinterpret_cast<const RT*>(kbase + (size_t)s_tab[tb + k_blk[i]] * block_elems +
+        kr[i] = *reinterpret_cast<const RT*>(kbase + blk_off(s_tab[tb + k_blk[i]]) +
                                               k_src[i]);
 #pragma unroll
       for (int i = 0; i < VCH; ++i)
-        vr[i] = *reinterpret_cast<const RT*>(vbase + (size_t)s_tab[tb + v_blk[i]] * block_elems +
+        vr[i] = *reinterpret_cast<const RT*>(vbase + blk_off(s_tab[tb + v_blk[i]]) +
                                               v_src[i]);
       return;
     }
@@ -304,7 +308,7 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
       const int kpos = k0 + (k_src[i] / D) + 16 * k_blk[i];
       RT v = {};
       if (kpos < seq_len)
-        v = *reinterpret_cast<const RT*>(kbase + (size_t)s_tab[tb + k_blk[i]] * block_elems +
+        v = *reinterpret_cast<const RT*>(kbase + blk_off(s_tab[tb + k_blk[i]]) +
                                          k_src[i]);
       kr[i] = v;
     }
@@ -313,7 +317,7 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
       const int kpos = k0 + v_key[i];
       RT v = {};
       if (kpos < seq_len) {
-        v = *reinterpret_cast<const RT*>(vbase + (size_t)s_tab[tb + v_blk[i]] * block_elems +
+        v = *reinterpret_cast<const RT*>(vbase + blk_off(s_tab[tb + v_blk[i]]) +
                                          v_src[i]);
         if (kpos + 8 > seq_len) {
           // keys past the context may hold anything (even NaN): zero them
@@ -352,14 +356,17 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
     }
   };
 
-  float m[RG], l[RG], alpha[RG];
+  // m: running max (base 2); l: denominator at m; m_prev, lpend, rescale:
+  // the previous tile's max move and row sum, folded in by settle()
+  float m[RG], l[RG], m_prev[RG], lpend[RG];
   bool rescale[RG];
   f32x16 acc[RG][DB];
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) {
     m[rg] = -INFINITY;
     l[rg] = 0.f;
-    alpha[rg] = 1.f;
+    m_prev[rg] = -INFINITY;
+    lpend[rg] = 0.f;
     rescale[rg] = false;
 #pragma unroll
     for (int i = 0; i < DB; ++i)
@@ -380,6 +387,26 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
   gload(kbeg);
   lstore(0, 0);
   __syncthreads();
+
+  // A moved max of the previous tile: acc holds every P.V up to two tiles
+  // back and l every row sum up to two tiles back, both at the old max; the
+  // previous tile's row sum is at the new one.  The rescale (and its one
+  // exponential) runs only on tiles where the max moved: the branch is
+  // wave-uniform.  CASC rows that have seen no key yet keep a factor of 1.
+  auto settle = [&]() {
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) {
+      if (rescale[rg]) {
+        const float alpha =
+            (CASC && m[rg] == -INFINITY) ? 1.f : fast_exp2(m_prev[rg] - m[rg]);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[rg][db] *= alpha;
+        l[rg] = l[rg] * alpha + lpend[rg];
+      } else {
+        l[rg] += lpend[rg];
+      }
+    }
+  };
 
   // O^T += V^T P^T over a tile: four 16-key steps; each V^T fragment read
   // from LDS feeds the MFMAs of every row group of the wave
@@ -418,14 +445,7 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
   for (int k0 = kbeg; k0 < kend; k0 += kBK, ++it) {
     const int kbuf = it & 1, vbuf = it % 3;
     const bool more = k0 + kBK < kend;
-    // a moved max of the previous tile: acc now holds every P.V up to two
-    // tiles back, accumulated at the old max
-#pragma unroll
-    for (int rg = 0; rg < RG; ++rg)
-      if (rescale[rg]) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db) acc[rg][db] *= alpha[rg];
-      }
+    settle();
     if (more && ((k0 + kBK) >> 4) >= tab_base + kTabWin) {
       // the next tile starts a new window (tiles never straddle one); every
       // thread is past its last use of the old entries
@@ -493,16 +513,20 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
     bool move[RG];
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
-      // row max as a tree (short dependence chains)
-      float mx[4 * KB];
+      // row max: 2 * KB independent chains of three-input maxima (8 values
+      // per chain, 4 instructions), then the chains
+      float mx[2 * KB];
 #pragma unroll
-      for (int u = 0; u < 4 * KB; ++u) {
-        const f32x16& sv = s[rg][u >> 2];
-        const int o = 4 * (u & 3);
-        mx[u] = fmaxf(fmaxf(sv[o], sv[o + 1]), fmaxf(sv[o + 2], sv[o + 3]));
+      for (int u = 0; u < 2 * KB; ++u) {
+        const f32x16& sv = s[rg][u >> 1];
+        const int o = 8 * (u & 1);
+        float c = fmaxf(fmaxf(sv[o], sv[o + 1]), sv[o + 2]);
+        c = fmaxf(fmaxf(c, sv[o + 3]), sv[o + 4]);
+        c = fmaxf(fmaxf(c, sv[o + 5]), sv[o + 6]);
+        mx[u] = fmaxf(c, sv[o + 7]);
       }
 #pragma unroll
-      for (int w = 4 * KB; w > 1; w >>= 1)
+      for (int w = 2 * KB; w > 1; w >>= 1)
 #pragma unroll
         for (int u = 0; u < w / 2; ++u) mx[u] = fmaxf(mx[u], mx[u + w / 2]);
       float mt = mx[0];
@@ -522,13 +546,15 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
     pv(vprev, pprev);
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
-      float ps4[4] = {0.f, 0.f, 0.f, 0.f};
+      float ps4[4];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           s[rg][kb][j] = fast_exp2(__builtin_fmaf(s[rg][kb][j], scale_log2, -m_ref[rg]));
-          ps4[j & 3] += s[rg][kb][j];
+          // the first four values seed the partial sums (no 0 + x)
+          if (kb == 0 && j < 4) ps4[j] = s[rg][kb][j];
+          else ps4[j & 3] += s[rg][kb][j];
         }
       const float rs = (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
 #pragma unroll
@@ -539,12 +565,11 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
             pack_bf16x2(sp[o + 0], sp[o + 1]), pack_bf16x2(sp[o + 2], sp[o + 3]),
             pack_bf16x2(sp[o + 4], sp[o + 5]), pack_bf16x2(sp[o + 6], sp[o + 7])));
       }
-      // a moved max rescales l now and acc at the top of the next iteration,
+      // folded into acc and l by settle() at the top of the next iteration,
       // after the previous tile's P.V (accumulated at the old max) is in
-      // 1 when the max stays (CASC: also while a row has seen no key yet)
-      alpha[rg] = (CASC && m_new[rg] == -INFINITY) ? 1.f : fast_exp2(m[rg] - m_new[rg]);
+      m_prev[rg] = m[rg];
       rescale[rg] = move[rg];
-      l[rg] = l[rg] * alpha[rg] + rs;
+      lpend[rg] = rs;
       m[rg] = m_new[rg];
     }
     vprev = vbuf;
@@ -553,12 +578,7 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
     lstore(kbuf ^ 1, (it + 1) % 3);
     __syncthreads();
   }
-#pragma unroll
-  for (int rg = 0; rg < RG; ++rg)
-    if (rescale[rg]) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db) acc[rg][db] *= alpha[rg];
-    }
+  settle();
   pv(vprev, pprev);
 
 #pragma unroll
