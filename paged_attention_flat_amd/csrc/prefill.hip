@@ -410,14 +410,23 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
 
   // O^T += V^T P^T over a tile: four 16-key steps; each V^T fragment read
   // from LDS feeds the MFMAs of every row group of the wave
-  auto pv = [&](int vbuf, const bf16x8 (&pf)[RG][PS]) {
+  // (the fragments of the first step, fv0, are read by the caller ahead of
+  // time, so the first MFMAs do not wait for LDS)
+  auto vfrag = [&](uint4 (&f)[DB], int vbuf, int ps) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      f[db] = *reinterpret_cast<const uint4*>(&sV[vbuf][32 * db + row][16 * ps + 8 * kg]);
+  };
+  auto pv = [&](int vbuf, const bf16x8 (&pf)[RG][PS], const uint4 (&fv0)[DB]) {
 #pragma unroll
     for (int ps = 0; ps < PS; ++ps) {
-      const int base = 16 * ps + 8 * kg;
       uint4 fv[DB];
+      if (ps == 0) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-        fv[db] = *reinterpret_cast<const uint4*>(&sV[vbuf][32 * db + row][base]);
+        for (int db = 0; db < DB; ++db) fv[db] = fv0[db];
+      } else {
+        vfrag(fv, vbuf, ps);
+      }
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -461,8 +470,9 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
     f32x16 s[RG][KB];
     constexpr int SG = 2;                    // k-steps per group
     constexpr int NG = QSTEPS / SG;          // groups per tile
-    static_assert(QSTEPS % SG == 0, "k-steps split into groups");
+    static_assert(QSTEPS % SG == 0 && NG % 2 == 0, "k-steps split into an even number of groups");
     uint4 fka[KB][SG], fkb[KB][SG];
+    uint4 fv0[DB];
     auto kfrag = [&](uint4 (&f)[KB][SG], int g) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
@@ -491,6 +501,8 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
       __builtin_amdgcn_sched_barrier(0);
       if (g + 1 < NG) {
         if (g + 2 < NG) kfrag(fka, g + 2);
+        // the first V^T fragments of the P.V below load during the last group
+        if (g + 2 >= NG) vfrag(fv0, vprev, 0);
         __builtin_amdgcn_sched_barrier(0);
         kmfma(fkb, g + 1);
         __builtin_amdgcn_sched_barrier(0);
@@ -543,7 +555,7 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
       m_ref[rg] = (CASC && m_new[rg] == -INFINITY) ? 0.f : m_new[rg];
 
     // ---- P.V of the previous tile, interleaved with this tile's softmax -----
-    pv(vprev, pprev);
+    pv(vprev, pprev, fv0);
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
       float ps4[4];
@@ -579,7 +591,11 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
     __syncthreads();
   }
   settle();
-  pv(vprev, pprev);
+  {
+    uint4 fv0[DB];
+    vfrag(fv0, vprev, 0);
+    pv(vprev, pprev, fv0);
+  }
 
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) {
