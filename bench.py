@@ -69,9 +69,10 @@ def parse_args():
                     help="first run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--skip-main", action="store_true",
                     help="profiling aid: run only --sections and print them (no headline line)")
-    ap.add_argument("--sections", default="sweep,extra,fp8,rope,shared,tiny,achievable",
+    ap.add_argument("--sections", default="sweep,extra,fp8,rope,shared,shard,tiny,achievable",
                     help="comma list of the reports after the headline (profiling runs pick "
-                         "a subset): sweep, extra, fp8, rope, shared, tiny, achievable")
+                         "a subset): sweep, extra, fp8, rope, shared, shard, tiny, "
+                         "achievable")
     ap.add_argument("--profile", choices=WORKLOADS, default=None,
                     help="profiling aid: warm up and time one workload, nothing else")
     return ap.parse_args()
@@ -585,6 +586,48 @@ def split_sweep(args, log, splits=(1, 8, 16, 32, 64, 128)):
     return out
 
 
+def bench_shard(args, log):
+    """One GPU's share of the two decode workloads under 8-way tensor
+    parallelism by KV head: the same requests, contexts and block placement at
+    Hq 4 / Hkv 1 (an eighth of the heads and of the K/V bytes).  The long
+    single decode also at fixed split counts beside the heuristic's."""
+    import torch
+
+    from workloads import config_step
+    dev = torch.device("cuda:0")
+    res = []
+    for cfg in (2, 3):
+        step = config_step(cfg, device=dev, fill="zero", scale_down={"q_heads": 4, "kv_heads": 1})
+        wm = work_model(step)
+        kb, _ = decode_kernel_bytes(step)
+        pools = [(step.k_pool, step.v_pool)]
+        if cfg == 2:
+            for _ in range(args.replicas - 1):
+                pools.append((step.k_pool.clone(), step.v_pool.clone()))
+        rows = []
+        for S in ((0, 32, 64, 128) if cfg == 2 else (0,)):
+            runners = [StepRunner(step, dev, S, pools=pl, fused=True) for pl in pools]
+            n = len(runners) * (20 if cfg == 2 else 5)
+            ms, mode = time_steps(runners, n, len(runners), not args.eager, log,
+                                  per_graph=len(runners))
+            kt = kernel_times(runners, 20, log)
+            name = "decode_split_partial" if runners[0].splits > 1 else "decode"
+            gbs = kb / (kt[name]["avg_us"] * 1e-6) / 1e9
+            rows.append({"num_splits": runners[0].splits, "heuristic": S == 0,
+                         "us_per_step": round(ms * 1e3, 2), "launch": mode,
+                         "step_GBps": round(wm["bytes"] / (ms * 1e-3) / 1e9, 1),
+                         "decode_kernel_us": round(kt[name]["avg_us"], 2),
+                         "decode_kernel_GBps": round(gbs, 1),
+                         "decode_frac_hbm": round(gbs / PEAK_HBM_GBS, 4)})
+            log(f"shard config{cfg}: {json.dumps(rows[-1])}")
+            del runners
+        res.append({"workload": WORKLOAD_NAMES[cfg] + " -- TP8 shard (Hq 4 / Hkv 1)",
+                    "step_bytes": wm["bytes"], "runs": rows})
+        del pools, step
+        torch.cuda.empty_cache()
+    return res
+
+
 def achievable(log):
     """What plain library code reaches on this machine: a 1 GiB device copy
     (read + write bytes) and an 8192^3 bf16 GEMM through torch."""
@@ -862,6 +905,8 @@ def main():
             part["rope_kv_write"] = bench_rope(args, log)
         if "shared" in sec:
             part["shared_prefix"] = bench_shared_prefix(args, log)
+        if "shard" in sec:
+            part["tensor_parallel_shard"] = bench_shard(args, log)
         if "extra" in sec:
             part["extra_workloads"] = [bench_extra(c, args, log) for c in (3, 4, 5)]
         print(json.dumps(part, default=str), flush=True)
@@ -880,6 +925,7 @@ def main():
     fp8 = None
     rope = None
     shared = None
+    shard = None
     if not args.only_main:
         sec = set(x.strip() for x in args.sections.split(",") if x.strip())
         if "sweep" in sec:
@@ -894,6 +940,8 @@ def main():
             rope = bench_rope(args, log)
         if "shared" in sec:
             shared = bench_shared_prefix(args, log)
+        if "shard" in sec:
+            shard = bench_shard(args, log)
         if "tiny" in sec:
             cfg1 = bench_config1(args, log)
         if "achievable" in sec:
@@ -934,6 +982,7 @@ def main():
         "fp8_kv_cache": fp8,
         "rope_kv_write": rope,
         "shared_prefix": shared,
+        "tensor_parallel_shard": shard,
         "correctness_workload": cfg1,
         "achievable": ach,
     }

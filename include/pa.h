@@ -359,7 +359,9 @@ size_t pa_attention_workspace_size(int32_t num_seqs, int32_t num_tokens,
  * may have more new tokens than the decode kernel packs (max_query_len above
  * 16 / group size) or when num_seqs * num_kv_heads work units already fill
  * the device; otherwise enough splits to give every compute unit work,
- * bounded by PA_MAX_SPLITS and by the number of 16-token blocks.  num_cus <= 0
+ * bounded by 64 (the in-launch merge of more partials costs more than the
+ * extra work-groups gain), by PA_MAX_SPLITS and by the number of 16-token
+ * blocks (at least 8 per split).  num_cus <= 0
  * means "ask the current device".  Performance only: results do not depend on
  * it.
  */

@@ -114,6 +114,10 @@ def test_split_heuristic_crossover(lib):
     assert f(4, 8192, 8192, 32, 8, 256) == 1         # prefill rows present
     assert f(4098, 2048, 18432, 32, 8, 256) == 1
     assert f(1, 1, 64, 32, 8, 256) == 1              # too few blocks to split
+    # one KV head (a tensor-parallel shard): a split per CU would be 256, but
+    # the in-launch merge of that many partials costs more than it gains
+    assert f(1, 1, 32768, 4, 1, 256) == 64
+    assert f(1, 1, 4096, 4, 1, 256) == 32            # >= 8 blocks per split
     assert 1 < f(2, 1, 4096, 32, 8, 256) <= 256
     assert f(1, 4, 4096, 32, 8, 256) > 1             # 4 new tokens still pack (G = 4)
     assert f(1, 5, 4096, 32, 8, 256) == 1

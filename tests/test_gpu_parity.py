@@ -215,7 +215,7 @@ def test_split_sweep_small_decode(splits):
 
 
 @pytest.mark.parametrize("dtype,d", [("bf16", 64), ("bf16", 128), ("f32", 64), ("f32", 128)])
-@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4), (16, 4), (32, 4), (16, 1)])
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4), (16, 4), (32, 4), (16, 1), (4, 1)])
 def test_head_dims_and_groups(dtype, d, hq, hkv):
     # a prefill chunk with prior context, a decode, a 2-token and a 3-token
     # request, a fresh prefill, and an empty request
@@ -395,6 +395,19 @@ def test_full_config3():
     order = np.argsort(step.seq_lens)
     ids = sorted(set(order[:3].tolist() + order[-3:].tolist() + [7, 100, 200]))
     sampled_parity(step, ids)
+
+
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_full_tensor_parallel_shard(cfg):
+    # one GPU's share under 8-way tensor parallelism by KV head: Hq 4 / Hkv 1
+    # at the full contexts (config 2: 32768 keys, split by the heuristic)
+    step = config_step(cfg, device="cuda", scale_down={"q_heads": 4, "kv_heads": 1})
+    assert step.num_q_heads == 4 and step.num_kv_heads == 1
+    if cfg == 2:
+        sampled_parity(step, [0])
+    else:
+        order = np.argsort(step.seq_lens)
+        sampled_parity(step, sorted(set(order[:2].tolist() + order[-2:].tolist() + [50])))
 
 
 def test_full_config4():

@@ -305,7 +305,10 @@ def config_step(cfg: int, *, device="cpu", fill="nan", variant=None,
     ``variant="alt"`` for config 1 reads the decode contexts as prior tokens
     (seq_lens 6, 18, 65) instead of totals (5, 17, 64).  ``scale_down`` gives
     smaller versions of configs 3-5 with the same structure, for tests the CPU
-    oracle finishes in seconds: a dict of overrides (see below).
+    oracle finishes in seconds: a dict of overrides (see below).  For configs 2
+    and 3 it may also set ``q_heads`` / ``kv_heads``: with 4 / 1 the step is
+    one GPU's share of the workload under 8-way tensor parallelism by KV head
+    (same requests, contexts and block placement, one eighth of the heads).
     """
     seed = cfg
     rng = np.random.default_rng(seed)
@@ -327,8 +330,9 @@ def config_step(cfg: int, *, device="cpu", fill="nan", variant=None,
         need = -(-ctx // BLOCK)
         table = list(rng.permutation(pool)[:need])
         reqs = [Request(ctx - 1, 1, table)]
-        return build_step("config2", reqs, dtype="bf16", num_q_heads=32,
-                          num_kv_heads=8, head_dim=128, num_blocks=pool, seed=seed,
+        return build_step("config2", reqs, dtype="bf16", num_q_heads=sd.get("q_heads", 32),
+                          num_kv_heads=sd.get("kv_heads", 8), head_dim=128, num_blocks=pool,
+                          seed=seed,
                           device=device, fill=fill, stride=need,
                           with_values=with_values)
     if cfg == 3:
@@ -341,8 +345,9 @@ def config_step(cfg: int, *, device="cpu", fill="nan", variant=None,
         perm = rng.permutation(pool)
         tables, _ = _assign_tables(perm, need)
         reqs = [Request(int(c) - 1, 1, t) for c, t in zip(ctx, tables)]
-        return build_step("config3", reqs, dtype="bf16", num_q_heads=32,
-                          num_kv_heads=8, head_dim=128, num_blocks=pool, seed=seed,
+        return build_step("config3", reqs, dtype="bf16", num_q_heads=sd.get("q_heads", 32),
+                          num_kv_heads=sd.get("kv_heads", 8), head_dim=128, num_blocks=pool,
+                          seed=seed,
                           device=device, fill=fill, stride=-(-hi // BLOCK),
                           with_values=with_values)
     if cfg == 4:
