@@ -178,6 +178,7 @@ __global__ __launch_bounds__(256) void rope_kv_write_kernel(
   typedef typename Piece4<E>::T P4;
   constexpr int kPad = 16 / sizeof(E);
   __shared__ __align__(16) E vrow[kTok][128 + kPad];
+  __shared__ __align__(16) float scs[kTok][128];  // the tokens' cos | sin rows
   __shared__ int64_t sslot[kTok];
   __shared__ int spos[kTok];
   const int tid = threadIdx.x;
@@ -198,6 +199,16 @@ __global__ __launch_bounds__(256) void rope_kv_write_kernel(
     spos[tid] = p;
   }
   __syncthreads();
+  // each token's cos / sin row is read from the table once per work-group
+  // and serves its K row and the G query rows
+  for (int c = tid; c < kTok * (d / 4); c += 256) {
+    const int ti = c / (d / 4), part = c - ti * (d / 4);
+    const int p = spos[ti];
+    if (ti < ntok && p >= 0)
+      *reinterpret_cast<float4*>(&scs[ti][4 * part]) =
+          *reinterpret_cast<const float4*>(cos_sin + (size_t)p * d + 4 * part);
+  }
+  __syncthreads();
   const int half = d / 2, qpr = half / 4;  // 4-pair pieces per head row
   // K: rotate, write token-major into the cache
   for (int c = tid; c < kTok * qpr; c += 256) {
@@ -209,7 +220,7 @@ __global__ __launch_bounds__(256) void rope_kv_write_kernel(
     float lo[4], hi[4];
     Piece4<E>::get(*reinterpret_cast<const P4*>(key + src), lo);
     Piece4<E>::get(*reinterpret_cast<const P4*>(key + src + half), hi);
-    const float* row = cos_sin + (size_t)p * d + 4 * pc;
+    const float* row = &scs[ti][4 * pc];
     rotate4(lo, hi, *reinterpret_cast<const float4*>(row),
             *reinterpret_cast<const float4*>(row + half));
     if (s < 0) continue;
@@ -228,7 +239,7 @@ __global__ __launch_bounds__(256) void rope_kv_write_kernel(
     float lo[4], hi[4];
     Piece4<E>::get(*reinterpret_cast<const P4*>(qrow), lo);
     Piece4<E>::get(*reinterpret_cast<const P4*>(qrow + half), hi);
-    const float* row = cos_sin + (size_t)p * d + 4 * pc;
+    const float* row = &scs[ti][4 * pc];
     rotate4(lo, hi, *reinterpret_cast<const float4*>(row),
             *reinterpret_cast<const float4*>(row + half));
     *reinterpret_cast<P4*>(qrow) = Piece4<E>::put(lo);
