@@ -91,6 +91,18 @@ def test_config3_and_2_full_metadata():
     assert len(set(st2.block_tables[0].tolist())) == 2048
 
 
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_tensor_parallel_shard_keeps_requests_and_placement(cfg):
+    # one GPU's share at 8-way tensor parallelism: the heads change, nothing else
+    full = config_step(cfg, with_values=False)
+    shard = config_step(cfg, with_values=False, scale_down={"q_heads": 4, "kv_heads": 1})
+    assert (shard.num_q_heads, shard.num_kv_heads) == (4, 1)
+    assert shard.seq_lens.tolist() == full.seq_lens.tolist()
+    assert (shard.block_tables == full.block_tables).all()
+    assert list(shard.slot_mapping) == list(full.slot_mapping)
+    assert shard.num_blocks == full.num_blocks
+
+
 def test_extract_requests_preserves_rows():
     st = config_step(5, scale_down={"chunk": 40, "priors": (33, 70), "decodes": 24,
                                     "lo": 10, "hi": 200, "prefix": 32, "sharers": 6,
