@@ -304,13 +304,19 @@ __global__ __launch_bounds__(64 * NW, (PIPE == 2 && NW < 8 ? 8 / NW : 1)) void d
     }
   };
 
-  // Q as the B operand: lane (col, kg) holds d = 32*st + 8*kg .. +8
+  // Q as the B operand: lane (col, kg) holds d = kd(st) .. +8 with
+  // kd(st) = 32*st + 8*kg.  E4M3 cache: the head dimension is taken in the
+  // order kd(st) = 64*(st/2) + 16*kg + 8*(st%2) (a permutation of the
+  // dot product's terms, the same for K and Q), so that one 16-byte load
+  // gives a lane its K codes for two steps.
+  static_assert(!F8 || KSTEPS % 2 == 0, "E4M3 K loads cover two steps");
+  auto kd = [&](int st) { return F8 ? 64 * (st >> 1) + 16 * kg + 8 * (st & 1) : 32 * st + 8 * kg; };
   bf16x8 qf[KSTEPS];
   if (col_valid) {
     const uint16_t* qrow = p.q + ((size_t)(q0 + qi) * p.hq + kvh * G + g) * D;
 #pragma unroll
     for (int st = 0; st < KSTEPS; ++st)
-      qf[st] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 32 * st + 8 * kg));
+      qf[st] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + kd(st)));
   } else {
 #pragma unroll
     for (int st = 0; st < KSTEPS; ++st) qf[st] = as_bf16x8(make_uint4(0, 0, 0, 0));
@@ -325,7 +331,7 @@ __global__ __launch_bounds__(64 * NW, (PIPE == 2 && NW < 8 ? 8 / NW : 1)) void d
   const int rb = ra + 4;                       // second product
   const size_t head_elems = 16 * D;
   const size_t block_elems = (size_t)p.hkv * head_elems;
-  const CT* kbase = static_cast<const CT*>(p.kc) + kvh * head_elems + 8 * kg;
+  const CT* kbase = static_cast<const CT*>(p.kc) + kvh * head_elems + kd(0);
   const CT* vbase = static_cast<const CT*>(p.vc) + kvh * head_elems + col * 16 + 8 * (kg & 1);
   // E4M3 cache: a cached K value is code * k_scale, so the scale folds into
   // the score scale; V's scale multiplies the normalised output
@@ -367,10 +373,23 @@ __global__ __launch_bounds__(64 * NW, (PIPE == 2 && NW < 8 ? 8 / NW : 1)) void d
       if constexpr (PIPE == 2 && !F8) return load_stream16(reinterpret_cast<const uint4*>(ptr));
       else return *reinterpret_cast<const RT*>(ptr);
     };
+    if constexpr (F8) {
+      // 16 codes per load: steps 2t and 2t+1 (kd(2t + 1) = kd(2t) + 8)
 #pragma unroll
-    for (int st = 0; st < KSTEPS; ++st) {
-      f.a[st] = ld(ka + 32 * st);
-      f.b[st] = ld(kb + 32 * st);
+      for (int t = 0; t < KSTEPS / 2; ++t) {
+        const uint4 wa = *reinterpret_cast<const uint4*>(ka + 64 * t);
+        const uint4 wb = *reinterpret_cast<const uint4*>(kb + 64 * t);
+        f.a[2 * t] = make_uint2(wa.x, wa.y);
+        f.a[2 * t + 1] = make_uint2(wa.z, wa.w);
+        f.b[2 * t] = make_uint2(wb.x, wb.y);
+        f.b[2 * t + 1] = make_uint2(wb.z, wb.w);
+      }
+    } else {
+#pragma unroll
+      for (int st = 0; st < KSTEPS; ++st) {
+        f.a[st] = ld(ka + 32 * st);
+        f.b[st] = ld(kb + 32 * st);
+      }
     }
 #pragma unroll
     for (int db = 0; db < DB; ++db) f.v[db] = ld(vp + db * 256);
