@@ -1,7 +1,7 @@
 """GPU parity on random small batches (hypothesis, derandomized, bounded
 examples) and the decode and prefill kernels on the same rows.
 
-Each example draws a flat step -- 1 to 5 requests, each with 0 to 40 new
+Each example draws a flat step (also over an E4M3 cache) -- 1 to 5 requests, each with 0 to 40 new
 tokens on 0 to 200 tokens of prior context (so rows go to the decode or the
 matrix-core kernel, splits or not, blocks end anywhere), block placement a
 seeded permutation of a NaN-poisoned pool, group sizes 1 to 8, head dims 64
@@ -98,3 +98,24 @@ def test_decode_and_prefill_kernels_agree_on_the_same_row(dtype, d, hq, hkv, n):
     assert np.abs(a - b).max() <= TOL_OUT[dtype]
     la, lb = lse_a[-1].cpu().double().numpy(), lse_b[0].cpu().double().numpy()
     assert np.abs(la - rl[-1]).max() <= 1e-3 and np.abs(lb - rl[-1]).max() <= 1e-3
+
+
+@settings(max_examples=30, deadline=None, derandomize=True,
+          suppress_health_check=[HealthCheck.too_slow])
+@given(flat_step())
+def test_random_flat_steps_fp8_cache_match_oracle(case):
+    # the same random steps over an E4M3 cache (bf16 query): quantised write
+    # bit-exact, attention against the oracle over the dequantised pools
+    from test_gpu_fp8 import check as check8, oracle_attn, oracle_write, run_gpu as run_gpu8
+    from test_gpu_fp8 import same_codes
+    from workloads import fp8_cache
+    shapes, hq, hkv, d, _, splits, seed = case
+    step = fp8_cache(random_step(shapes, hq, hkv, d, "bf16", seed), seed % 1000)
+    print(f"fp8 case shapes={shapes} hq={hq} hkv={hkv} d={d} splits={splits} seed={seed}",
+          flush=True)
+    out, lse, g = run_gpu8(step, num_splits=splits)
+    kp, vp = oracle_write(step)
+    assert same_codes(g["k_pool"], kp) and same_codes(g["v_pool"], vp)
+    ro, rl = oracle_attn(step, kp, vp)
+    check8(step, out, lse, ro, rl, what=f"fp8 random {shapes} hq={hq} hkv={hkv} d={d}")
+
