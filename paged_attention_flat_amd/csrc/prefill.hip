@@ -228,8 +228,20 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
     if constexpr (CASC) pos[rg] = min(p.vpos[min(tokr[rg], q_len - 1)], seq_len - 1);
     else pos[rg] = ctx + min(tokr[rg], q_len - 1);
   }
-  // CASC: rows carry unrelated positions, so every tile is masked per row
-  const int wpos_lo = CASC ? -1 : ctx + min(tok0 + (WROWS * wave) / G, q_len - 1);
+  // smallest position among the wave's rows: a tile needs the per-row causal
+  // mask only where it reaches past it.  Rows are token-major, so the wave's
+  // first row has it; CASC rows carry unrelated positions: a wave minimum.
+  int wpos_lo;
+  if constexpr (CASC) {
+    int mn = pos[0];
+#pragma unroll
+    for (int rg = 1; rg < RG; ++rg) mn = min(mn, pos[rg]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mn = min(mn, __shfl_xor(mn, off, 64));
+    wpos_lo = mn;
+  } else {
+    wpos_lo = ctx + min(tok0 + (WROWS * wave) / G, q_len - 1);
+  }
   const int kend = CASC ? min(seq_len, kbeg + p.pre_chunk)
                         : ctx + min(tok0 + TQ, q_len);  // one past the last key
 
