@@ -117,15 +117,17 @@ WsLayout ws_layout(int32_t num_seqs, int32_t num_tokens, int32_t hq, int32_t d, 
   return w;
 }
 
-// Key ranges of the shared-prefix stage: enough work-groups for about two
-// per compute unit, each range a whole number of 64-key tiles.
+// Key ranges of the shared-prefix stage: enough work-groups for one per
+// compute unit (the matrix-core kernel's LDS admits one per CU, so a second
+// round only adds start-up, partial stores and partials for the decode
+// kernel to merge), each range a whole number of 64-key tiles.
 void cascade_key_split(int32_t num_pre_blocks, int64_t casc_rows, int32_t group, int32_t hkv,
                        int32_t num_cus, int32_t* ksplits, int32_t* kchunk) {
   const int64_t tq = prefill_tile_tokens(group);
   const int64_t tiles = std::max<int64_t>(1, (casc_rows + tq - 1) / tq);
   const int64_t units = tiles * hkv;
   const int64_t ktiles = std::max<int64_t>(1, (num_pre_blocks + 3) / 4);  // 64-key tiles
-  int64_t ks = std::max<int64_t>(1, (2 * (int64_t)num_cus + units - 1) / units);
+  int64_t ks = std::max<int64_t>(1, ((int64_t)num_cus + units - 1) / units);
   ks = std::min<int64_t>(ks, std::min<int64_t>(ktiles, 64));
   const int64_t per = (ktiles + ks - 1) / ks;                  // tiles per range
   *ksplits = (int32_t)((ktiles + per - 1) / per);              // no empty range
