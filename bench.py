@@ -393,16 +393,10 @@ class RopeRunner:
 
         import paged_attention_flat_amd as pa
         self.pa = pa
-        nt, hq, d = step.query.shape
-        qsl = step.query_start_loc
-        pos = torch.empty(nt, dtype=torch.int64)
-        for b in range(step.num_seqs):
-            n = int(qsl[b + 1] - qsl[b])
-            pos[int(qsl[b]):int(qsl[b + 1])] = int(step.seq_lens[b]) - n + torch.arange(n)
+        from workloads import rope_table, token_positions
+        pos = torch.as_tensor(token_positions(step))
         maxp = int(pos.max()) + 1
-        w = 10000.0 ** (-2.0 * torch.arange(d // 2, dtype=torch.float64) / d)
-        ang = torch.arange(maxp, dtype=torch.float64)[:, None] * w[None, :]
-        self.table = torch.cat([ang.cos(), ang.sin()], dim=1).to(torch.float32).to(dev)
+        self.table = torch.as_tensor(rope_table(maxp, step.head_dim)).to(dev)
         self.pos = pos.to(dev)
         self.sm = torch.as_tensor(step.slot_mapping).to(dev)
         self.q = step.query.to(dev).clone()

@@ -266,8 +266,9 @@ size_t pa_cascade_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t n
  *   key_cache[s / 16][h][s % 16][j] = e4m3(clamp(key[t][h][j] / k_scale[h]))
  * (and V dim-major), where the division is IEEE fp32 (key widened exactly
  * from bf16 or fp32, `dtype`), clamp is to [-448, 448] and e4m3() rounds to
- * the nearest code, ties to the even mantissa.  NaN inputs give a NaN code.
- * Negative or out-of-pool slots write nothing.  Errors as pa_kv_write.
+ * the nearest code, ties to the even mantissa; +-inf clamp to +-448.  Every
+ * NaN input, whatever its sign bit, gives the one code 0x7F.  Negative or
+ * out-of-pool slots write nothing.  Errors as pa_kv_write.
  */
 pa_status pa_kv_write_fp8(const void* key, const void* value,
                           void* key_cache, void* value_cache,

@@ -44,7 +44,7 @@ from .paged_attention import (  # noqa: F401
     combine_partials,
     attention_cascade,
 )
-from .rope import rope_table, rope, round_to, rope_kv_write  # noqa: F401
+from .rope import rope, round_to, rope_kv_write  # noqa: F401
 from .fp8 import (  # noqa: F401
     E4M3_MAX,
     e4m3_decode,

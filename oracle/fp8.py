@@ -14,7 +14,8 @@ for K and one for V: a cached value stands for code * scale.
 Quantisation (the KV write): y = float32(x) / scale[h] in float32 (IEEE
 division, as the kernel computes it, since the float decides the code), then
 y is clamped to [-448, 448] and rounded to the nearest E4M3 value, ties to the
-even mantissa.  NaN encodes as 0x7F.
+even mantissa.  Every NaN, whatever its sign bit, encodes as 0x7F (the pages
+fix no NaN code; one canonical code keeps the write deterministic).
 """
 
 from __future__ import annotations

@@ -57,42 +57,46 @@ def flatten_schedule(schedule, block_size: int = BLOCK_SIZE) -> dict:
     """Build the flat tensors of one step from a schedule.
 
     ``schedule`` is a list of ``(done, n, table)``: tokens already computed,
-    tokens scheduled this step, and the request's physical block ids.  The
-    page's table of flat tensors defines each output:
+    tokens scheduled this step, and the request's physical block ids.  Each
+    output is the page's definition of that flat tensor, evaluated over all
+    rows at once:
 
-    * positions: each new token's position in its own sequence, done..done+n-1
-    * query_start_loc: where each request's tokens start (cumulative counts)
+    * query_start_loc: cumulative token counts, starting at 0
+    * request_index: the request a flat row belongs to (its count repeated)
+    * positions: done of the row's request plus the row's offset inside it
     * seq_lens: total context after the step, done + n
-    * slot_mapping: block_id * block_size + offset for the block that holds the
-      position
-    * logits_indices: the last flat row of each request
+    * slot_mapping: block_id * block_size + offset, block_id the table entry of
+      the block holding the position
+    * logits_indices: the last flat row of each request (next start - 1)
     """
-    positions, slots, request_index = [], [], []
-    query_start_loc = [0]
-    seq_lens = []
-    for r, (done, n, table) in enumerate(schedule):
-        for pos in range(done, done + n):
-            positions.append(pos)
-            block_id = table[pos // block_size]
-            slots.append(block_id * block_size + pos % block_size)
-            request_index.append(r)
-        query_start_loc.append(query_start_loc[-1] + n)
-        seq_lens.append(done + n)
-    logits_indices = [q - 1 for q in query_start_loc[1:]]
+    done = np.array([int(s[0]) for s in schedule], dtype=np.int64)
+    count = np.array([int(s[1]) for s in schedule], dtype=np.int64)
+    qsl = np.concatenate([[0], np.cumsum(count)]).astype(np.int64)
+    req = np.repeat(np.arange(len(schedule), dtype=np.int64), count)
+    offset = np.arange(int(qsl[-1]), dtype=np.int64) - qsl[req]
+    pos = done[req] + offset
+    block_id = np.array([int(schedule[r][2][p // block_size]) for r, p in zip(req, pos)],
+                        dtype=np.int64)
+    slots = block_id * block_size + pos % block_size
     return {
-        "request_index": request_index,
-        "positions": positions,
-        "query_start_loc": query_start_loc,
-        "seq_lens": seq_lens,
-        "slot_mapping": slots,
-        "logits_indices": logits_indices,
+        "request_index": req.tolist(),
+        "positions": pos.tolist(),
+        "query_start_loc": qsl.tolist(),
+        "seq_lens": (done + count).tolist(),
+        "slot_mapping": slots.tolist(),
+        "logits_indices": (qsl[1:] - 1).tolist(),
     }
 
 
 def capture_sizes(top: int = 512) -> list:
-    """Capture-size ladder of the same page: 1, 2, 4, then steps of 8 below 256,
-    then steps of 16 up to ``top``."""
-    return [1, 2, 4] + list(range(8, 256, 8)) + list(range(256, top + 1, 16))
+    """Capture-size ladder of the same page, from its stated rule: 1, 2 and 4,
+    then every multiple of 8 below 256, then every multiple of 16 from 256 up
+    to ``top``."""
+    def on_ladder(n: int) -> bool:
+        if n < 8:
+            return n in (1, 2, 4)
+        return n % (8 if n < 256 else 16) == 0
+    return [n for n in range(1, top + 1) if on_ladder(n)]
 
 
 def validate_step(query_start_loc, seq_lens, block_tables, slot_mapping,
@@ -344,19 +348,22 @@ def combine_partials(partial_out, partial_lse):
     """Merge split partials into the unsplit result.
 
     With M = max_s lse_s: LSE = M + ln sum_s e^(lse_s - M) and
-    o = sum_s e^(lse_s - LSE) o_s.  Splits with lse_s = -inf weigh 0.
-    Entries whose every split is -inf (no visible key anywhere) give NaN.
+    o = sum_s e^(lse_s - LSE) o_s.  Splits with lse_s = -inf weigh 0 (their
+    o_s is never read).  An entry whose every split is -inf saw no key at
+    all: its sum is empty, so LSE = ln 0 = -inf, and o (0 / 0) is NaN.
     """
     po = np.asarray(partial_out, dtype=np.float64)
     pl = np.asarray(partial_lse, dtype=np.float64)
-    M = pl.max(axis=0)
-    with np.errstate(invalid="ignore"):
-        w = np.exp(pl - M[None])
-        LSE = M + np.log(w.sum(axis=0))
-        coef = np.exp(pl - LSE[None])
-    coef = np.where(np.isneginf(pl), 0.0, coef)
-    out = (coef[..., None] * np.where(np.isneginf(pl)[..., None], 0.0, po)).sum(axis=0)
-    out = np.where(np.isfinite(LSE)[..., None], out, np.nan)
+    empty = np.isneginf(pl)
+    none = empty.all(axis=0)                       # no split saw a key
+    M = np.where(none, 0.0, pl.max(axis=0))        # finite reference for the sums
+    w = np.where(empty, 0.0, np.exp(np.where(empty, 0.0, pl) - M[None]))
+    total = w.sum(axis=0)
+    with np.errstate(divide="ignore"):
+        LSE = np.where(none, -np.inf, M + np.log(np.where(none, 1.0, total)))
+    coef = w / np.where(none, 1.0, total)[None]
+    out = (coef[..., None] * np.where(empty[..., None], 0.0, po)).sum(axis=0)
+    out = np.where(none[..., None], np.nan, out)
     return out, LSE
 
 

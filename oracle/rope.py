@@ -14,8 +14,8 @@ form a pair rotated by the angle of (position, i):
 
 with cos / sin read from a caller-supplied float32 table [max_position, d]
 (row p: cos of the d/2 angles, then their sin), so both sides use identical
-angles.  The usual table (``rope_table``) has angle p * base^(-2i/d).  The
-fused step rotates every query head and the new keys, then writes the
+angles.  The table is an input (the seeded generators build the usual one,
+angle p * base^(-2i/d)); the oracle only reads it.  The fused step rotates every query head and the new keys, then writes the
 rotated K and the unrotated V through slot_mapping; tokens whose position
 falls outside the table are left alone (no rotation, nothing written).
 """
@@ -25,14 +25,6 @@ from __future__ import annotations
 import numpy as np
 
 from .paged_attention import BLOCK_SIZE, to_f64
-
-
-def rope_table(max_position: int, head_dim: int, base: float = 10000.0) -> np.ndarray:
-    """float32 [max_position, head_dim]: cos(p * w_i) for i < d/2, then sin."""
-    half = head_dim // 2
-    w = base ** (-2.0 * np.arange(half, dtype=np.float64) / head_dim)
-    ang = np.arange(max_position, dtype=np.float64)[:, None] * w[None, :]
-    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
 
 
 def rope(x, positions, table, dtype: str) -> np.ndarray:

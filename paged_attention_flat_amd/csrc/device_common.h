@@ -54,16 +54,27 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint2 v) {
 
 // E4M3 codes of four values already divided by their scale: clamped to the
 // largest finite magnitude (448; the conversion gives NaN past it), then
-// rounded to nearest even by the hardware conversion.  NaN stays NaN.
+// rounded to nearest even by the hardware conversion.  Every NaN, whatever
+// its sign, encodes as the one code 0x7F (the test is on the bits, so it
+// holds in translation units built without NaN semantics).
 __device__ __forceinline__ float e4m3_sat(float y) {
   return y > 448.f ? 448.f : (y < -448.f ? -448.f : y);
+}
+__device__ __forceinline__ bool is_nan_bits(float y) {
+  return (__float_as_uint(y) & 0x7fffffffu) > 0x7f800000u;
 }
 __device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_sat(a), e4m3_sat(b), 0, false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_sat(c), e4m3_sat(d), w, true);
-  return (uint32_t)w;
+  uint32_t u = (uint32_t)w;
+  if (is_nan_bits(a)) u = (u & 0xffffff00u) | 0x0000007fu;
+  if (is_nan_bits(b)) u = (u & 0xffff00ffu) | 0x00007f00u;
+  if (is_nan_bits(c)) u = (u & 0xff00ffffu) | 0x007f0000u;
+  if (is_nan_bits(d)) u = (u & 0x00ffffffu) | 0x7f000000u;
+  return u;
 }
 __device__ __forceinline__ uint8_t e4m3_code(float y) {
+  if (is_nan_bits(y)) return 0x7f;
   return (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_sat(y), 0.f, 0, false) & 0xff);
 }
 

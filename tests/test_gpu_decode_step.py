@@ -36,9 +36,12 @@ def run_step(step, num_splits=0):
     return out, lse, g
 
 
-def check_all(step, out, lse, g, what):
-    kp, vp = oracle.kv_write(raw_numpy(step.key), raw_numpy(step.value), raw_numpy(step.k_pool),
-                             raw_numpy(step.v_pool), step.slot_mapping)
+def check_all(step, out, lse, g, what, before=None):
+    # `before`: host copies of the pools taken before the call (needed when
+    # the step lives on the GPU, where the call writes the step's own pools)
+    kb, vb = before if before is not None else (raw_numpy(step.k_pool), raw_numpy(step.v_pool))
+    kp, vp = oracle.kv_write(raw_numpy(step.key), raw_numpy(step.value), kb, vb,
+                             step.slot_mapping)
     for got, ref in ((g["k_pool"], kp), (g["v_pool"], vp)):
         gb = np.ascontiguousarray(raw_numpy(got)).view(np.uint8)
         assert np.array_equal(gb, np.ascontiguousarray(ref).view(np.uint8)), f"{what}: pool"
@@ -114,3 +117,80 @@ def test_decode_step_falls_back_for_prefill_rows_and_fp32():
     step1 = config_step(1)
     out, lse, g = run_step(step1)
     check_all(step1, out, lse, g, "fp32 step (two calls)")
+
+
+@pytest.mark.parametrize("splits", [0, 1])
+def test_full_config2_decode_step(splits):
+    # the headline workload in the launch the benchmark times: one call, the
+    # new token written inside the decode launch, 32768 keys, the heuristic
+    # split count (0) and no split (1).  Whole pools byte-compared, the row
+    # against the oracle.
+    step = config_step(2, device="cuda")
+    before = (raw_numpy(step.k_pool), raw_numpy(step.v_pool))
+    out, lse, g = run_step(step, splits)
+    assert g["k_pool"].data_ptr() == step.k_pool.data_ptr()   # written in place
+    check_all(step, out, lse, g, f"full config2 decode step S={splits}", before)
+
+
+def test_full_config5_decode_step_pools():
+    # the mixed step (prefill chunks + 4096 decodes, 65 GB of pools) through
+    # the one call the benchmark times: every block holding a new token is
+    # compared with the oracle's write of that block, and every other block
+    # of both pools must keep its bytes (compared on the device against a
+    # copy taken before the call)
+    step = config_step(5, device="cuda")
+    sm = step.slot_mapping
+    blocks = np.unique(sm[sm >= 0] // 16)
+    bidx = torch.as_tensor(blocks).to("cuda")
+    k_before = {n: getattr(step, n).view(torch.int16).clone() for n in ("k_pool", "v_pool")}
+    k_sel = {n: raw_numpy(getattr(step, n)[bidx]) for n in ("k_pool", "v_pool")}
+    out, lse, g = run_step(step, 0)
+    # the written blocks: the oracle's write applied to their old contents
+    remap = {int(b): i for i, b in enumerate(blocks)}
+    local = np.array([remap[int(s) // 16] * 16 + int(s) % 16 if s >= 0 else -1 for s in sm])
+    kp, vp = oracle.kv_write(raw_numpy(step.key), raw_numpy(step.value), k_sel["k_pool"],
+                             k_sel["v_pool"], local)
+    for name, ref in (("k_pool", kp), ("v_pool", vp)):
+        got = raw_numpy(g[name][bidx])
+        assert np.array_equal(np.ascontiguousarray(got).view(np.uint8),
+                              np.ascontiguousarray(ref).view(np.uint8)), name
+        keep = torch.ones(g[name].shape[0], dtype=torch.bool, device="cuda")
+        keep[bidx] = False
+        after = g[name].view(torch.int16)
+        assert torch.equal(after[keep], k_before[name][keep]), f"{name}: other blocks changed"
+    del k_before
+
+
+def check_pools(step, g, before, what):
+    kp, vp = oracle.kv_write(raw_numpy(step.key), raw_numpy(step.value), before[0], before[1],
+                             step.slot_mapping)
+    for got, ref, name in ((g["k_pool"], kp, "K"), (g["v_pool"], vp, "V")):
+        gb = np.ascontiguousarray(raw_numpy(got)).view(np.uint8)
+        assert np.array_equal(gb, np.ascontiguousarray(ref).view(np.uint8)), f"{what}: {name} pool"
+    return kp, vp
+
+
+def test_full_config4_step():
+    # the long prefill step (4 x 8192 new tokens) through the one call the
+    # benchmark times: both 128 MB pools byte-compared with the oracle's
+    # write, then a seeded sample of rows (first, last and 40 random rows of
+    # each request) against the oracle's attention over its own pools
+    step = config_step(4, device="cuda")
+    before = (raw_numpy(step.k_pool), raw_numpy(step.v_pool))
+    out, lse, g = run_step(step, 0)
+    kp, vp = check_pools(step, g, before, "full config4")
+    rng = np.random.default_rng(404)
+    qsl = step.query_start_loc
+    rows = []
+    for b in range(step.num_seqs):
+        lo, hi = int(qsl[b]), int(qsl[b + 1])
+        rows += [lo, hi - 1] + rng.integers(lo, hi, 40).tolist()
+    rows = sorted(set(rows))
+    ro, rl = oracle.attention(raw_numpy(step.query), kp, vp, step.query_start_loc,
+                              step.seq_lens, step.block_tables, step.scale, step.num_kv_heads,
+                              step.dtype, rows=rows)
+    o = out.float().cpu().double().numpy()[rows]
+    assert np.isfinite(o).all()
+    assert float(np.abs(o - ro[rows]).max()) <= 2e-2
+    assert float(np.linalg.norm(o - ro[rows]) / np.linalg.norm(ro[rows])) <= 2e-2
+    assert float(np.abs(lse.cpu().double().numpy()[rows] - rl[rows]).max()) <= 1e-3

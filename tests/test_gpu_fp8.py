@@ -233,3 +233,59 @@ def test_fp8_decode_step_tokens_across_blocks():
         assert same_codes(g["k_pool"], kp) and same_codes(g["v_pool"], vp)
         ro, rl = oracle_attn(step, kp, vp)
         check(step, out, lse, ro, rl, what=f"fp8 straddle S={splits}")
+
+
+@pytest.mark.parametrize("splits", [0, 1])
+def test_fp8_full_long_decode_step(splits):
+    # the FP8 headline step in the launch the benchmark times: one call,
+    # the new token quantised and written inside the decode launch, at the
+    # heuristic split count (0) and without a split (1)
+    step = fp8_cache(config_step(2), 2)
+    out, lse, g = run_step_fp8(step, splits)
+    kp, vp = oracle_write(step)
+    assert same_codes(g["k_pool"], kp) and same_codes(g["v_pool"], vp)
+    ro, rl = oracle_attn(step, kp, vp)
+    check(step, out, lse, ro, rl, what=f"fp8 full long decode step S={splits}")
+
+
+NAN_BITS = {"bf16": [0x7FC0, 0xFFC0, 0x7F81, 0xFFFF],
+            "f32": [0x7FC00000, 0xFFC00000, 0x7F800001, 0xFFFFFFFF]}
+
+
+@pytest.mark.parametrize("path,dtype", [("write", "bf16"), ("write", "f32"), ("step", "bf16")])
+def test_fp8_nan_inputs_encode_canonically(path, dtype):
+    # NaN of either sign and several payloads in live tokens' K and V: the
+    # quantising write (alone, or inside the decode launch) gives code 0x7F
+    # for every one of them, as the oracle does; all other codes bit-exact
+    reqs = [Request(20, 1, [3, 0]), Request(47, 1, [1, 6, 2, 5]), Request(5, 1, [4])]
+    step = build_step("nan8", reqs, dtype=dtype, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                      num_blocks=8, seed=55)
+    step = fp8_cache(step, 55)
+    ibits = torch.int16 if dtype == "bf16" else torch.int32
+    nan = [b - (1 << 16) if dtype == "bf16" and b >= 1 << 15 else
+           (b - (1 << 32) if dtype == "f32" and b >= 1 << 31 else b) for b in NAN_BITS[dtype]]
+    k = step.key.clone()
+    v = step.value.clone()
+    kb, vb = k.view(ibits), v.view(ibits)
+    for t in range(3):
+        for j, bits in enumerate(nan):
+            kb[t, t % 2, 5 + 31 * j] = bits
+            vb[t, (t + 1) % 2, 3 + 29 * j] = bits
+    step.key, step.value = k, v
+    if path == "write":
+        import paged_attention_flat_amd as pa
+        g = upload(step)
+        pa.kv_write_fp8(g["key"], g["value"], g["k_pool"], g["v_pool"], g["slots"],
+                        g["k_scale"], g["v_scale"])
+        torch.cuda.synchronize()
+    else:
+        _, _, g = run_step_fp8(step, 0)
+    kp, vp = oracle_write(step)
+    assert same_codes(g["k_pool"], kp) and same_codes(g["v_pool"], vp)
+    kc, vc = g["k_pool"].cpu().numpy(), g["v_pool"].cpu().numpy()
+    for t in range(3):
+        s = int(step.slot_mapping[t])
+        blk, off = divmod(s, 16)
+        for j in range(4):
+            assert kc[blk, t % 2, off, 5 + 31 * j] == 0x7F
+            assert vc[blk, (t + 1) % 2, 3 + 29 * j, off] == 0x7F

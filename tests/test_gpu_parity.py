@@ -348,11 +348,16 @@ def test_split_combine_entry_point(dtype, d):
     torch.cuda.synchronize()
     ro, rl = oracle.combine_partials(po.astype(np.float64), pl.astype(np.float64))
     o = to64(out)
-    mask = np.isfinite(rl)
+    lg = lse.cpu().numpy().astype(np.float64)
     tol = 2e-2 if dtype == torch.bfloat16 else 1e-5
-    assert np.abs(o[mask] - ro[mask]).max() <= tol
-    assert np.abs(lse.cpu().numpy()[mask] - rl[mask]).max() <= 1e-4
-    assert np.isnan(o[2, 3]).all() and np.isneginf(lse.cpu().numpy()[2, 3])
+    # every entry, the one with no key included (oracle: out NaN, lse -inf)
+    assert np.array_equal(np.isnan(o), np.isnan(ro))
+    assert np.array_equal(np.isneginf(lg), np.isneginf(rl))
+    fin = ~np.isnan(ro)
+    assert np.abs(o[fin] - ro[fin]).max() <= tol
+    fl = np.isfinite(rl)
+    assert np.abs(lg[fl] - rl[fl]).max() <= 1e-4
+    assert np.isnan(ro[2, 3]).all() and np.isneginf(rl[2, 3])
 
 
 # ----------------------------------------------------------------------------

@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import oracle
-from workloads import Request, build_step, config_step, raw_numpy
+from workloads import Request, build_step, config_step, raw_numpy, rope_table, token_positions
 
 pytestmark = pytest.mark.gpu
 
@@ -64,7 +64,7 @@ def run(step, max_pos, table_np):
 
 def rotated_positions_case(step, positions, max_pos):
     step.info["positions"] = positions
-    table = oracle.rope_table(max_pos, step.head_dim)
+    table = rope_table(max_pos, step.head_dim)
     q, kc, vc = run(step, max_pos, table)
     qr, kp, vp = oracle.rope_kv_write(raw_numpy(step.query), raw_numpy(step.key),
                                       raw_numpy(step.value), raw_numpy(step.k_pool),
@@ -144,3 +144,45 @@ def test_rope_dtypes_and_out_of_table_positions(dtype, d):
             old = raw_numpy(step.k_pool)[b, :, o, :]
             assert np.array_equal(np.ascontiguousarray(kg[b, :, o, :]).view(np.uint8),
                                   np.ascontiguousarray(old).view(np.uint8))
+
+
+def test_rope_kv_write_full_long_prefill_step():
+    # the workload the benchmark times: all 4 x 8192 new tokens of the long
+    # prefill step rotated and written in one launch.  Every rotated key and
+    # a seeded sample of 2048 query tokens against the oracle; V and every
+    # byte the write must not touch bit-exact over the whole pools.
+    import paged_attention_flat_amd as pa
+    step = config_step(4, device="cuda")
+    pos = token_positions(step)
+    maxp = int(pos.max()) + 1
+    table = rope_table(maxp, step.head_dim)
+    dev = "cuda"
+    q = step.query.clone()
+    kc, vc = step.k_pool.clone(), step.v_pool.clone()
+    pa.rope_kv_write(q, step.key, step.value, kc, vc, torch.as_tensor(step.slot_mapping).to(dev),
+                     torch.as_tensor(pos).to(dev), torch.as_tensor(table).to(dev))
+    torch.cuda.synchronize()
+    key = raw_numpy(step.key)
+    krot = oracle.rope(key, pos, table, step.dtype)            # [Nt, Hkv, d] float64
+    kg = raw_numpy(kc)
+    sm = step.slot_mapping
+    live = sm >= 0
+    blk, off = sm[live] // 16, sm[live] % 16
+    check_rotated(kg[blk, :, off, :], krot[live], step.dtype, "full long prefill keys")
+    # everything but the written key rows keeps the old bytes
+    written = np.zeros((kg.shape[0], 16), dtype=bool)
+    written[blk, off] = True
+    kold = raw_numpy(step.k_pool)
+    keep = ~np.broadcast_to(written[:, None, :, None], kg.shape)
+    assert np.array_equal(kg[keep], kold[keep])
+    # V: the plain write, whole pool
+    _, vp = oracle.kv_write(key, raw_numpy(step.value), kold, raw_numpy(step.v_pool), sm)
+    assert np.array_equal(np.ascontiguousarray(raw_numpy(vc)).view(np.uint8),
+                          np.ascontiguousarray(vp).view(np.uint8))
+    rng = np.random.default_rng(44)
+    pick = np.unique(np.concatenate([[0, step.num_tokens - 1],
+                                     rng.integers(0, step.num_tokens, 2048)]))
+    qg = raw_numpy(q[torch.as_tensor(pick).to(dev)])
+    qr = oracle.rope(raw_numpy(step.query[torch.as_tensor(pick).to(dev)]), pos[pick], table,
+                     step.dtype)
+    check_rotated(qg, qr, step.dtype, "full long prefill queries (sampled)")

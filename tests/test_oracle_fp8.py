@@ -78,7 +78,10 @@ def test_encode_matches_exhaustive_nearest_search():
 def test_encode_special_values():
     e = oracle.e4m3_encode
     assert list(e([1e9, -1e9, 448.0, 464.0, 500.0])) == [0x7E, 0xFE, 0x7E, 0x7E, 0x7E]
-    assert e([np.nan])[0] == 0x7F
+    # every NaN -- either sign bit, any payload -- is the one code 0x7F
+    nans = np.array([0x7FC00000, 0xFFC00000, 0x7F800001, 0xFFFFFFFF], dtype=np.uint32)
+    assert list(e(nans.view(np.float32).astype(np.float64))) == [0x7F] * 4
+    assert list(e([np.inf, -np.inf])) == [0x7E, 0xFE]
     assert e([0.0])[0] == 0x00 and e([-0.0])[0] == 0x80
     # ties to even: 1.0625 -> 1.0 (mantissa 0), 1.1875 -> 1.25 (mantissa 2)
     assert list(e([1.0625, 1.1875, 2.0 ** -10, 3 * 2.0 ** -10])) == [0x38, 0x3A, 0x00, 0x02]

@@ -418,6 +418,20 @@ def test_combine_against_direct_weights():
     assert abs(lse[0, 0] - math.log(4.0)) < 1e-15
 
 
+def test_combine_empty_entries():
+    # an entry with one non-empty split is that split; an entry with none saw
+    # no key: the sum over splits is empty, so lse = ln 0 = -inf and o = 0/0
+    po = np.array([[[[1.0, 2.0]], [[5.0, 6.0]]],
+                   [[[np.nan, np.nan]], [[np.nan, np.nan]]],
+                   [[[7.0, -8.0]], [[np.inf, np.nan]]]])       # [S=3, Nt=2, Hq=1, d=2]
+    pl = np.array([[[-np.inf], [-np.inf]],
+                   [[-np.inf], [-np.inf]],
+                   [[0.75], [-np.inf]]])                        # [S=3, Nt=2, Hq=1]
+    out, lse = oracle.combine_partials(po, pl)
+    assert np.array_equal(out[0, 0], [7.0, -8.0]) and lse[0, 0] == 0.75
+    assert np.isneginf(lse[1, 0]) and np.isnan(out[1, 0]).all()
+
+
 def test_block_permutation_invariance():
     rng = np.random.default_rng(23)
     st = tiny_step(rng, [(33, 1), (0, 20), (5, 3)], 4, 2, 8, "bf16")

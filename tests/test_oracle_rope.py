@@ -14,17 +14,18 @@ import numpy as np
 import torch
 
 import oracle
+from workloads import rope_table
 
 
 def test_position_zero_is_identity():
-    tab = oracle.rope_table(4, 8)
+    tab = rope_table(4, 8)
     x = np.random.default_rng(0).normal(size=(3, 2, 8)).astype(np.float32)
     assert np.array_equal(oracle.rope(x, [0, 0, 0], tab, "f32"), x.astype(np.float64))
 
 
 def test_pair_norms_are_kept():
     rng = np.random.default_rng(1)
-    tab = oracle.rope_table(5000, 64)
+    tab = rope_table(5000, 64)
     x = rng.normal(size=(20, 3, 64)).astype(np.float32)
     pos = rng.integers(0, 5000, 20)
     y = oracle.rope(x, pos, tab, "f32")
@@ -35,7 +36,7 @@ def test_pair_norms_are_kept():
 
 def test_scores_depend_on_distance_only():
     rng = np.random.default_rng(2)
-    tab = oracle.rope_table(3000, 32)
+    tab = rope_table(3000, 32)
     q = rng.normal(size=(1, 1, 32)).astype(np.float32)
     k = rng.normal(size=(1, 1, 32)).astype(np.float32)
     s = [float(np.sum(oracle.rope(q, [m + t], tab, "f32") * oracle.rope(k, [n + t], tab, "f32")))
@@ -44,7 +45,7 @@ def test_scores_depend_on_distance_only():
 
 
 def test_unit_frequency_pair_traces_the_circle():
-    tab = oracle.rope_table(100, 2)          # one pair, angle p * 1
+    tab = rope_table(100, 2)          # one pair, angle p * 1
     x = np.array([[[1.0, 0.0]]], dtype=np.float32)
     for p in (1, 7, 99):
         y = oracle.rope(x, [p], tab, "f32")[0, 0]
@@ -52,7 +53,7 @@ def test_unit_frequency_pair_traces_the_circle():
 
 
 def test_pairing_is_half_split():
-    tab = oracle.rope_table(10, 4)
+    tab = rope_table(10, 4)
     e1 = np.array([[[0.0, 1.0, 0.0, 0.0]]], dtype=np.float32)
     y = oracle.rope(e1, [3], tab, "f32")[0, 0]
     # dim 1 pairs with dim 3 (half split), never with dim 0 (interleaved)
@@ -72,7 +73,7 @@ def test_bf16_rounding_matches_torch():
 def test_rope_kv_write_brute_force():
     rng = np.random.default_rng(4)
     nt, hq, hkv, d, nb = 6, 4, 2, 8, 3
-    tab = oracle.rope_table(40, d)
+    tab = rope_table(40, d)
     bits = lambda a: torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     q = bits(rng.normal(size=(nt, hq, d)).astype(np.float32))
     k = bits(rng.normal(size=(nt, hkv, d)).astype(np.float32))
@@ -101,3 +102,14 @@ def test_rope_kv_write_brute_force():
         if not ok:
             assert np.array_equal(qr[t], oracle.to_f64(q[t], "bf16"))
     assert np.array_equal(kq, ek) and np.array_equal(vq, ev)
+
+
+def test_rope_table_frequencies():
+    # the input table's angles p * 10000^(-2i/d): at d = 128 pair 16 turns by
+    # 10000^(-1/4) = 1/10 per position and pair 32 by 10000^(-1/2) = 1/100,
+    # pair 0 by 1; the last pair by 10000^(-63/64)
+    tab = rope_table(2000, 128).astype(np.float64)
+    p = np.arange(2000)
+    for i, w in ((0, 1.0), (16, 0.1), (32, 0.01), (63, 10000.0 ** (-63 / 64))):
+        assert np.abs(tab[:, i] - np.cos(w * p)).max() < 1e-6, i
+        assert np.abs(tab[:, 64 + i] - np.sin(w * p)).max() < 1e-6, i

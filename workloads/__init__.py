@@ -18,4 +18,6 @@ from .gen import (  # noqa: F401
     unique_block_count,
     fp8_cache,
     shared_prefix_step,
+    token_positions,
+    rope_table,
 )

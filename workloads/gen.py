@@ -455,3 +455,25 @@ def extract_requests(step: StepInputs, req_ids, device="cpu") -> tuple:
         v_pool=step.v_pool[idx_blocks.to(src_dev)].to(device),
         info=dict(step.info))
     return small, np.asarray(rows, dtype=np.int64)
+
+
+def token_positions(step: StepInputs) -> np.ndarray:
+    """Position of every flat token in its own sequence ("Model execution",
+    "Flattening a step": context before the step plus the row's offset);
+    -1 for padded tokens."""
+    pos = np.full(step.num_tokens, -1, dtype=np.int64)
+    qsl = step.query_start_loc.astype(np.int64)
+    for b in range(step.num_seqs):
+        n = int(qsl[b + 1] - qsl[b])
+        pos[qsl[b]: qsl[b + 1]] = int(step.seq_lens[b]) - n + np.arange(n)
+    return pos
+
+
+def rope_table(max_position: int, head_dim: int, base: float = 10000.0) -> np.ndarray:
+    """The usual rotary table, an input of the fused rotary write: float32
+    [max_position, head_dim], row p = cos(p * w_i) for i < d/2, then
+    sin(p * w_i), with w_i = base^(-2i/d)."""
+    half = head_dim // 2
+    w = base ** (-2.0 * np.arange(half, dtype=np.float64) / head_dim)
+    ang = np.arange(max_position, dtype=np.float64)[:, None] * w[None, :]
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
