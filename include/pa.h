@@ -207,6 +207,34 @@ pa_status pa_decode_step(const void* key, const void* value, void* key_cache, vo
                          size_t workspace_bytes, pa_dtype dtype, void* stream);
 
 /*
+ * pa_decode_step_noalloc -- pa_decode_step for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid hipMalloc.  Arguments, results and errors are those
+ * of pa_decode_step without the workspace: the step's workspace is a
+ * library-owned device array of PA_NOALLOC_SCRATCH_BYTES per GPU (each GPU
+ * the library runs on keeps its own copy until the process ends).  A step
+ * whose workspace (pa_attention_workspace_size at the split count used: the
+ * heuristic's when num_splits is 0) exceeds that size returns
+ * PA_ERR_WORKSPACE before anything is enqueued.  The call allocates and
+ * frees nothing; its first call on a device looks the array up and clears
+ * it on `stream`.  Every call on one GPU shares that GPU's array, so calls
+ * that overlap on one GPU (different streams, or different host threads,
+ * without ordering between them) race and give undefined results; calls
+ * ordered on one stream are safe.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (16u << 20)
+pa_status pa_decode_step_noalloc(const void* key, const void* value, void* key_cache,
+                                 void* value_cache, const int64_t* slot_mapping,
+                                 const void* query, const int32_t* query_start_loc,
+                                 const int32_t* seq_lens, const int32_t* block_tables,
+                                 int32_t num_seqs, int32_t num_tokens, int32_t max_query_len,
+                                 int32_t max_seq_len, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                 int32_t block_table_stride, int64_t num_blocks, float scale,
+                                 int32_t num_splits, void* out, float* lse, pa_dtype dtype,
+                                 void* stream);
+
+/*
  * pa_attention_fwd_cascade -- pa_attention_fwd (bf16) with a shared prefix
  * read once.  Block tables may point several requests at the same physical
  * blocks ("Model execution", "Flattening a step"; prefix caching in "Anatomy

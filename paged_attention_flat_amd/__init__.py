@@ -25,7 +25,7 @@ __all__ = [
     "PaError", "kv_write", "attention", "split_combine", "workspace_size",
     "kv_write_fp8", "attention_fp8", "alloc_cache_fp8", "rope_kv_write", "attention_cascade",
     "decode_step", "decode_step_fp8",
-    "choose_num_splits", "capture_size", "alloc_cache", "workspace", "trace_begin", "trace_end",
+    "decode_step_noalloc", "choose_num_splits", "capture_size", "alloc_cache", "workspace", "trace_begin", "trace_end",
     "trace_read",
     "kernel_name", "version", "validate_step", "step_problems",
 ]
@@ -187,12 +187,8 @@ def attention_fp8(query, key_cache, value_cache, k_scale, v_scale, query_start_l
     return out, lse
 
 
-def decode_step(key, value, key_cache, value_cache, slot_mapping, query, query_start_loc,
-                seq_lens, block_tables, max_query_len: int, max_seq_len: int, scale: float,
-                num_splits: int = 0, out=None, lse=None, want_lse: bool = True, workspace=None,
-                stream=None):
-    """kv_write then attention as one call (one launch for bf16 decode steps).
-    Returns (out, lse)."""
+def _check_step_args(key, value, key_cache, value_cache, slot_mapping, query,
+                     query_start_loc, seq_lens, block_tables):
     nt, hq, d = query.shape
     nb, hkv = key_cache.shape[0], key_cache.shape[1]
     if key.shape != (nt, hkv, d) or value.shape != key.shape:
@@ -212,6 +208,17 @@ def decode_step(key, value, key_cache, value_cache, slot_mapping, query, query_s
     if query_start_loc.shape != (ns + 1,) or block_tables.dim() != 2 or \
             block_tables.shape[0] != ns:
         raise ValueError("metadata shapes disagree")
+    return nt, hq, d, nb, hkv, ns
+
+
+def decode_step(key, value, key_cache, value_cache, slot_mapping, query, query_start_loc,
+                seq_lens, block_tables, max_query_len: int, max_seq_len: int, scale: float,
+                num_splits: int = 0, out=None, lse=None, want_lse: bool = True, workspace=None,
+                stream=None):
+    """kv_write then attention as one call (one launch for bf16 decode steps).
+    Returns (out, lse)."""
+    nt, hq, d, nb, hkv, ns = _check_step_args(key, value, key_cache, value_cache, slot_mapping,
+                                              query, query_start_loc, seq_lens, block_tables)
     splits = num_splits
     if splits == 0:
         splits = choose_num_splits(ns, max_query_len, max_seq_len, hq, hkv)
@@ -232,6 +239,29 @@ def decode_step(key, value, key_cache, value_cache, slot_mapping, query, query_s
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _dtype_code(query), _stream(stream))
     _check(st, "pa_decode_step")
+    return out, lse
+
+
+def decode_step_noalloc(key, value, key_cache, value_cache, slot_mapping, query,
+                        query_start_loc, seq_lens, block_tables, max_query_len: int,
+                        max_seq_len: int, scale: float, out, lse=None, num_splits: int = 0,
+                        stream=None):
+    """decode_step with the library's own per-GPU workspace: no device memory
+    is allocated (out, and lse if wanted, are the caller's).  Calls that
+    overlap on one GPU race.  Returns (out, lse)."""
+    nt, hq, d, nb, hkv, ns = _check_step_args(key, value, key_cache, value_cache, slot_mapping,
+                                              query, query_start_loc, seq_lens, block_tables)
+    if out.shape != query.shape or out.dtype != query.dtype:
+        raise ValueError("out must match the query")
+    st = LIB.pa_decode_step_noalloc(
+        _dev(key, "key"), _dev(value, "value"), _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), _dev(slot_mapping, "slot_mapping"),
+        _dev(query, "query"), _dev(query_start_loc, "query_start_loc"),
+        _dev(seq_lens, "seq_lens"), _dev(block_tables, "block_tables"), ns, nt,
+        int(max_query_len), int(max_seq_len), hq, hkv, d, PA_BLOCK_SIZE, block_tables.shape[1],
+        nb, float(scale), int(num_splits), _dev(out, "out"),
+        None if lse is None else _dev(lse, "lse"), _dtype_code(query), _stream(stream))
+    _check(st, "pa_decode_step_noalloc")
     return out, lse
 
 

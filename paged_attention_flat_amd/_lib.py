@@ -23,6 +23,7 @@ PA_F32 = 0
 PA_BF16 = 1
 PA_BLOCK_SIZE = 16
 PA_MAX_SPLITS = 256
+PA_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -39,6 +40,9 @@ PROTOTYPES = {
     "pa_decode_step": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
                               _i32, _i32, _i32, _i32, _i32, _i32, _i64, _f32, _i32, _vp, _vp,
                               _vp, _sz, _i32, _vp]),
+    "pa_decode_step_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                                      _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i64, _f32,
+                                      _i32, _vp, _vp, _i32, _vp]),
     "pa_attention_fwd_cascade": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                         _i32, _i32, _i32, _i32, _i32, _i64, _f32, _i32, _vp,
                                         _i32, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
