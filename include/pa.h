@@ -120,7 +120,12 @@ pa_status pa_kv_write(const void* key, const void* value,
  * 1 has almost none"): in bf16 mode the last split of each request and KV
  * head to finish performs it inside the same launch, in fp32 mode a separate
  * combine kernel does.  Rows of requests with many new tokens run the tiled
- * matrix-core kernel.  num_splits: 0 = pa_choose_num_splits() for these
+ * matrix-core kernel.  In bf16 mode a step with such rows runs the
+ * matrix-core kernel on a second stream the library keeps per device
+ * (created on first use, default priority), forked from `stream` with an
+ * event and joined back to it before the call returns, so it overlaps the
+ * decode kernel; the call stays asynchronous and capturable (the fork and
+ * join are event record / wait pairs).  num_splits: 0 = pa_choose_num_splits() for these
  * scalars, 1 = no split, 2..PA_MAX_SPLITS = forced.  The result does not
  * depend on num_splits beyond rounding.
  *
@@ -193,8 +198,12 @@ pa_status pa_rope_kv_write(void* query, const void* key, const void* value,
  * This relies on the definition of the flat batch ("Model execution",
  * "Flattening a step"): the slot of position p of request b is
  * block_tables[b][p / 16] * 16 + p % 16, so no other work-group reads a
- * new token's entry.  Otherwise (prefill rows, fp32) the two calls run in
- * order.  Results (pool bytes, out, lse) are those of the two calls.
+ * new token's entry.  A bf16 step that also has prefill rows (more than
+ * 16 / group new tokens) writes their tokens with a kernel over the
+ * matrix-core kernel's work list, ahead of it on the second stream of
+ * pa_attention_fwd, while the decode kernel writes the decode rows' tokens
+ * and those after the last request.  fp32 steps run the two calls in order.
+ * Results (pool bytes, out, lse) are those of the two calls.
  */
 pa_status pa_decode_step(const void* key, const void* value, void* key_cache, void* value_cache,
                          const int64_t* slot_mapping, const void* query,
@@ -330,10 +339,11 @@ pa_status pa_attention_fwd_fp8(const void* query, const void* key_cache,
 
 /*
  * pa_decode_step_fp8 -- pa_kv_write_fp8 followed by pa_attention_fwd_fp8 as
- * one call, fused into the decode launch under the conditions of
- * pa_decode_step (bf16 key / value / query; decode rows only), where the
- * decode kernel quantises each new token exactly as pa_kv_write_fp8 does.
- * dtype: of key / value (the query is bf16); PA_F32 runs the two calls.
+ * one call, fused as pa_decode_step is (bf16 key / value / query): the
+ * decode kernel quantises its rows' new tokens, and in a step with prefill
+ * rows a write over the matrix-core kernel's work list quantises theirs,
+ * each exactly as pa_kv_write_fp8 does.  dtype: of key / value (the query is
+ * bf16); PA_F32 runs the two calls.
  */
 pa_status pa_decode_step_fp8(const void* key, const void* value, void* key_cache,
                              void* value_cache, const int64_t* slot_mapping,

@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libpa.so")
 SOURCES = ["kv_write.hip", "decode.hip", "prefill.hip", "attn_f32.hip", "combine.hip",
-           "pa_api.cpp", "noalloc.cpp"]
+           "mixed.hip", "pa_api.cpp", "noalloc.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 instructions are kept off for every kernel (hipcc -O3 would

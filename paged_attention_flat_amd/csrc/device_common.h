@@ -137,6 +137,17 @@ __device__ __forceinline__ float sum_xor16(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// threadIdx.x as a value the compiler cannot treat as the same on every pass
+// of a persistent loop: a work unit's per-thread address arithmetic then
+// stays inside the unit instead of being hoisted out of the loop and kept
+// live (in registers) across the other kind of unit.  (Kernels without such
+// a loop use threadIdx.x itself, which the compiler may rematerialise.)
+__device__ __forceinline__ int unit_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) {
   return __builtin_amdgcn_exp2f(x);
 }

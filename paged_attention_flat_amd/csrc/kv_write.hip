@@ -9,6 +9,8 @@
 // index write neighbouring offsets of one dimension, which coalesce when the
 // tokens fill consecutive slots of a block (the usual case for a prefill
 // chunk).  The copy is a bit copy; the element type only fixes the width.
+#include <type_traits>
+
 #include "device_common.h"
 #include "pa_internal.h"
 
@@ -17,19 +19,18 @@ namespace {
 
 constexpr int kTok = 16;
 
+// Writes the `ntok` (<= 16) tokens t0 .. t0 + ntok - 1 of KV head h.  Every
+// thread of the work-group calls it (it holds a barrier); `vrow` / `sslot`
+// are the caller's LDS staging.
 template <typename E>
-__global__ __launch_bounds__(256) void kv_write_kernel(
-    const E* __restrict__ key, const E* __restrict__ value, E* __restrict__ kc,
-    E* __restrict__ vc, const int64_t* __restrict__ slots, int32_t nt,
-    int32_t hkv, int32_t d, int64_t num_slots) {
-  constexpr int kPad = 16 / sizeof(E);  // keeps LDS rows 16-byte aligned
-  __shared__ __align__(16) E vrow[kTok][128 + kPad];
-  __shared__ int64_t sslot[kTok];
+__device__ __forceinline__ void write_tokens(const E* __restrict__ key,
+                                             const E* __restrict__ value, E* __restrict__ kc,
+                                             E* __restrict__ vc,
+                                             const int64_t* __restrict__ slots, int t0,
+                                             int ntok, int h, int32_t hkv, int32_t d,
+                                             int64_t num_slots, E (*vrow)[128 + 16 / sizeof(E)],
+                                             int64_t* sslot) {
   const int tid = threadIdx.x;
-  const int t0 = blockIdx.x * kTok;
-  const int h = blockIdx.y;
-  const int ntok = min(kTok, nt - t0);
-
   // The K/V loads do not depend on the slot, so they are issued together with
   // the slot load (one memory round trip before the stores).
   const int cpr = d * (int)sizeof(E) / 16;  // 16-byte pieces per row
@@ -60,6 +61,18 @@ __global__ __launch_bounds__(256) void kv_write_kernel(
   }
 }
 
+template <typename E>
+__global__ __launch_bounds__(256) void kv_write_kernel(
+    const E* __restrict__ key, const E* __restrict__ value, E* __restrict__ kc,
+    E* __restrict__ vc, const int64_t* __restrict__ slots, int32_t nt,
+    int32_t hkv, int32_t d, int64_t num_slots) {
+  __shared__ __align__(16) E vrow[kTok][128 + 16 / sizeof(E)];
+  __shared__ int64_t sslot[kTok];
+  const int t0 = blockIdx.x * kTok;
+  write_tokens<E>(key, value, kc, vc, slots, t0, min(kTok, nt - t0), blockIdx.y, hkv, d,
+                  num_slots, vrow, sslot);
+}
+
 // FP8 (E4M3) cache: the same geometry with one byte per element.  Each
 // value is divided by its KV head's scale (IEEE fp32 division), clamped to
 // the largest finite E4M3 magnitude (448; the conversion would give NaN past
@@ -75,18 +88,15 @@ template <>
 __device__ __forceinline__ float widen<uint32_t>(uint32_t v) { return __uint_as_float(v); }
 
 template <typename E>
-__global__ __launch_bounds__(256) void kv_write_fp8_kernel(
-    const E* __restrict__ key, const E* __restrict__ value, uint8_t* __restrict__ kc,
-    uint8_t* __restrict__ vc, const int64_t* __restrict__ slots,
-    const float* __restrict__ k_scale, const float* __restrict__ v_scale, int32_t nt,
-    int32_t hkv, int32_t d, int64_t num_slots) {
-  __shared__ __align__(16) uint8_t vrow[kTok][128 + 16];
-  __shared__ int64_t sslot[kTok];
+__device__ __forceinline__ void write_tokens_fp8(const E* __restrict__ key,
+                                                 const E* __restrict__ value,
+                                                 uint8_t* __restrict__ kc,
+                                                 uint8_t* __restrict__ vc,
+                                                 const int64_t* __restrict__ slots, float ks,
+                                                 float vs, int t0, int ntok, int h, int32_t hkv,
+                                                 int32_t d, int64_t num_slots,
+                                                 uint8_t (*vrow)[128 + 16], int64_t* sslot) {
   const int tid = threadIdx.x;
-  const int t0 = blockIdx.x * kTok;
-  const int h = blockIdx.y;
-  const int ntok = min(kTok, nt - t0);
-  const float ks = k_scale[h], vs = v_scale[h];
   const int cpr = d / 8;  // 8-element pieces per row
   for (int c = tid; c < kTok * cpr; c += 256) {
     const int ti = c / cpr, part = c - ti * cpr;
@@ -118,6 +128,52 @@ __global__ __launch_bounds__(256) void kv_write_fp8_kernel(
     if (s < 0) continue;
     const size_t blk = (size_t)(s >> 4), off = (size_t)(s & 15);
     vc[((blk * hkv + h) * d + c) * kTok + off] = vrow[ti][c];
+  }
+}
+
+template <typename E>
+__global__ __launch_bounds__(256) void kv_write_fp8_kernel(
+    const E* __restrict__ key, const E* __restrict__ value, uint8_t* __restrict__ kc,
+    uint8_t* __restrict__ vc, const int64_t* __restrict__ slots,
+    const float* __restrict__ k_scale, const float* __restrict__ v_scale, int32_t nt,
+    int32_t hkv, int32_t d, int64_t num_slots) {
+  __shared__ __align__(16) uint8_t vrow[kTok][128 + 16];
+  __shared__ int64_t sslot[kTok];
+  const int t0 = blockIdx.x * kTok;
+  const int h = blockIdx.y;
+  write_tokens_fp8<E>(key, value, kc, vc, slots, k_scale[h], v_scale[h], t0,
+                      min(kTok, nt - t0), h, hkv, d, num_slots, vrow, sslot);
+}
+
+// The KV write of the tokens of the matrix-core kernel's work list only: one
+// work-group per (work item, KV head) writes the item's query tile (tq
+// consecutive tokens of one request), 16 tokens at a time.  In a step that
+// also has decode rows, the decode kernel writes those rows' tokens itself.
+template <typename E, bool F8>
+__global__ __launch_bounds__(256) void kv_write_plan_kernel(
+    const E* __restrict__ key, const E* __restrict__ value, void* __restrict__ kc,
+    void* __restrict__ vc, const int64_t* __restrict__ slots,
+    const float* __restrict__ k_scale, const float* __restrict__ v_scale,
+    const int32_t* __restrict__ plan, const int32_t* __restrict__ qsl, int32_t tq,
+    int32_t hkv, int32_t d, int64_t num_slots) {
+  typedef typename std::conditional<F8, uint8_t, E>::type CE;
+  __shared__ __align__(16) CE vrow[kTok][128 + 16 / sizeof(CE)];
+  __shared__ int64_t sslot[kTok];
+  const int item = blockIdx.x;
+  if (item >= plan[0]) return;
+  const int b = plan[1 + 2 * item], tile = plan[2 + 2 * item];
+  const int q0 = qsl[b], q1 = qsl[b + 1];
+  const int t_begin = q0 + tile * tq;
+  const int t_end = min(q1, t_begin + tq);
+  const int h = blockIdx.y;
+  for (int t0 = t_begin; t0 < t_end; t0 += kTok) {
+    if constexpr (F8)
+      write_tokens_fp8<E>(key, value, (uint8_t*)kc, (uint8_t*)vc, slots, k_scale[h], v_scale[h],
+                          t0, min(kTok, t_end - t0), h, hkv, d, num_slots, vrow, sslot);
+    else
+      write_tokens<E>(key, value, (E*)kc, (E*)vc, slots, t0, min(kTok, t_end - t0), h, hkv, d,
+                      num_slots, vrow, sslot);
+    __syncthreads();  // the staging is reused by the next 16 tokens
   }
 }
 
@@ -303,6 +359,24 @@ hipError_t launch_kv_write_fp8(const void* key, const void* value, void* kc, voi
                        (const uint32_t*)key, (const uint32_t*)value, (uint8_t*)kc, (uint8_t*)vc,
                        slots, k_scale, v_scale, nt, hkv, d, num_blocks * kTok);
   }
+  trace_after(stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_write_plan(const AttnArgs& a, int32_t tq, hipStream_t stream) {
+  dim3 grid(a.plan_cap, a.hkv);
+  const int64_t num_slots = a.num_blocks * kTok;
+  trace_before(a.cache_fp8 ? K_KV_WRITE_FP8 : K_KV_WRITE, stream);
+  if (a.cache_fp8)
+    hipLaunchKernelGGL((kv_write_plan_kernel<uint16_t, true>), grid, dim3(256), 0, stream,
+                       (const uint16_t*)a.knew, (const uint16_t*)a.vnew, (void*)a.kc,
+                       (void*)a.vc, a.slots, a.k_scale, a.v_scale, a.plan, a.qsl, tq, a.hkv, a.d,
+                       num_slots);
+  else
+    hipLaunchKernelGGL((kv_write_plan_kernel<uint16_t, false>), grid, dim3(256), 0, stream,
+                       (const uint16_t*)a.knew, (const uint16_t*)a.vnew, (void*)a.kc,
+                       (void*)a.vc, a.slots, a.k_scale, a.v_scale, a.plan, a.qsl, tq, a.hkv, a.d,
+                       num_slots);
   trace_after(stream);
   return hipGetLastError();
 }

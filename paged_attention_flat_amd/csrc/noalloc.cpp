@@ -76,9 +76,9 @@ extern "C" pa_status pa_decode_step_noalloc(
   void* ws = nullptr;
   const pa_status st = scratch_of_current_device((hipStream_t)stream, &ws);
   if (st != PA_OK) return st;
-  return pa_decode_step(key, value, key_cache, value_cache, slot_mapping, query,
-                        query_start_loc, seq_lens, block_tables, num_seqs, num_tokens,
-                        max_query_len, max_seq_len, num_q_heads, num_kv_heads, head_dim,
-                        block_size, block_table_stride, num_blocks, scale, splits, out, lse, ws,
-                        (size_t)PA_NOALLOC_SCRATCH_BYTES, dtype, stream);
+  return pa::decode_step_impl(key, value, key_cache, value_cache, slot_mapping, query,
+                              query_start_loc, seq_lens, block_tables, num_seqs, num_tokens,
+                              max_query_len, max_seq_len, num_q_heads, num_kv_heads, head_dim,
+                              block_size, block_table_stride, num_blocks, scale, splits, out, lse,
+                              ws, (size_t)PA_NOALLOC_SCRATCH_BYTES, dtype, stream);
 }

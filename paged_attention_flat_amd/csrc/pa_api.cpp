@@ -74,9 +74,10 @@ size_t plan_capacity(int32_t num_seqs, int32_t num_tokens) {
 // Workspace layout (each region 256-byte aligned):
 //   [split-merge counters: num_seqs * hq ints, zero between calls]
 //   [plan: 1 + 2 * cap ints][plan_tmp: 2 * cap ints][decode order: 1 + num_seqs ints]
+//   [mixed kernel's work counters: 2 ints, zeroed by the plan kernel]
 //   [partial out: splits * nt * hq * d floats][partial lse: splits * nt * hq floats]
 struct WsLayout {
-  size_t sem, plan, plan_tmp, order, part_out, part_lse;
+  size_t sem, plan, plan_tmp, order, claim, part_out, part_lse;
   size_t pre_index, vtok, vpos, casc_count, pre_out, pre_lse;  // cascade only
   size_t total;
 };
@@ -95,7 +96,8 @@ WsLayout ws_layout(int32_t num_seqs, int32_t num_tokens, int32_t hq, int32_t d, 
   w.plan = align256((size_t)num_seqs * hq * sizeof(int32_t));
   w.plan_tmp = align256(w.plan + (1 + 2 * cap) * sizeof(int32_t));
   w.order = align256(w.plan_tmp + 2 * cap * sizeof(int32_t));
-  w.part_out = align256(w.order + (1 + (size_t)num_seqs) * sizeof(int32_t));
+  w.claim = align256(w.order + (1 + (size_t)num_seqs) * sizeof(int32_t));
+  w.part_out = align256(w.claim + 2 * sizeof(int32_t));
   w.part_lse = w.part_out;
   w.total = w.part_out;
   if (splits > 1 || casc_rows > 0) {
@@ -196,6 +198,7 @@ const char* pa_kernel_name(int32_t id) {
     case K_ROPE_KV_WRITE: return "rope_kv_write";
     case K_CASCADE_SETUP: return "cascade_setup";
     case K_CASCADE_PREFIX: return "cascade_prefix";
+    case K_MIXED: return "mixed_prefill_decode";
   }
   return "unknown";
 }
@@ -421,6 +424,7 @@ pa_status attention_impl(const void* query, const void* key_cache, const void* v
   a.decode_order = nullptr;
   if ((int64_t)num_seqs * num_kv_heads * splits > a.num_cus && num_seqs >= 64)
     a.decode_order = reinterpret_cast<int32_t*>(ws + lay.order);
+  a.claim = reinterpret_cast<int32_t*>(ws + lay.claim);
   a.cache_fp8 = cache_fp8 ? 1 : 0;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
@@ -457,17 +461,70 @@ pa_status attention_impl(const void* query, const void* key_cache, const void* v
       e = launch_combine(a.part_out, a.part_lse, splits, num_tokens, num_q_heads, head_dim, out,
                          lse, 0, query_start_loc, num_seqs, 1 << 30, s);
   } else {
-    // the bf16 decode kernel merges its own split partials (the last split of
-    // each request and KV head to finish does it)
+    // The bf16 decode kernel merges its own split partials (the last split of
+    // each request and KV head to finish does it).  A step with prefill rows
+    // that certainly also has decode rows (more requests than can each hold
+    // more than dq of the step's tokens) runs its MFMA-bound prefill units
+    // and its HBM-bound decode units in one persistent launch (mixed.hip),
+    // except with a shared prefix, whose stage must finish before the decode
+    // rows merge it.  Otherwise the matrix-core kernel runs on its own: in
+    // persistent form it is ~4 % slower, which only an overlap repays.
     const int32_t dq = decode_max_q(group);
-    if (max_query_len > dq) e = launch_prefill_bf16(a, s);
-    if (e == hipSuccess && cascade) e = launch_cascade_prefix(a, s);
-    if (e == hipSuccess) e = launch_decode_bf16(a, s);
+    const bool prefill = max_query_len > dq;
+    const bool has_decode_rows = (int64_t)num_seqs > (int64_t)num_tokens / (dq + 1);
+    if (prefill && has_decode_rows && !cascade) {
+      e = launch_mixed_bf16(a, s);
+    } else {
+      if (prefill) e = launch_prefill_bf16(a, s);
+      if (e == hipSuccess && cascade) e = launch_cascade_prefix(a, s);
+      if (e == hipSuccess) e = launch_decode_bf16(a, s);
+    }
   }
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 }  // namespace
+
+namespace pa {
+
+pa_status decode_step_impl(const void* key, const void* value, void* key_cache,
+                           void* value_cache, const int64_t* slot_mapping, const void* query,
+                           const int32_t* query_start_loc, const int32_t* seq_lens,
+                           const int32_t* block_tables, int32_t num_seqs, int32_t num_tokens,
+                           int32_t max_query_len, int32_t max_seq_len, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int32_t block_table_stride, int64_t num_blocks, float scale,
+                           int32_t num_splits, void* out, float* lse, void* workspace,
+                           size_t workspace_bytes, pa_dtype dtype, void* stream) {
+  if (num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return PA_ERR_INVALID;
+  const int32_t group = num_q_heads / num_kv_heads;
+  // one call for bf16: the decode kernel writes the decode rows' tokens (and
+  // those after the last request), and in a step with prefill rows a write
+  // over the matrix-core kernel's work list writes theirs ahead of it
+  const bool fuse = dtype == PA_BF16 && is_pow2_group(group) && num_seqs > 0 &&
+                    num_tokens > 0 && max_query_len >= 1;
+  if (!fuse) {
+    // the two calls in order (same results, two launches)
+    pa_status st = pa_kv_write(key, value, key_cache, value_cache, slot_mapping, num_tokens,
+                               num_kv_heads, head_dim, block_size, num_blocks, dtype, stream);
+    if (st != PA_OK) return st;
+    return attention_impl(query, key_cache, value_cache, nullptr, nullptr, query_start_loc,
+                          seq_lens, block_tables, num_seqs, num_tokens, max_query_len,
+                          max_seq_len, num_q_heads, num_kv_heads, head_dim, block_size,
+                          block_table_stride, num_blocks, scale, num_splits, out, lse, workspace,
+                          workspace_bytes, dtype, false, stream);
+  }
+  if (!key || !value || !slot_mapping) return PA_ERR_NULL;
+  if (!aligned16(key) || !aligned16(value)) return PA_ERR_INVALID;
+  return attention_impl(query, key_cache, value_cache, nullptr, nullptr, query_start_loc,
+                        seq_lens, block_tables, num_seqs, num_tokens, max_query_len, max_seq_len,
+                        num_q_heads, num_kv_heads, head_dim, block_size, block_table_stride,
+                        num_blocks, scale, num_splits, out, lse, workspace, workspace_bytes,
+                        dtype, false, stream, nullptr, 0, nullptr, 0, key, value, slot_mapping);
+}
+
+}  // namespace pa
 
 extern "C" {
 
@@ -536,29 +593,11 @@ pa_status pa_decode_step(const void* key, const void* value, void* key_cache, vo
                          int32_t block_table_stride, int64_t num_blocks, float scale,
                          int32_t num_splits, void* out, float* lse, void* workspace,
                          size_t workspace_bytes, pa_dtype dtype, void* stream) {
-  if (num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
-    return PA_ERR_INVALID;
-  const int32_t group = num_q_heads / num_kv_heads;
-  const bool fuse = dtype == PA_BF16 && is_pow2_group(group) && num_seqs > 0 &&
-                    num_tokens > 0 && max_query_len >= 1 && max_query_len <= decode_max_q(group);
-  if (!fuse) {
-    // the two calls in order (same results, two launches)
-    pa_status st = pa_kv_write(key, value, key_cache, value_cache, slot_mapping, num_tokens,
-                               num_kv_heads, head_dim, block_size, num_blocks, dtype, stream);
-    if (st != PA_OK) return st;
-    return pa_attention_fwd(query, key_cache, value_cache, query_start_loc, seq_lens,
-                            block_tables, num_seqs, num_tokens, max_query_len, max_seq_len,
-                            num_q_heads, num_kv_heads, head_dim, block_size, block_table_stride,
-                            num_blocks, scale, num_splits, out, lse, workspace, workspace_bytes,
-                            dtype, stream);
-  }
-  if (!key || !value || !slot_mapping) return PA_ERR_NULL;
-  if (!aligned16(key) || !aligned16(value)) return PA_ERR_INVALID;
-  return attention_impl(query, key_cache, value_cache, nullptr, nullptr, query_start_loc,
-                        seq_lens, block_tables, num_seqs, num_tokens, max_query_len, max_seq_len,
-                        num_q_heads, num_kv_heads, head_dim, block_size, block_table_stride,
-                        num_blocks, scale, num_splits, out, lse, workspace, workspace_bytes,
-                        dtype, false, stream, nullptr, 0, nullptr, 0, key, value, slot_mapping);
+  return pa::decode_step_impl(key, value, key_cache, value_cache, slot_mapping, query,
+                              query_start_loc, seq_lens, block_tables, num_seqs, num_tokens,
+                              max_query_len, max_seq_len, num_q_heads, num_kv_heads, head_dim,
+                              block_size, block_table_stride, num_blocks, scale, num_splits, out,
+                              lse, workspace, workspace_bytes, dtype, stream);
 }
 
 pa_status pa_decode_step_fp8(const void* key, const void* value, void* key_cache,
@@ -574,8 +613,11 @@ pa_status pa_decode_step_fp8(const void* key, const void* value, void* key_cache
   if (num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
     return PA_ERR_INVALID;
   const int32_t group = num_q_heads / num_kv_heads;
+  // one call: the decode kernel writes the decode rows' tokens, and in a
+  // step with prefill rows a write over the matrix-core kernel's work list
+  // writes theirs ahead of it
   const bool fuse = dtype == PA_BF16 && is_pow2_group(group) && num_seqs > 0 &&
-                    num_tokens > 0 && max_query_len >= 1 && max_query_len <= decode_max_q(group);
+                    num_tokens > 0 && max_query_len >= 1;
   if (!fuse) {
     pa_status st = pa_kv_write_fp8(key, value, key_cache, value_cache, slot_mapping, k_scale,
                                    v_scale, num_tokens, num_kv_heads, head_dim, block_size,

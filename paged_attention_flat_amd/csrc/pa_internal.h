@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/pa.h"
+
 namespace pa {
 
 // ---- kernel ids for tracing -------------------------------------------------
@@ -23,7 +25,8 @@ enum KernelId : int32_t {
   K_ROPE_KV_WRITE = 11,
   K_CASCADE_SETUP = 12,
   K_CASCADE_PREFIX = 13,
-  K_COUNT = 14
+  K_MIXED = 14,
+  K_COUNT = 15
 };
 
 // Tracing hooks (pa_api.cpp).  trace_before/after bracket one launch.
@@ -67,6 +70,7 @@ struct AttnArgs {
   int32_t* plan_tmp;    // unsorted work list (2 ints/item)
   int32_t plan_cap;     // capacity of the work list (items)
   int32_t* decode_order;  // nullable: count + ranked decode requests
+  int32_t* claim;         // [2] work counters of the mixed kernel (prefill, decode)
   int32_t num_cus;        // compute units of the current device
   int32_t* sem;           // nullable: zeroed arrival counters, one per (request, KV head)
   int32_t cache_fp8;      // 1: kc / vc hold E4M3 codes (query and out bf16)
@@ -108,7 +112,18 @@ inline int32_t prefill_tile_tokens(int32_t group) {
   return 32 * PA_PREFILL_ROW_GROUPS * PA_PREFILL_WAVES / group;
 }
 
+// KV write of the tokens of the matrix-core kernel's work list (a.plan, built
+// on the same stream first): a.knew / a.vnew / a.slots into a.kc / a.vc, bf16
+// or quantised to E4M3 (a.cache_fp8), tq tokens per work item.
+hipError_t launch_kv_write_plan(const AttnArgs& a, int32_t tq, hipStream_t stream);
 hipError_t launch_decode_bf16(const AttnArgs& a, hipStream_t stream);
+// The pieces of a step with prefill rows, run as one persistent launch:
+// the matrix-core kernel's work list (and, with a.knew, the write of its
+// tokens; a.claim zeroed), the decode order, then the mixed kernel whose
+// work-groups take prefill units and decode units from two counters.
+hipError_t launch_prefill_plan(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_decode_order(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_mixed_bf16(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t stream);
 // shared-prefix stage: gather the sharers' decode rows, attend them to the
 // shared blocks (partials in pre_out / pre_lse); the decode kernel merges
@@ -119,5 +134,17 @@ hipError_t launch_combine(const float* po, const float* pl, int32_t splits,
                           int32_t nt, int32_t hq, int32_t d, void* out, float* lse,
                           int32_t out_bf16, const int32_t* qsl, int32_t num_seqs,
                           int32_t decode_max_q, hipStream_t stream);
+
+// pa_decode_step (shared with the no-alloc entry point, which passes the
+// library's own workspace).
+pa_status decode_step_impl(const void* key, const void* value, void* key_cache,
+                           void* value_cache, const int64_t* slot_mapping, const void* query,
+                           const int32_t* query_start_loc, const int32_t* seq_lens,
+                           const int32_t* block_tables, int32_t num_seqs, int32_t num_tokens,
+                           int32_t max_query_len, int32_t max_seq_len, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int32_t block_table_stride, int64_t num_blocks, float scale,
+                           int32_t num_splits, void* out, float* lse, void* workspace,
+                           size_t workspace_bytes, pa_dtype dtype, void* stream);
 
 }  // namespace pa

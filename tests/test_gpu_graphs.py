@@ -101,3 +101,64 @@ def test_decode_graphs_past_the_top_size_run_eagerly():
     torch.cuda.synchronize()
     check_step(step, out, lse, kc, vc, "n=20 eager")
     assert dg.graphs == {}
+
+
+def test_mixed_step_graph_replays_match_eager():
+    # a mixed step (prefill chunks + decodes) in one call: its matrix-core
+    # kernel runs on the library's second stream, forked from and joined to
+    # the capturing stream.  Captured once, replayed three times with the
+    # pools reset by eager copies in between; every replay must give the
+    # eager call's bytes (pools, out, lse), and the eager call the oracle's.
+    import paged_attention_flat_amd as pa
+    from workloads import config_step
+    step = config_step(5, scale_down={"chunk": 90, "priors": (70, 300), "decodes": 40,
+                                      "lo": 20, "hi": 900, "prefix": 64, "sharers": 10,
+                                      "stride": 64})
+    dev = torch.device("cuda:0")
+    g = {n: getattr(step, n).to(dev).contiguous() for n in ("query", "key", "value")}
+    k0, v0 = step.k_pool.to(dev), step.v_pool.to(dev)
+    kc, vc = k0.clone(), v0.clone()
+    meta = [torch.as_tensor(x).to(dev) for x in (step.slot_mapping, step.query_start_loc,
+                                                   step.seq_lens, step.block_tables)]
+    out = torch.empty_like(g["query"])
+    lse = torch.empty(step.num_tokens, step.num_q_heads, dtype=torch.float32, device=dev)
+    ws = pa.workspace(step.num_seqs, step.num_tokens, step.num_q_heads, step.head_dim, 1,
+                      device=dev)
+
+    def call():
+        pa.decode_step(g["key"], g["value"], kc, vc, meta[0], g["query"], meta[1], meta[2],
+                       meta[3], step.max_query_len, step.max_seq_len, step.scale,
+                       num_splits=1, out=out, lse=lse, workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    n = int(step.query_start_loc[-1])
+    ref = [t.clone() for t in (out[:n], lse[:n], kc, vc)]
+    kp, vp = oracle.kv_write(raw_numpy(step.key), raw_numpy(step.value), raw_numpy(step.k_pool),
+                             raw_numpy(step.v_pool), step.slot_mapping)
+    for got, r in ((kc, kp), (vc, vp)):
+        assert np.array_equal(np.ascontiguousarray(got.view(torch.int16).cpu().numpy()).view(np.uint8),
+                              np.ascontiguousarray(r).view(np.uint8))
+    ro, rl = oracle.attention(raw_numpy(step.query), kp, vp, step.query_start_loc,
+                              step.seq_lens, step.block_tables, step.scale, step.num_kv_heads,
+                              "bf16")
+    assert float(np.abs(out[:n].float().cpu().double().numpy() - ro[:n]).max()) <= TOL_OUT
+    assert float(np.abs(lse[:n].cpu().double().numpy() - rl[:n]).max()) <= TOL_LSE
+    kc.copy_(k0)
+    vc.copy_(v0)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for rep in range(3):
+        kc.copy_(k0)
+        vc.copy_(v0)
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.randn(1 << 20, device=dev).mul_(2.0).sum().item()   # eager work between
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b, what in zip((out[:n], lse[:n], kc, vc), ref, ("out", "lse", "K", "V")):
+            ab = a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32)
+            bb = b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32)
+            assert torch.equal(ab, bb), f"replay {rep}: {what} differs from the eager call"
