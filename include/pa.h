@@ -120,12 +120,11 @@ pa_status pa_kv_write(const void* key, const void* value,
  * 1 has almost none"): in bf16 mode the last split of each request and KV
  * head to finish performs it inside the same launch, in fp32 mode a separate
  * combine kernel does.  Rows of requests with many new tokens run the tiled
- * matrix-core kernel.  In bf16 mode a step with such rows runs the
- * matrix-core kernel on a second stream the library keeps per device
- * (created on first use, default priority), forked from `stream` with an
- * event and joined back to it before the call returns, so it overlaps the
- * decode kernel; the call stays asynchronous and capturable (the fork and
- * join are event record / wait pairs).  num_splits: 0 = pa_choose_num_splits() for these
+ * matrix-core kernel.  In bf16 mode, when the host scalars show that the
+ * step also has decode rows (num_seqs > num_tokens / (16 / group + 1)), the
+ * two run as one persistent launch whose work-groups take prefill and
+ * decode work units from two counters in the workspace, so the MFMA-bound
+ * and the HBM-bound rows overlap.  num_splits: 0 = pa_choose_num_splits() for these
  * scalars, 1 = no split, 2..PA_MAX_SPLITS = forced.  The result does not
  * depend on num_splits beyond rounding.
  *
@@ -200,9 +199,9 @@ pa_status pa_rope_kv_write(void* query, const void* key, const void* value,
  * block_tables[b][p / 16] * 16 + p % 16, so no other work-group reads a
  * new token's entry.  A bf16 step that also has prefill rows (more than
  * 16 / group new tokens) writes their tokens with a kernel over the
- * matrix-core kernel's work list, ahead of it on the second stream of
- * pa_attention_fwd, while the decode kernel writes the decode rows' tokens
- * and those after the last request.  fp32 steps run the two calls in order.
+ * matrix-core kernel's work list, ahead of the attention launch, while the
+ * decode work writes the decode rows' tokens and those after the last
+ * request.  fp32 steps run the two calls in order.
  * Results (pool bytes, out, lse) are those of the two calls.
  */
 pa_status pa_decode_step(const void* key, const void* value, void* key_cache, void* value_cache,
