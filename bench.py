@@ -380,8 +380,21 @@ def kernel_times(runners, steps, log):
         v = sorted(v)
         q = lambda f: v[min(len(v) - 1, int(f * (len(v) - 1) + 0.5))]
         out[k] = {"avg_us": sum(v) / len(v), "launches": len(v), "p10_us": q(0.1),
-                  "p50_us": q(0.5), "p90_us": q(0.9)}
+                  "p50_us": q(0.5), "p90_us": q(0.9), "per_step_us": sum(v) / steps}
     return out
+
+
+KERNELS_TIMING = ("kernels_us: the step time split over its kernels in proportion to their "
+                  "HIP-event durations around traced eager launches (so they sum to "
+                  "ms_per_step); kernels_us_eager_traced: those durations themselves (each "
+                  "includes the events' own overhead, ~1-2 us per launch)")
+
+
+def attributed_us(kt, ms):
+    """The step time (ms) split over the kernels of kernel_times() in
+    proportion to each kernel's traced time per step."""
+    tot = sum(v["per_step_us"] for v in kt.values())
+    return {k: round(v["per_step_us"] / tot * ms * 1e3, 2) for k, v in kt.items()} if tot else {}
 
 
 class RopeRunner:
@@ -517,10 +530,15 @@ def bench_main(args, log):
     wm = work_model(step)
     ms, mode = time_steps(runners, n, warm, not args.eager, log, per_graph=per_graph)
     ev_ms = time_steps.last_event_ms   # one decode launch per step
+    graph_ms = ms
     eager_ms = sep_ms = None
     if not args.eager:
-        # the same steps launched one call at a time from the host (no graph)
-        eager_ms, _ = time_steps(runners, min(args.steps, 200), args.warmup, False, log)
+        # the same steps launched one call at a time from the host (no graph);
+        # the headline is the faster of the two launch paths (both measured
+        # over the same steps, the GPU kept busy by the queued launches)
+        eager_ms, _ = time_steps(runners, n, warm, False, log)
+        if eager_ms < ms:
+            ms, mode, ev_ms = eager_ms, "eager", time_steps.last_event_ms
         # and as two calls (pa_kv_write, pa_attention_fwd), from graphs
         sep = [StepRunner(step, dev, base.splits, pools=(r.g["kc"], r.g["vc"]))
                for r in runners]
@@ -537,7 +555,7 @@ def bench_main(args, log):
     achieved = kbytes / (dur_us * 1e-6) / 1e9
     res = {
         "step": step, "ms": ms, "mode": mode, "splits": base.splits, "work": wm,
-        "eager_ms": eager_ms, "sep_ms": sep_ms,
+        "eager_ms": eager_ms, "sep_ms": sep_ms, "graph_ms": graph_ms,
         "kernels": kt,
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
@@ -546,7 +564,8 @@ def bench_main(args, log):
                      "unit_def": "one context token of one request: K and V for 8 KV heads "
                                  "x 128 dims x 2 B = 4096 B (plus Q and table reads)",
                      "avg_launch_us": dur_us,
-                     "timing": "HIP events around the timed graph replays, / launches"},
+                     "timing": "HIP events around the timed steps of the reported launch "
+                               "path, / launches"},
     }
     del runners, base
     torch.cuda.empty_cache()
@@ -673,7 +692,8 @@ def bench_fp8(args, log):
         rec = {"workload": WORKLOAD_NAMES[cfg].split(" (")[0] + ", FP8 (E4M3) KV cache",
                "ms_per_step": ms, "launch": mode, "num_splits": runners[0].splits,
                "step_GBps": wm["bytes"] / (ms * 1e-3) / 1e9,
-               "kernels_us": {k: round(v["avg_us"], 2) for k, v in kt.items()}}
+               "kernels_us": attributed_us(kt, ms),
+               "kernels_us_eager_traced": {k: round(v["avg_us"], 2) for k, v in kt.items()}}
         name = "decode_split_partial" if "decode_split_partial" in kt else "decode"
         if name in kt and cfg != 4:
             kb, _ = decode_kernel_bytes(step)
@@ -753,7 +773,8 @@ def bench_shared_prefix(args, log):
         ms, _ = time_steps([run], n, warm, not args.eager, log)
         kt = kernel_times([run], min(n, 20), log)
         res[name] = {"ms_per_step": ms, "step_GBps_unique": wm["bytes"] / (ms * 1e-3) / 1e9,
-                     "kernels_us": {k: round(v["avg_us"], 2) for k, v in kt.items()}}
+                     "kernels_us": attributed_us(kt, ms),
+                     "kernels_us_eager_traced": {k: round(v["avg_us"], 2) for k, v in kt.items()}}
     log(f"shared prefix: {json.dumps(res)}")
     del r, rc, step
     torch.cuda.empty_cache()
@@ -801,7 +822,8 @@ def bench_extra(cfg, args, log):
            "step_GBps": wm["bytes"] / (ms * 1e-3) / 1e9,
            "step_hbm_frac": wm["bytes"] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
            "step_TFLOPps": wm["flops"] / (ms * 1e-3) / 1e12,
-           "kernels_us": {k: round(v["avg_us"], 2) for k, v in kt.items()}}
+           "kernels_us": attributed_us(kt, ms),
+           "kernels_us_eager_traced": {k: round(v["avg_us"], 2) for k, v in kt.items()}}
     if "decode" in kt or "decode_split_partial" in kt:
         name = "decode" if "decode" in kt else "decode_split_partial"
         kb, _ = decode_kernel_bytes(step)
@@ -813,6 +835,19 @@ def bench_extra(cfg, args, log):
         out["prefill_kernel"] = {"flops": wm["prefill_flops"], "TFLOPps": tf,
                                  "frac_mfma": tf / PEAK_BF16_TFLOPS,
                                  "traffic": measured_traffic(PROFILE_NAMES[cfg], "prefill_mfma")}
+    if "mixed_prefill_decode" in kt:
+        # one persistent launch holds the step's prefill and decode work: its
+        # roofline time is the larger of the decode bytes at peak HBM and the
+        # prefill FLOPs at peak MFMA
+        us = kt["mixed_prefill_decode"]["avg_us"]
+        kb, _ = decode_kernel_bytes(step)
+        t_roof = max(kb / (PEAK_HBM_GBS * 1e9), wm["prefill_flops"] / (PEAK_BF16_TFLOPS * 1e12))
+        out["mixed_kernel"] = {"us": us, "decode_bytes": kb, "prefill_flops": wm["prefill_flops"],
+                               "decode_GBps": kb / (us * 1e-6) / 1e9,
+                               "prefill_TFLOPps": wm["prefill_flops"] / (us * 1e-6) / 1e12,
+                               "roofline_frac": t_roof / (us * 1e-6),
+                               "traffic": measured_traffic(PROFILE_NAMES[cfg],
+                                                           "mixed_prefill_decode")}
     if cfg == 5:
         t_roof = max(wm["bytes"] / (PEAK_HBM_GBS * 1e9), wm["flops"] / (PEAK_BF16_TFLOPS * 1e12))
         out["step_roofline_frac"] = t_roof / (ms * 1e-3)
@@ -825,7 +860,8 @@ def bench_extra(cfg, args, log):
             "sharers": int(rc.g["sharers"].numel()), "prefix_blocks": int(rc.g["prefix"].numel()),
             "ms_per_step": cms,
             "step_GBps": wm["bytes"] / (cms * 1e-3) / 1e9,
-            "kernels_us": {k: round(v["avg_us"], 2) for k, v in ckt.items()}}
+            "kernels_us": attributed_us(ckt, cms),
+            "kernels_us_eager_traced": {k: round(v["avg_us"], 2) for k, v in ckt.items()}}
         del rc
     log(f"config{cfg}: {json.dumps(out)}")
     del r
@@ -833,35 +869,145 @@ def bench_extra(cfg, args, log):
     return out
 
 
-def cpu_baseline(args, log):
-    """The fp64 oracle (as it stands) on the same workload shape, built on the
-    host: whole steps (KV write + attention of the one decode row), repeated
-    for about args.cpu_seconds.  BLAS is held to one thread."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def _cpu_workers():
+    """Worker processes for the oracle: the host cores this process may run
+    on, at most 16 (a GPU machine's host share per GPU)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+ORACLE_ARRAYS = ("query", "key", "value", "k_pool", "v_pool")
+
+
+def _dump_step(step, d, rows=None):
+    """The step's inputs as .npy files (raw bits) for the oracle workers."""
+    import numpy as np
+
+    from workloads import raw_numpy
+    os.makedirs(d, exist_ok=True)
+    for n in ORACLE_ARRAYS:
+        np.save(os.path.join(d, n + ".npy"), np.ascontiguousarray(raw_numpy(getattr(step, n))))
+    for n in ("query_start_loc", "seq_lens", "block_tables", "slot_mapping"):
+        np.save(os.path.join(d, n + ".npy"), np.asarray(getattr(step, n)))
+    with open(os.path.join(d, "meta.json"), "w") as f:
+        json.dump({"scale": step.scale, "num_kv_heads": step.num_kv_heads, "dtype": step.dtype,
+                   "rows": None if rows is None else [int(r) for r in rows]}, f)
+
+
+def _oracle_worker(task):
+    """One worker process: repeat the oracle's KV write + attention (of the
+    given rows, or every row) on memory-mapped inputs for about `seconds`,
+    one BLAS thread.  Returns (repetitions, wall seconds)."""
+    d, seconds = task
+    import numpy as np
     import threadpoolctl
 
     import oracle
-    from workloads import config_step, raw_numpy
-    step = config_step(2, device="cpu", fill="zero")
-    key, value = raw_numpy(step.key), raw_numpy(step.value)
-    kp0, vp0 = raw_numpy(step.k_pool), raw_numpy(step.v_pool)
-    q = raw_numpy(step.query)
-    wm = work_model(step)
+    ld = lambda n: np.load(os.path.join(d, n + ".npy"), mmap_mode="r")  # noqa: E731
+    with open(os.path.join(d, "meta.json")) as f:
+        meta = json.load(f)
+    q, k, v, kp0, vp0 = (ld(n) for n in ORACLE_ARRAYS)
+    qsl, sl, bt, sm = (np.asarray(ld(n)) for n in ("query_start_loc", "seq_lens",
+                                                    "block_tables", "slot_mapping"))
     n = 0
-    t_total = 0.0
+    t0 = time.perf_counter()
     with threadpoolctl.threadpool_limits(1):
-        while t_total < args.cpu_seconds and n < 50:
-            t0 = time.perf_counter()
-            kp, vp = oracle.kv_write(key, value, kp0, vp0, step.slot_mapping)
-            oracle.attention(q, kp, vp, step.query_start_loc, step.seq_lens,
-                             step.block_tables, step.scale, step.num_kv_heads, step.dtype)
-            t_total += time.perf_counter() - t0
+        while True:
+            kp, vp = oracle.kv_write(k, v, kp0, vp0, sm)
+            oracle.attention(q, kp, vp, qsl, sl, bt, meta["scale"], meta["num_kv_heads"],
+                             meta["dtype"], rows=meta["rows"])
             n += 1
-    per = t_total / n
-    log(f"cpu oracle: {n} steps, {per:.3f} s/step")
-    return {"value": wm["bytes"] / per / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} whole steps of the same workload (KV write + attention of the "
-                      f"decode row, 32 heads x 32768 keys) in fp64, {t_total:.1f} s total, "
-                      f"{per * 1e3:.1f} ms per step"}
+            if time.perf_counter() - t0 >= seconds:
+                break
+    return n, time.perf_counter() - t0
+
+
+def _run_oracle_pool(d, workers, seconds):
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+    t0 = time.perf_counter()
+    with ProcessPoolExecutor(workers, mp_context=mp.get_context("spawn")) as ex:
+        res = list(ex.map(_oracle_worker, [(d, seconds)] * workers))
+    wall = time.perf_counter() - t0
+    return sum(r[0] for r in res), max(r[1] for r in res), wall
+
+
+def cpu_baseline(args, log):
+    """The fp64 oracle (as it stands) on the GPU machine's host cores: N worker
+    processes (one BLAS thread each, N = the cores this process may use, at
+    most 16) repeat whole steps of the headline workload for about
+    args.cpu_seconds, and bounded samples of the large-batch decode (16
+    requests) and of the long prefill (48 rows) for a third of that each.
+    Inputs are generated on the host with the workloads' own seeds and shared
+    with the workers as memory-mapped files."""
+    import shutil
+    import tempfile
+
+    import numpy as np
+
+    from workloads import config_step
+    workers = _cpu_workers()
+    model = _cpu_model()
+    base = "/dev/shm" if os.path.isdir("/dev/shm") else None
+    tmp = tempfile.mkdtemp(prefix="pa_oracle_", dir=base)
+    try:
+        step = config_step(2, device="cpu", fill="zero")
+        wm = work_model(step)
+        _dump_step(step, os.path.join(tmp, "c2"))
+        del step
+        n, t_work, wall = _run_oracle_pool(os.path.join(tmp, "c2"), workers, args.cpu_seconds)
+        head = {"value": wm["bytes"] * n / t_work / 1e9, "unit": "GB/s", "cores": workers,
+                "kind": "oracle", "cpu_model": model, "threads_per_worker": 1,
+                "sample": f"{n} whole steps of the same workload (KV write + attention of the "
+                          f"decode row, 32 heads x 32768 keys) in fp64 over {workers} worker "
+                          f"processes, {t_work:.1f} s each ({wall:.1f} s wall incl. start-up)"}
+        log(f"cpu oracle: {n} steps on {workers} workers ({model})")
+        samples = {}
+        # large-batch decode: 16 requests drawn like the workload's 256
+        step = config_step(3, device="cpu", fill="zero", scale_down={"batch": 16})
+        wm3 = work_model(step)
+        _dump_step(step, os.path.join(tmp, "c3"))
+        del step
+        n, t_work, _ = _run_oracle_pool(os.path.join(tmp, "c3"), workers, args.cpu_seconds / 3)
+        samples["large_batch_decode"] = {
+            "value": wm3["bytes"] * n / t_work / 1e9, "unit": "GB/s", "cores": workers,
+            "sample": f"{n} steps of 16 requests with contexts U[512, 8192] (the workload's "
+                      f"draw rule; {wm3['ctx_tokens']} context tokens per step)"}
+        # long prefill: the full step's KV write and 48 of its 32768 rows
+        step = config_step(4, device="cpu", fill="zero")
+        rng = np.random.default_rng(4)
+        qsl = step.query_start_loc
+        rows = sorted(set(int(x) for b in range(step.num_seqs)
+                          for x in rng.integers(int(qsl[b]), int(qsl[b + 1]), 12)))
+        pos = [r - int(qsl[int(np.searchsorted(qsl, r, side="right")) - 1]) for r in rows]
+        flops = 4.0 * step.head_dim * step.num_q_heads * sum(p + 1 for p in pos)
+        _dump_step(step, os.path.join(tmp, "c4"), rows=rows)
+        del step
+        n, t_work, _ = _run_oracle_pool(os.path.join(tmp, "c4"), workers, args.cpu_seconds / 3)
+        samples["long_prefill"] = {
+            "value": flops * n / t_work / 1e12, "unit": "TFLOP/s", "cores": workers,
+            "sample": f"{n} passes of the full step's KV write (32768 tokens) plus "
+                      f"attention of {len(rows)} seeded rows ({flops / 1e9:.2f} GFLOP)"}
+        head["other_workloads"] = samples
+        log(f"cpu oracle samples: {json.dumps(samples)}")
+        return head
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
 
 
 def main():
@@ -943,6 +1089,11 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args, log)
+        # the oracle's samples beside the GPU numbers of the same workloads
+        by_cfg = {3: "large_batch_decode", 4: "long_prefill"}
+        for cfg, e in zip((3, 4, 5), extras):
+            if cfg in by_cfg:
+                e["oracle_cpu"] = cpu["other_workloads"][by_cfg[cfg]]
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -964,9 +1115,12 @@ def main():
         "roofline": {k: (round(v, 4) if isinstance(v, float) else v)
                      for k, v in res["roofline"].items()},
         "cpu_baseline": cpu,
-        "kernels_us": {k: {m: round(v[m], 2) for m in ("avg_us", "p10_us", "p50_us", "p90_us")}
-                       for k, v in res["kernels"].items()},
-        "launch_path": {"graph_us_per_step": round(ms * 1e3, 2),
+        "kernels_us": attributed_us(res["kernels"], ms),
+        "kernels_us_eager_traced": {k: {m: round(v[m], 2) for m in ("avg_us", "p10_us", "p50_us",
+                                                                     "p90_us")}
+                                    for k, v in res["kernels"].items()},
+        "kernels_timing": KERNELS_TIMING,
+        "launch_path": {"graph_us_per_step": round(res["graph_ms"] * 1e3, 2),
                         "eager_us_per_step": None if res["eager_ms"] is None
                         else round(res["eager_ms"] * 1e3, 2),
                         "two_calls_graph_us_per_step": None if res["sep_ms"] is None

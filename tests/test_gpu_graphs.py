@@ -104,16 +104,19 @@ def test_decode_graphs_past_the_top_size_run_eagerly():
 
 
 def test_mixed_step_graph_replays_match_eager():
-    # a mixed step (prefill chunks + decodes) in one call: its matrix-core
-    # kernel runs on the library's second stream, forked from and joined to
-    # the capturing stream.  Captured once, replayed three times with the
-    # pools reset by eager copies in between; every replay must give the
-    # eager call's bytes (pools, out, lse), and the eager call the oracle's.
+    # a mixed step (prefill chunks + decodes) in one call: the work-list
+    # write, the plan and order kernels and the attention launch (persistent
+    # prefill + decode units when decode rows are certain, else the separate
+    # kernels), with work counters reset inside the step.  Captured once,
+    # replayed three times with the pools reset by eager copies in between;
+    # every replay must give the eager call's bytes (pools, out, lse), and
+    # the eager call the oracle's.
     import paged_attention_flat_amd as pa
     from workloads import config_step
-    step = config_step(5, scale_down={"chunk": 90, "priors": (70, 300), "decodes": 40,
+    step = config_step(5, scale_down={"chunk": 90, "priors": (70, 300), "decodes": 80,
                                       "lo": 20, "hi": 900, "prefix": 64, "sharers": 10,
                                       "stride": 64})
+    assert step.num_seqs > step.num_tokens // 5       # the persistent launch is taken
     dev = torch.device("cuda:0")
     g = {n: getattr(step, n).to(dev).contiguous() for n in ("query", "key", "value")}
     k0, v0 = step.k_pool.to(dev), step.v_pool.to(dev)
