@@ -12,7 +12,7 @@
 // (converted to bf16 exactly in registers; K's scale folds into the score
 // scale, V's into the output).
 //
-// MI355X design.  One work-group = (KV head, request, split); its eight waves
+// MI355X design.  One work-group = (KV head, request, split); its waves
 // walk disjoint pairs of 16-token blocks of the split's range and each keeps
 // its own (m, l, acc) state, merged lane by lane through LDS at the end.  All
 // query heads of the KV head (group size G) and up to 16 / G new tokens are
@@ -28,8 +28,9 @@
 // of the two S^T products are assigned to keys so that each lane's P values
 // are 8 consecutive keys of one block, matching one 16-byte V load.  Block
 // ids come 64 at a time from one coalesced table load and are picked with
-// readlane.  Eight waves per work-group (16 per CU at 124 VGPRs) keep enough
-// loads in flight to cover HBM latency.  Row maxima use two cross-lane
+// readlane.  Sixteen waves per CU (four 4-wave work-groups at 118 VGPRs, or
+// two-fragment-set waves when there are few units) keep enough loads in
+// flight to cover HBM latency.  Row maxima use two cross-lane
 // exchanges; exponentials are base 2 on log2(e)-prescaled scores.
 //
 // Work order: work-group index = KV head fastest, then request rank.  For
