@@ -42,9 +42,7 @@
 namespace pa {
 namespace {
 
-// Counting sort of the decode requests (0 < q_len <= dq) by block count,
-// largest first.  One work-group; ties keep no particular order (the order
-// only schedules work, it never changes a result).
+// Counting sort of the decode requests by block count (decode_order_block).
 __global__ __launch_bounds__(1024) void decode_order_kernel(const int32_t* __restrict__ qsl,
                                                             const int32_t* __restrict__ seq_lens,
                                                             int32_t num_seqs, int32_t dq,
@@ -52,44 +50,7 @@ __global__ __launch_bounds__(1024) void decode_order_kernel(const int32_t* __res
                                                             int32_t* __restrict__ order) {
   __shared__ int hist[kBuckets];
   __shared__ int part[1024];
-  const int tid = threadIdx.x;
-  for (int i = tid; i < kBuckets; i += 1024) hist[i] = 0;
-  __syncthreads();
-  for (int b = tid; b < num_seqs; b += 1024) {
-    const int ql = qsl[b + 1] - qsl[b];
-    if (ql <= 0 || ql > dq) continue;
-    const int key = min(((seq_lens[b] + 15) >> 4) >> shift, kBuckets - 1);
-    atomicAdd(&hist[kBuckets - 1 - key], 1);
-  }
-  __syncthreads();
-  // exclusive scan of hist: 4 buckets per thread, then a scan of the partials
-  int loc[4], s = 0;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    loc[k] = s;
-    s += hist[tid * 4 + k];
-  }
-  part[tid] = s;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int v = tid >= off ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
-  }
-  const int base = part[tid] - s;
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < 4; ++k) hist[tid * 4 + k] = base + loc[k];
-  if (tid == 1023) order[0] = part[1023];
-  __syncthreads();
-  for (int b = tid; b < num_seqs; b += 1024) {
-    const int ql = qsl[b + 1] - qsl[b];
-    if (ql <= 0 || ql > dq) continue;
-    const int key = min(((seq_lens[b] + 15) >> 4) >> shift, kBuckets - 1);
-    const int pos = atomicAdd(&hist[kBuckets - 1 - key], 1);
-    order[1 + pos] = b;
-  }
+  decode_order_block(qsl, seq_lens, num_seqs, dq, shift, order, hist, part);
 }
 
 template <int D, int G, int NW, int PIPE, bool F8>
@@ -105,13 +66,11 @@ __global__ __launch_bounds__(64 * NW, (PIPE == 2 && NW < 8 ? 8 / NW : 1)) void d
 // the counting sort of the decode requests, when the launch ranks them
 template <int G>
 void order_dg(const AttnArgs& a, hipStream_t stream) {
-  if (a.decode_order == nullptr) return;
-  int shift = 0;
-  const int max_blocks = (a.max_seq_len + 15) / 16;
-  while ((max_blocks >> shift) >= kBuckets) ++shift;
+  // (the shared-prefix setup kernel may already have built it)
+  if (a.decode_order == nullptr || a.order_ready) return;
   trace_before(K_DECODE_ORDER, stream);
   hipLaunchKernelGGL(decode_order_kernel, dim3(1), dim3(1024), 0, stream, a.qsl, a.seq_lens,
-                     a.num_seqs, 16 / G, shift, a.decode_order);
+                     a.num_seqs, 16 / G, decode_order_shift(a.max_seq_len), a.decode_order);
   trace_after(stream);
 }
 

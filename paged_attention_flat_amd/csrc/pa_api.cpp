@@ -476,7 +476,10 @@ pa_status attention_impl(const void* query, const void* key_cache, const void* v
       e = launch_mixed_bf16(a, s);
     } else {
       if (prefill) e = launch_prefill_bf16(a, s);
-      if (e == hipSuccess && cascade) e = launch_cascade_prefix(a, s);
+      if (e == hipSuccess && cascade) {
+        e = launch_cascade_prefix(a, s);
+        a.order_ready = 1;  // its setup kernel also ranked the decode requests
+      }
       if (e == hipSuccess) e = launch_decode_bf16(a, s);
     }
   }

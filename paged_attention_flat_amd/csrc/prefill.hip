@@ -38,6 +38,7 @@
 // metadata.  Work-group index = KV head fastest: the tiles of one (request, KV
 // head) land on the same XCD (round-robin dispatch over 8 XCDs) and share its
 // L2 copy of that head's K/V.
+#include "decode_body.h"
 #include "prefill_body.h"
 
 namespace pa {
@@ -172,9 +173,11 @@ __global__ __launch_bounds__(1024) void cascade_setup_kernel(
     const int32_t* __restrict__ sharers, int32_t num_sharers, const int32_t* __restrict__ qsl,
     const int32_t* __restrict__ seq_lens, int32_t num_seqs, int32_t dq,
     int32_t* __restrict__ pre_index, int32_t* __restrict__ vtok, int32_t* __restrict__ vpos,
-    int32_t* __restrict__ count) {
+    int32_t* __restrict__ count, int32_t* __restrict__ order, int32_t order_dq,
+    int32_t order_shift) {
   __shared__ int s_scan[1024];
   __shared__ int s_base;
+  __shared__ int hist[kBuckets];
   const int tid = threadIdx.x;
   for (int b = tid; b < num_seqs; b += 1024) pre_index[b] = -1;
   if (tid == 0) s_base = 0;
@@ -211,6 +214,12 @@ __global__ __launch_bounds__(1024) void cascade_setup_kernel(
     __syncthreads();
   }
   if (tid == 0) count[0] = s_base;
+  // the decode order of this step, in the same launch (one kernel boundary
+  // fewer on the step's serial path)
+  if (order != nullptr) {
+    __syncthreads();
+    decode_order_block(qsl, seq_lens, num_seqs, order_dq, order_shift, order, hist, s_scan);
+  }
 }
 
 template <int D, int G>
@@ -240,7 +249,8 @@ void launch_cascade_dg(const AttnArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(cascade_setup_kernel, dim3(1), dim3(1024), 0, stream, a.sharers,
                      a.num_sharers, a.qsl, a.seq_lens, a.num_seqs,
                      min(decode_max_q(G), a.max_query_len), a.pre_index,
-                     a.vtok, a.vpos, a.casc_count);
+                     a.vtok, a.vpos, a.casc_count, a.decode_order, decode_max_q(G),
+                     decode_order_shift(a.max_seq_len));
   trace_after(stream);
   const int tiles = (a.casc_rows_max + TQ - 1) / TQ;
   trace_before(K_CASCADE_PREFIX, stream);
