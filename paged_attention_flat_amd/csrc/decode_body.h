@@ -256,12 +256,19 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& p, int bx, int b
 
   // Fused KV write.  The slot of position p is table[p / 16] * 16 + p % 16
   // ("Model execution", "Flattening a step"), so the only reader of a new
-  // token's entry (for this KV head) is the wave of this work-group that
-  // processes the pair of blocks holding it: that wave writes the token (K
-  // row and V column; E4M3 cache: quantised exactly as pa_kv_write_fp8 does)
-  // and waits for its own stores before it loads that pair.  No barrier: the
-  // other waves never read these entries, and the kernel starts with a clean
-  // vector L1, so the load after the acknowledged store reads the new bytes.
+  // token's entry (for this KV head) is the wave of this unit that processes
+  // the pair of blocks holding it: that wave writes the token (K row and V
+  // column; E4M3 cache: quantised exactly as pa_kv_write_fp8 does) and waits
+  // for its own stores (vmcnt(0)) before it loads that pair.  No barrier:
+  // the other waves never read these entries.  No stale copy can be read
+  // either: the vector L1 is write-through and starts each launch empty, and
+  // within a launch nothing else reads those bytes before the write -- other
+  // units of this request and KV head cover other blocks, other requests'
+  // units read other blocks (the slot rule puts a request's new tokens in its
+  // own last blocks, which no other request reads), and in the persistent
+  // mixed launch the prefill units read prefill requests' blocks only.  So
+  // the load, issued after the stores were acknowledged by this XCD's L2,
+  // finds no L1 line for them and reads the new bytes from that L2.
   // The first token a wave writes is fetched before its first K/V loads are
   // issued, so the write costs no round trip of its own.
   auto own_tok = [&](int i) {
@@ -637,9 +644,11 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& p, int bx, int b
   if (!merged || p.splits == 1 || p.sem == nullptr) return;
 
   // ---- merge of the split partials by the last split to finish ------------
-  // ("combining the partials in a second reduction", here done by whichever
-  // work-group of this (request, KV head) completes last, so the step needs
-  // no second launch).  Only wave 0 stored partials, all of them device-scope
+  // (the split-KV method merges its partials in a separate reduction pass:
+  // "Inside the engine: kernels, CUDA graphs and the life of a request",
+  // section "Prefill has a full grid; decode at batch 1 has almost none";
+  // here that pass is done by whichever work-group of this (request, KV head)
+  // completes last, so the step needs no second launch).  Only wave 0 stored partials, all of them device-scope
   // atomic stores: once the wave's store counter has drained they are visible
   // device-wide, and its lane 0 then counts the arrival.  (A release fence
   // would also write back this XCD's whole L2, which costs microseconds per
