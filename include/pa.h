@@ -256,8 +256,10 @@ pa_status pa_decode_step_noalloc(const void* key, const void* value, void* key_c
  * result is the attention of pa_attention_fwd (up to rounding): causality is
  * kept per row, so a sharer whose context is shorter than the prefix is still
  * exact.  The prefix keys are cut into ranges (one partial each) so that the
- * stage fills the device even for few sharers.  Sharers with more new tokens than the decode kernel packs, or none,
- * are computed as usual.  Workspace: pa_cascade_workspace_size (zeroed once
+ * stage fills the device even for few sharers.  Sharers with more new tokens
+ * than the decode kernel packs, or none, are computed as usual.  The stage
+ * runs first; the rest of the step (the decode rows, and any prefill rows,
+ * in one persistent launch under pa_attention_fwd's rule) follows.  Workspace: pa_cascade_workspace_size (zeroed once
  * like pa_attention_fwd's).  Every other argument and error as
  * pa_attention_fwd with dtype PA_BF16.
  */

@@ -104,17 +104,6 @@ void launch_d(const AttnArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_decode_order(const AttnArgs& a, hipStream_t stream) {
-  switch (a.hq / a.hkv) {
-    case 1: order_dg<1>(a, stream); break;
-    case 2: order_dg<2>(a, stream); break;
-    case 4: order_dg<4>(a, stream); break;
-    case 8: order_dg<8>(a, stream); break;
-    default: order_dg<16>(a, stream); break;
-  }
-  return hipGetLastError();
-}
-
 hipError_t launch_decode_bf16(const AttnArgs& a, hipStream_t stream) {
   if (a.cache_fp8) {
     if (a.d == 64) launch_d<64, true>(a, stream);

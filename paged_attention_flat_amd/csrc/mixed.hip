@@ -29,6 +29,10 @@ namespace pa {
 namespace {
 
 constexpr int kMixedWaves = 8;
+// one work-group in this many starts on the prefill units
+#ifndef PA_MIXED_PREFILL_SHARE
+#define PA_MIXED_PREFILL_SHARE 4
+#endif
 static_assert(PA_PREFILL_WAVES == kMixedWaves && PA_PREFILL_ROW_GROUPS == 1,
               "the mixed kernel runs the prefill body at eight waves, one row group");
 
@@ -88,7 +92,7 @@ void launch_dg(const AttnArgs& a, hipStream_t stream) {
   const int32_t decode_x = a.num_seqs * a.hkv;
   const int32_t decode_units = decode_x * a.splits;
   const int32_t wgs = a.num_cus;
-  const int32_t prefill_first = (wgs + 3) / 4;
+  const int32_t prefill_first = (wgs + PA_MIXED_PREFILL_SHARE - 1) / PA_MIXED_PREFILL_SHARE;
   trace_before(K_MIXED, stream);
   hipLaunchKernelGGL((mixed_kernel<D, G, F8>), dim3(wgs), dim3(64 * kMixedWaves), 0, stream, pp,
                      dp, a.claim, prefill_first, decode_x, decode_units);
@@ -108,10 +112,12 @@ void launch_d(const AttnArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_mixed_bf16(const AttnArgs& a, hipStream_t stream) {
-  hipError_t e = launch_prefill_plan(a, stream);
-  if (e == hipSuccess) e = launch_decode_order(a, stream);
+hipError_t launch_mixed_bf16(const AttnArgs& a0, hipStream_t stream) {
+  // the work list and the decode order come from one launch
+  hipError_t e = launch_prefill_plan(a0, stream, true);
   if (e != hipSuccess) return e;
+  AttnArgs a = a0;
+  a.order_ready = 1;
   if (a.cache_fp8) {
     if (a.d == 64) launch_d<64, true>(a, stream);
     else launch_d<128, true>(a, stream);

@@ -465,21 +465,22 @@ pa_status attention_impl(const void* query, const void* key_cache, const void* v
     // each request and KV head to finish does it).  A step with prefill rows
     // that certainly also has decode rows (more requests than can each hold
     // more than dq of the step's tokens) runs its MFMA-bound prefill units
-    // and its HBM-bound decode units in one persistent launch (mixed.hip),
-    // except with a shared prefix, whose stage must finish before the decode
-    // rows merge it.  Otherwise the matrix-core kernel runs on its own: in
-    // persistent form it is ~4 % slower, which only an overlap repays.
+    // and its HBM-bound decode units in one persistent launch (mixed.hip);
+    // with a shared prefix, the prefix stage runs first, since the sharers'
+    // decode units merge its partials.  Otherwise the matrix-core kernel runs
+    // on its own: in persistent form it is ~4 % slower, which only an
+    // overlap repays.
     const int32_t dq = decode_max_q(group);
     const bool prefill = max_query_len > dq;
     const bool has_decode_rows = (int64_t)num_seqs > (int64_t)num_tokens / (dq + 1);
-    if (prefill && has_decode_rows && !cascade) {
+    if (cascade) {
+      e = launch_cascade_prefix(a, s);
+      a.order_ready = 1;  // its setup kernel also ranked the decode requests
+    }
+    if (e == hipSuccess && prefill && has_decode_rows) {
       e = launch_mixed_bf16(a, s);
-    } else {
+    } else if (e == hipSuccess) {
       if (prefill) e = launch_prefill_bf16(a, s);
-      if (e == hipSuccess && cascade) {
-        e = launch_cascade_prefix(a, s);
-        a.order_ready = 1;  // its setup kernel also ranked the decode requests
-      }
       if (e == hipSuccess) e = launch_decode_bf16(a, s);
     }
   }

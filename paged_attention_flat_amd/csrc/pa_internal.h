@@ -119,11 +119,11 @@ inline int32_t prefill_tile_tokens(int32_t group) {
 hipError_t launch_kv_write_plan(const AttnArgs& a, int32_t tq, hipStream_t stream);
 hipError_t launch_decode_bf16(const AttnArgs& a, hipStream_t stream);
 // The pieces of a step with prefill rows, run as one persistent launch:
-// the matrix-core kernel's work list (and, with a.knew, the write of its
-// tokens; a.claim zeroed), the decode order, then the mixed kernel whose
-// work-groups take prefill units and decode units from two counters.
-hipError_t launch_prefill_plan(const AttnArgs& a, hipStream_t stream);
-hipError_t launch_decode_order(const AttnArgs& a, hipStream_t stream);
+// the matrix-core kernel's work list (a.claim zeroed; with_order: the decode
+// order built beside it; with a.knew, then the write of its tokens), then
+// the mixed kernel whose work-groups take prefill units and decode units
+// from two counters.
+hipError_t launch_prefill_plan(const AttnArgs& a, hipStream_t stream, bool with_order);
 hipError_t launch_mixed_bf16(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t stream);
 // shared-prefix stage: gather the sharers' decode rows, attend them to the

@@ -48,16 +48,26 @@ constexpr int kPlanBuckets = 4096;
 
 // Work list: plan[0] = item count, then (request, query tile) pairs sorted by
 // the number of keys the tile's last row sees, largest first.  `tmp` holds
-// the unsorted list (2 ints per item).  One work-group.
+// the unsorted list (2 ints per item).  Work-group 0 builds it; a second
+// work-group, when launched, ranks the decode requests into `order` (the
+// decode order of the same step, built beside the plan instead of in a
+// launch of its own).
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ qsl,
                                                     const int32_t* __restrict__ seq_lens,
                                                     int32_t num_seqs, int32_t dq, int32_t tq,
                                                     int32_t shift, int32_t* __restrict__ plan,
                                                     int32_t* __restrict__ tmp, int32_t cap,
-                                                    int32_t* __restrict__ claim) {
+                                                    int32_t* __restrict__ claim,
+                                                    int32_t* __restrict__ order,
+                                                    int32_t order_shift) {
   __shared__ int s_scan[1024];
   __shared__ int hist[kPlanBuckets];
   __shared__ int s_base;
+  static_assert(kPlanBuckets == kBuckets, "the decode order shares the plan's histogram");
+  if (blockIdx.x == 1) {
+    decode_order_block(qsl, seq_lens, num_seqs, dq, order_shift, order, hist, s_scan);
+    return;
+  }
   const int tid = threadIdx.x;
   if (tid == 0) s_base = 0;
   // the mixed kernel's work counters start from zero every call
@@ -133,17 +143,20 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(PrefillParams p) {
   prefill_unit<D, G, NW, RG, kBK, F8, CASC>(p, blockIdx.x, sm, threadIdx.x);
 }
 
-// The work list (plan kernel; it also zeroes a.claim) and, when the call
-// writes the step's tokens, the write of the prefill rows' tokens (the decode
-// kernel writes its own rows').
+// The work list (plan kernel; it also zeroes a.claim, and with_order: ranks
+// the decode requests in a second work-group unless that order is already
+// built) and, when the call writes the step's tokens, the write of the
+// prefill rows' tokens (the decode kernel writes its own rows').
 template <int G>
-hipError_t plan_dg(const AttnArgs& a, hipStream_t stream) {
+hipError_t plan_dg(const AttnArgs& a, hipStream_t stream, bool with_order) {
   int shift = 0;
   while ((a.max_seq_len >> shift) >= kPlanBuckets) ++shift;
+  const bool order = with_order && a.decode_order != nullptr && !a.order_ready;
   trace_before(K_PLAN, stream);
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, a.qsl, a.seq_lens, a.num_seqs,
-                     decode_max_q(G), prefill_tile_tokens(G), shift, a.plan, a.plan_tmp,
-                     a.plan_cap, a.claim);
+  hipLaunchKernelGGL(plan_kernel, dim3(order ? 2 : 1), dim3(1024), 0, stream, a.qsl, a.seq_lens,
+                     a.num_seqs, decode_max_q(G), prefill_tile_tokens(G), shift, a.plan,
+                     a.plan_tmp, a.plan_cap, a.claim, order ? a.decode_order : nullptr,
+                     decode_order_shift(a.max_seq_len));
   trace_after(stream);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && a.knew != nullptr) e = launch_kv_write_plan(a, prefill_tile_tokens(G), stream);
@@ -156,7 +169,7 @@ void launch_dg(const AttnArgs& a, hipStream_t stream) {
   constexpr int RG = PA_PREFILL_ROW_GROUPS;
   constexpr int BK = PA_PREFILL_KEYS;
   const PrefillParams p = make_prefill_params(a);
-  if (plan_dg<G>(a, stream) != hipSuccess) return;
+  if (plan_dg<G>(a, stream, false) != hipSuccess) return;
   trace_before(K_PREFILL, stream);
   hipLaunchKernelGGL((prefill_kernel<D, G, NW, RG, BK, F8, false>), dim3(a.plan_cap * a.hkv),
                      dim3(64 * NW), 0, stream, p);
@@ -293,13 +306,13 @@ hipError_t launch_cascade_prefix(const AttnArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_prefill_plan(const AttnArgs& a, hipStream_t stream) {
+hipError_t launch_prefill_plan(const AttnArgs& a, hipStream_t stream, bool with_order) {
   switch (a.hq / a.hkv) {
-    case 1: return plan_dg<1>(a, stream);
-    case 2: return plan_dg<2>(a, stream);
-    case 4: return plan_dg<4>(a, stream);
-    case 8: return plan_dg<8>(a, stream);
-    default: return plan_dg<16>(a, stream);
+    case 1: return plan_dg<1>(a, stream, with_order);
+    case 2: return plan_dg<2>(a, stream, with_order);
+    case 4: return plan_dg<4>(a, stream, with_order);
+    case 8: return plan_dg<8>(a, stream, with_order);
+    default: return plan_dg<16>(a, stream, with_order);
   }
 }
 
