@@ -565,7 +565,12 @@ def bench_main(args, log):
                                  "x 128 dims x 2 B = 4096 B (plus Q and table reads)",
                      "avg_launch_us": dur_us,
                      "timing": "HIP events around the timed steps of the reported launch "
-                               "path, / launches"},
+                               "path, / launches",
+                     "traffic_source": "not measured in this run: profiles/hbm_traffic.json "
+                                       "(rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 per "
+                                       "launch, scaled by a 1 GiB copy), reported only while "
+                                       "the kernel sources hash to the value recorded there, "
+                                       "else null"},
     }
     del runners, base
     torch.cuda.empty_cache()
@@ -952,7 +957,9 @@ def cpu_baseline(args, log):
     processes (one BLAS thread each, N = the cores this process may use, at
     most 16) repeat whole steps of the headline workload for about
     args.cpu_seconds, and bounded samples of the large-batch decode (16
-    requests) and of the long prefill (48 rows) for a third of that each.
+    requests), of the long prefill (48 rows) and of the mixed step (its
+    chunks with 64 decodes; decode rows and 48 chunk rows timed apart) for a
+    third of that each.
     Inputs are generated on the host with the workloads' own seeds and shared
     with the workers as memory-mapped files."""
     import shutil
@@ -1003,6 +1010,41 @@ def cpu_baseline(args, log):
             "value": flops * n / t_work / 1e12, "unit": "TFLOP/s", "cores": workers,
             "sample": f"{n} passes of the full step's KV write (32768 tokens) plus "
                       f"attention of {len(rows)} seeded rows ({flops / 1e9:.2f} GFLOP)"}
+        # mixed chunked-prefill step: its two chunks with 64 decodes drawn by
+        # the workload's rule; the decode rows and 48 seeded chunk rows are
+        # timed apart, and the full step is extrapolated from the two rates
+        step = config_step(5, device="cpu", fill="zero", scale_down={"decodes": 64})
+        qsl = np.asarray(step.query_start_loc)
+        ql = np.diff(qsl)
+        dec_rows = [int(qsl[b]) for b in range(step.num_seqs) if ql[b] == 1]
+        chunks = [b for b in range(step.num_seqs) if ql[b] > 1]
+        pre_rows = sorted(set(int(x) for b in chunks
+                              for x in rng.integers(int(qsl[b]), int(qsl[b + 1]), 24)))
+        pre_flops = 0.0
+        for r in pre_rows:
+            b = int(np.searchsorted(qsl, r, side="right")) - 1
+            pos = int(step.seq_lens[b]) - int(ql[b]) + (r - int(qsl[b]))
+            pre_flops += 4.0 * step.head_dim * step.num_q_heads * (pos + 1)
+        dec_bytes, _ = decode_kernel_bytes(step)
+        _dump_step(step, os.path.join(tmp, "c5d"), rows=dec_rows)
+        _dump_step(step, os.path.join(tmp, "c5p"), rows=pre_rows)
+        del step
+        nd, td, _ = _run_oracle_pool(os.path.join(tmp, "c5d"), workers, args.cpu_seconds / 3)
+        npf, tp, _ = _run_oracle_pool(os.path.join(tmp, "c5p"), workers, args.cpu_seconds / 3)
+        dec_rate = dec_bytes * nd / td          # B/s, KV write included
+        pre_rate = pre_flops * npf / tp         # FLOP/s, KV write included
+        full = config_step(5, device="cpu", with_values=False)
+        full_dec, _ = decode_kernel_bytes(full)
+        full_pre = work_model(full)["prefill_flops"]
+        del full
+        est_ms = (full_dec / dec_rate + full_pre / pre_rate) * 1e3
+        samples["mixed_chunked_prefill_step"] = {
+            "value": est_ms, "unit": "ms per step (extrapolated)", "cores": workers,
+            "decode_GBps": dec_rate / 1e9, "prefill_TFLOPps": pre_rate / 1e12,
+            "sample": f"the step's two 2048-token chunks with 64 decodes drawn by the "
+                      f"workload's rule: {nd} passes of the KV write plus the 64 decode rows "
+                      f"and {npf} passes of the KV write plus {len(pre_rows)} seeded chunk "
+                      f"rows; the full step (4096 decodes) extrapolated from the two rates"}
         head["other_workloads"] = samples
         log(f"cpu oracle samples: {json.dumps(samples)}")
         return head
@@ -1090,7 +1132,7 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args, log)
         # the oracle's samples beside the GPU numbers of the same workloads
-        by_cfg = {3: "large_batch_decode", 4: "long_prefill"}
+        by_cfg = {3: "large_batch_decode", 4: "long_prefill", 5: "mixed_chunked_prefill_step"}
         for cfg, e in zip((3, 4, 5), extras):
             if cfg in by_cfg:
                 e["oracle_cpu"] = cpu["other_workloads"][by_cfg[cfg]]
