@@ -76,6 +76,28 @@ def test_cascade_mixed_step_small(splits):
     check(out, lse, ro, rl, rows, f"cascade small config5 S={splits}")
 
 
+@pytest.mark.parametrize("splits", [1, 3])
+def test_cascade_persistent_mixed_step(splits):
+    # enough decode requests that the host knows decode rows are present: the
+    # prefix stage runs, then the prefill and decode units share one
+    # persistent launch whose sharers' decode units merge the stage's partials
+    import paged_attention_flat_amd as pa
+    step = config_step(5, scale_down=dict(SMALL5, decodes=80, sharers=20))
+    assert step.num_seqs > step.num_tokens // 5 and step.max_query_len > 4
+    prefix = list(step.info["shared_blocks"])
+    sharers = sharers_of(step, prefix)
+    assert len(sharers) >= 10
+    pa.trace_begin()
+    out, lse = run_cascade(step, sharers, prefix, num_splits=splits)
+    names = [n for n, _ in pa.trace_read()]
+    pa.trace_end()
+    assert "cascade_prefix" in names and "mixed_prefill_decode" in names, names
+    assert names.index("cascade_prefix") < names.index("mixed_prefill_decode"), names
+    ro, rl = oracle_plain(step)
+    rows = np.arange(int(step.query_start_loc[-1]))
+    check(out, lse, ro, rl, rows, f"cascade persistent config5 S={splits}")
+
+
 @pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (32, 4), (16, 2)])
 def test_cascade_edge_cases(hq, hkv):
     # sharers: decodes with 1 and 2 new tokens, one whose context ends inside
