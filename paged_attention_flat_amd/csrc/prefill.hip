@@ -9,10 +9,10 @@
 // tensor").  Rows of a request are causal with prior context: row i of a
 // request with q_len new tokens sees positions 0 .. seq_len - q_len + i.
 //
-// MI355X design.  A work-group owns 128 query rows = (128 / G) tokens x the G
+// MI355X design.  A work-group owns 256 query rows = (256 / G) tokens x the G
 // query heads of one KV head (token-major), so each K/V tile staged in LDS
-// serves every head that reads it.  Each of its four waves owns 32 rows and
-// runs 32x32x16 bf16 MFMAs:
+// serves every head that reads it.  Each of its eight waves (two per SIMD)
+// owns 32 rows and runs 32x32x16 bf16 MFMAs:
 //   S^T[key][row] = K[key][:] . Q[row][:]   A = K tile rows from LDS (16-byte
 //                                          reads), B = Q in registers
 //   O^T[d][row]  += V^T[d][keys] P[keys][row]  A = V^T tile (the cache block
@@ -25,9 +25,11 @@
 // the order a lane's P operand carries them in, so one 16-byte LDS read gives
 // the matching V operand.
 //
-// Key tiles are 64 keys (four cache blocks), double-buffered in LDS: the
-// global loads of tile k+1 are issued before the MFMAs of tile k and written
-// to the other buffer afterwards, one barrier per tile.  The running max is
+// Key tiles are 64 keys (four cache blocks); K is double-buffered in LDS and
+// V^T triple-buffered: the global loads of tile k+1 are issued before the
+// MFMAs of tile k and written to LDS afterwards, one barrier per tile, and
+// the P.V MFMAs of tile k-1 are spread through the softmax of tile k (whose
+// exponentials would otherwise run with the matrix core idle).  The running max is
 // only moved when a row's tile max exceeds it by more than 2^8 (base 2): the
 // stale max keeps P <= 256, exact after the final division, and the
 // accumulator rescale is skipped on almost every tile.
