@@ -259,7 +259,9 @@ pa_status pa_decode_step_noalloc(const void* key, const void* value, void* key_c
  * stage fills the device even for few sharers.  Sharers with more new tokens
  * than the decode kernel packs, or none, are computed as usual.  The stage
  * runs first; the rest of the step (the decode rows, and any prefill rows,
- * in one persistent launch under pa_attention_fwd's rule) follows.  Workspace: pa_cascade_workspace_size (zeroed once
+ * in one persistent launch under pa_attention_fwd's rule) follows.  The
+ * decode rows read the remaining blocks as unshared (pa_set_unshared_blocks),
+ * whatever the process-wide setting.  Workspace: pa_cascade_workspace_size (zeroed once
  * like pa_attention_fwd's).  Every other argument and error as
  * pa_attention_fwd with dtype PA_BF16.
  */
@@ -428,6 +430,22 @@ int32_t pa_choose_num_splits(int32_t num_seqs, int32_t max_query_len,
  * that size.
  */
 int32_t pa_capture_size(int32_t num_tokens, int32_t max_size);
+
+/*
+ * pa_set_unshared_blocks -- cache-read hint for later calls in this process.
+ * Block tables may point several requests of a step at the same physical
+ * blocks (prefix caching: "Anatomy of a serving engine"; "Model execution",
+ * "Flattening a step").  on = 1 states that no cache block is read by two
+ * requests of a step; the decode rows of pa_attention_fwd / pa_decode_step
+ * (bf16 cache) then read V with the non-temporal policy, which streams it
+ * without keeping it in L2/MALL (measured: 256 unshared decodes ~8 % faster;
+ * 256 decodes that all re-read one 16K-token prefix ~25 % slower).  Results
+ * are the same either way, bit for bit.  pa_attention_fwd_cascade always
+ * reads that way (its decode rows skip the shared prefix).  Default 0;
+ * process-wide, takes effect for launches issued after the call.  Returns
+ * the previous setting.
+ */
+int32_t pa_set_unshared_blocks(int32_t on);
 
 /* pa_status_string -- static text for a status code (never NULL). */
 const char* pa_status_string(pa_status status);

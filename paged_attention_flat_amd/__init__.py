@@ -27,7 +27,7 @@ __all__ = [
     "decode_step", "decode_step_fp8",
     "decode_step_noalloc", "choose_num_splits", "capture_size", "alloc_cache", "workspace", "trace_begin", "trace_end",
     "trace_read",
-    "kernel_name", "version", "validate_step", "step_problems",
+    "kernel_name", "version", "set_unshared_blocks", "validate_step", "step_problems",
 ]
 
 
@@ -68,6 +68,13 @@ def _stream(stream) -> ctypes.c_void_p:
 
 def version() -> int:
     return int(LIB.pa_version())
+
+
+def set_unshared_blocks(on: bool) -> bool:
+    """pa_set_unshared_blocks: declare that no cache block is read by two
+    requests of a step (later decode reads of V then bypass L2/MALL
+    allocation).  Returns the previous setting."""
+    return bool(LIB.pa_set_unshared_blocks(1 if on else 0))
 
 
 def alloc_cache(num_blocks: int, num_kv_heads: int, head_dim: int, dtype, device="cuda"):

@@ -64,6 +64,7 @@ PROTOTYPES = {
     "pa_capture_size": (_i32, [_i32, _i32]),
     "pa_status_string": (ctypes.c_char_p, [_i32]),
     "pa_version": (_i32, []),
+    "pa_set_unshared_blocks": (_i32, [_i32]),
     "pa_trace_begin": (_i32, [_i32]),
     "pa_trace_end": (_i32, []),
     "pa_trace_read": (_i32, [ctypes.POINTER(_i32), ctypes.POINTER(_f32), _i32]),

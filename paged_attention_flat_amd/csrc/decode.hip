@@ -53,14 +53,18 @@ __global__ __launch_bounds__(1024) void decode_order_kernel(const int32_t* __res
   decode_order_block(qsl, seq_lens, num_seqs, dq, shift, order, hist, part);
 }
 
-template <int D, int G, int NW, int PIPE, bool F8>
+// NTP: the loads that take the non-temporal policy (bf16 cache).  The
+// long-context shape streams K and V that way (measured 9-10 % faster from
+// 16K keys on, equal below).  The many-work-group shape streams V only, and
+// only when the call's blocks are unshared: 8 % faster on 256 unshared
+// requests, 25 % slower where all of them re-read one long prefix, which
+// cached loads serve from L2/MALL; non-temporal K loads (64 bytes of 16
+// rows each) were slower there in either case.
+template <int D, int G, int NW, int PIPE, bool F8, int NTP>
 __global__ __launch_bounds__(64 * NW, (PIPE == 2 && NW < 8 ? 8 / NW : 1)) void decode_kernel(
     DecodeParams p) {
   __shared__ DecodeSmem<D, NW> sm;
-  // the long-context shape (bf16) streams K/V with the non-temporal policy:
-  // measured 9-10 % faster from 16K keys on (equal below); the FP8 and the
-  // many-work-group shapes measured slower with it and keep cached loads
-  decode_unit<D, G, NW, PIPE, F8, PIPE == 2>(p, blockIdx.x, blockIdx.y, sm, threadIdx.x);
+  decode_unit<D, G, NW, PIPE, F8, NTP>(p, blockIdx.x, blockIdx.y, sm, threadIdx.x);
 }
 
 // the counting sort of the decode requests, when the launch ranks them
@@ -83,10 +87,14 @@ void launch_dg(const AttnArgs& a, hipStream_t stream) {
   trace_before(a.splits > 1 ? K_DECODE_SPLIT : K_DECODE, stream);
   if (units <= 2 * (int64_t)a.num_cus) {
     constexpr int NW = PA_DECODE_WAVES_PIPE;
-    hipLaunchKernelGGL((decode_kernel<D, G, NW, 2, F8>), grid, dim3(64 * NW), 0, stream, p);
+    hipLaunchKernelGGL((decode_kernel<D, G, NW, 2, F8, kNtK | kNtV>), grid, dim3(64 * NW), 0,
+                       stream, p);
+  } else if (a.unshared && !F8) {
+    constexpr int NW = PA_DECODE_WAVES_WIDE;
+    hipLaunchKernelGGL((decode_kernel<D, G, NW, 1, F8, kNtV>), grid, dim3(64 * NW), 0, stream, p);
   } else {
     constexpr int NW = PA_DECODE_WAVES_WIDE;
-    hipLaunchKernelGGL((decode_kernel<D, G, NW, 1, F8>), grid, dim3(64 * NW), 0, stream, p);
+    hipLaunchKernelGGL((decode_kernel<D, G, NW, 1, F8, 0>), grid, dim3(64 * NW), 0, stream, p);
   }
   trace_after(stream);
 }

@@ -169,11 +169,20 @@ struct DecodeSmem {
   int last;
 };
 
+// Cache policy of a decode unit's K/V loads (bf16 cache): non-temporal loads
+// are not kept in L2/MALL for other readers.  A stream of whole 128-byte lines
+// gains from them (V: each load covers 512 contiguous bytes of a block); K
+// loads cover 64 bytes of 16 rows, which gains only in the long single
+// decode.  Blocks read by several requests of a step are re-read from HBM
+// under this policy.
+constexpr int kNtK = 1;  // K loads non-temporal
+constexpr int kNtV = 2;  // V loads non-temporal
+
 // One decode work unit: (KV head, request rank) = bx (KV head fastest) and
 // split = by, computed by the NW waves of the calling work-group (tidx: the
-// thread's index in it).  STREAM: K/V
-// loads with the non-temporal policy.  Every exit is work-group uniform.
-template <int D, int G, int NW, int PIPE, bool F8, bool STREAM>
+// thread's index in it).  NTP: kNtK | kNtV, the loads that take the
+// non-temporal policy.  Every exit is work-group uniform.
+template <int D, int G, int NW, int PIPE, bool F8, int NTP>
 __device__ __forceinline__ void decode_unit(const DecodeParams& p, int bx, int by,
                                             DecodeSmem<D, NW>& sm, const int tidx) {
   typedef typename Frag8<F8>::elem CT;
@@ -408,8 +417,12 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& p, int bx, int b
     const CT* ka = kbase + (size_t)pa_ * block_elems + (ra & 15) * D;
     const CT* kb = kbase + (size_t)pb_ * block_elems + (rb & 15) * D;
     const CT* vp = vbase + (size_t)(kg < 2 ? phys0 : phys1) * block_elems;
-    auto ld = [](const CT* ptr) -> RT {
-      if constexpr (STREAM && !F8) return load_stream16(reinterpret_cast<const uint4*>(ptr));
+    auto ldk = [](const CT* ptr) -> RT {
+      if constexpr ((NTP & kNtK) && !F8) return load_stream16(reinterpret_cast<const uint4*>(ptr));
+      else return *reinterpret_cast<const RT*>(ptr);
+    };
+    auto ldv = [](const CT* ptr) -> RT {
+      if constexpr ((NTP & kNtV) && !F8) return load_stream16(reinterpret_cast<const uint4*>(ptr));
       else return *reinterpret_cast<const RT*>(ptr);
     };
     if constexpr (F8) {
@@ -426,12 +439,12 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& p, int bx, int b
     } else {
 #pragma unroll
       for (int st = 0; st < KSTEPS; ++st) {
-        f.a[st] = ld(ka + 32 * st);
-        f.b[st] = ld(kb + 32 * st);
+        f.a[st] = ldk(ka + 32 * st);
+        f.b[st] = ldk(kb + 32 * st);
       }
     }
 #pragma unroll
-    for (int db = 0; db < DB; ++db) f.v[db] = ld(vp + db * 256);
+    for (int db = 0; db < DB; ++db) f.v[db] = ldv(vp + db * 256);
   };
   auto compute = [&](Frag& f, int pr) {
     const int j0 = blk_lo + 2 * pr;

@@ -42,7 +42,7 @@ union MixedSmem {
   DecodeSmem<D, kMixedWaves> d;
 };
 
-template <int D, int G, bool F8>
+template <int D, int G, bool F8, int NTP>
 __global__ __launch_bounds__(64 * kMixedWaves, 1) void mixed_kernel(PrefillParams pp,
                                                                     DecodeParams dp,
                                                                     int32_t* __restrict__ claim,
@@ -80,7 +80,7 @@ __global__ __launch_bounds__(64 * kMixedWaves, 1) void mixed_kernel(PrefillParam
     if (kind == 0)
       prefill_unit<D, G, kMixedWaves, 1, PA_PREFILL_KEYS, F8, false>(pp, u, sm.p, tid);
     else
-      decode_unit<D, G, kMixedWaves, 2, F8, false>(dp, u % decode_x, u / decode_x, sm.d, tid);
+      decode_unit<D, G, kMixedWaves, 2, F8, NTP>(dp, u % decode_x, u / decode_x, sm.d, tid);
     __syncthreads();  // the next unit reuses the shared memory
   }
 }
@@ -94,8 +94,14 @@ void launch_dg(const AttnArgs& a, hipStream_t stream) {
   const int32_t wgs = a.num_cus;
   const int32_t prefill_first = (wgs + PA_MIXED_PREFILL_SHARE - 1) / PA_MIXED_PREFILL_SHARE;
   trace_before(K_MIXED, stream);
-  hipLaunchKernelGGL((mixed_kernel<D, G, F8>), dim3(wgs), dim3(64 * kMixedWaves), 0, stream, pp,
-                     dp, a.claim, prefill_first, decode_x, decode_units);
+  // V streamed non-temporally when the call's blocks are unshared (as in the
+  // many-work-group decode kernel)
+  if (a.unshared && !F8)
+    hipLaunchKernelGGL((mixed_kernel<D, G, F8, kNtV>), dim3(wgs), dim3(64 * kMixedWaves), 0,
+                       stream, pp, dp, a.claim, prefill_first, decode_x, decode_units);
+  else
+    hipLaunchKernelGGL((mixed_kernel<D, G, F8, 0>), dim3(wgs), dim3(64 * kMixedWaves), 0,
+                       stream, pp, dp, a.claim, prefill_first, decode_x, decode_units);
   trace_after(stream);
 }
 

@@ -182,6 +182,12 @@ const char* pa_status_string(pa_status s) {
 
 int32_t pa_version(void) { return 100; }  // 0.1.0
 
+namespace {
+std::atomic<int32_t> g_unshared{0};  // pa_set_unshared_blocks
+}  // namespace
+
+int32_t pa_set_unshared_blocks(int32_t on) { return g_unshared.exchange(on ? 1 : 0); }
+
 const char* pa_kernel_name(int32_t id) {
   switch (id) {
     case K_KV_WRITE: return "kv_write";
@@ -436,6 +442,9 @@ pa_status attention_impl(const void* query, const void* key_cache, const void* v
     a.part_lse = reinterpret_cast<float*>(ws + lay.part_lse);
     a.sem = reinterpret_cast<int32_t*>(ws + lay.sem);
   }
+  // the decode rows' blocks are unshared when the caller says so, and in a
+  // shared-prefix call once the prefix is read by its own stage
+  a.unshared = (cascade || g_unshared.load(std::memory_order_relaxed)) ? 1 : 0;
   a.sharers = cascade ? sharers : nullptr;
   a.num_sharers = cascade ? num_sharers : 0;
   a.pre_blocks = pre_blocks;

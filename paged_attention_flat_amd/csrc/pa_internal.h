@@ -72,6 +72,8 @@ struct AttnArgs {
   int32_t* decode_order;  // nullable: count + ranked decode requests
   int32_t* claim;         // [2] work counters of the mixed kernel (prefill, decode)
   int32_t order_ready;    // 1: decode_order was already built this call
+  int32_t unshared;       // 1: no cache block is read by two requests of the step
+                          //    (the many-unit decode then streams V non-temporally)
   int32_t num_cus;        // compute units of the current device
   int32_t* sem;           // nullable: zeroed arrival counters, one per (request, KV head)
   int32_t cache_fp8;      // 1: kc / vc hold E4M3 codes (query and out bf16)

@@ -247,3 +247,15 @@ def test_workspace_init_validation(lib):
     assert lib.pa_attention_workspace_init(None, 0, None) == 0
     assert lib.pa_attention_workspace_init(None, 64, None) == 1
     assert lib.pa_attention_workspace_init(ctypes.c_void_p(260), 64, None) == 2
+
+
+def test_unshared_blocks_hint(lib):
+    # a host-side setting: returns the previous value, any nonzero means on
+    before = lib.pa_set_unshared_blocks(0)
+    try:
+        assert lib.pa_set_unshared_blocks(1) == 0
+        assert lib.pa_set_unshared_blocks(7) == 1
+        assert lib.pa_set_unshared_blocks(0) == 1
+        assert lib.pa_set_unshared_blocks(0) == 0
+    finally:
+        lib.pa_set_unshared_blocks(before)

@@ -1,0 +1,81 @@
+"""The unshared-blocks hint (pa_set_unshared_blocks) changes only the cache
+policy of the decode rows' V loads: every output, lse and pool byte must be
+the same as without it, on the many-work-group decode shape, on a mixed step
+(persistent launch) and through the one-call step; and both must match the
+fp64 oracle at the usual bars (output 2e-2, lse 1e-3)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import config_step, raw_numpy
+
+pytestmark = pytest.mark.gpu
+
+
+def run_step(step, hint, fused):
+    import paged_attention_flat_amd as pa
+    dev = "cuda"
+    g = {n: getattr(step, n).to(dev).contiguous() for n in ("query", "key", "value",
+                                                              "k_pool", "v_pool")}
+    qsl = torch.as_tensor(step.query_start_loc).to(dev)
+    sl = torch.as_tensor(step.seq_lens).to(dev)
+    bt = torch.as_tensor(step.block_tables).to(dev)
+    sm = torch.as_tensor(step.slot_mapping).to(dev)
+    prev = pa.set_unshared_blocks(hint)
+    try:
+        if fused:
+            out, lse = pa.decode_step(g["key"], g["value"], g["k_pool"], g["v_pool"], sm,
+                                      g["query"], qsl, sl, bt, step.max_query_len,
+                                      step.max_seq_len, step.scale)
+        else:
+            pa.kv_write(g["key"], g["value"], g["k_pool"], g["v_pool"], sm)
+            out, lse = pa.attention(g["query"], g["k_pool"], g["v_pool"], qsl, sl, bt,
+                                    step.max_query_len, step.max_seq_len, step.scale)
+        torch.cuda.synchronize()
+    finally:
+        pa.set_unshared_blocks(prev)
+    n = int(step.query_start_loc[-1])
+    return out[:n].cpu(), lse[:n].cpu(), g["k_pool"].cpu(), g["v_pool"].cpu()
+
+
+def check_oracle(step, out, lse):
+    kp, vp = oracle.kv_write(raw_numpy(step.key), raw_numpy(step.value), raw_numpy(step.k_pool),
+                             raw_numpy(step.v_pool), step.slot_mapping)
+    ro, rl = oracle.attention(raw_numpy(step.query), kp, vp, step.query_start_loc,
+                              step.seq_lens, step.block_tables, step.scale, step.num_kv_heads,
+                              step.dtype)
+    n = out.shape[0]
+    o = out.float().double().numpy()
+    assert np.isfinite(o).all()
+    assert float(np.abs(o - ro[:n]).max()) <= 2e-2
+    assert float(np.linalg.norm(o - ro[:n]) / np.linalg.norm(ro[:n])) <= 2e-2
+    assert float(np.abs(lse.double().numpy() - rl[:n]).max()) <= 1e-3
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_many_unit_decode_same_with_hint(fused):
+    # 96 decodes x 8 KV heads = 768 work units: the many-work-group shape
+    step = config_step(3, scale_down={"batch": 96, "lo": 200, "hi": 1200})
+    a = run_step(step, False, fused)
+    b = run_step(step, True, fused)
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.uint8) if x.dtype == torch.bfloat16 else x,
+                           y.view(torch.uint8) if y.dtype == torch.bfloat16 else y)
+    check_oracle(step, b[0], b[1])
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_mixed_step_same_with_hint(fused):
+    # two prefill chunks and 120 decodes: the persistent mixed launch
+    step = config_step(5, scale_down={"chunk": 90, "priors": (70, 300), "decodes": 120,
+                                      "lo": 20, "hi": 900, "prefix": 64, "sharers": 30,
+                                      "stride": 64})
+    assert step.num_seqs > step.num_tokens // 5
+    a = run_step(step, False, fused)
+    b = run_step(step, True, fused)
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.uint8) if x.dtype == torch.bfloat16 else x,
+                           y.view(torch.uint8) if y.dtype == torch.bfloat16 else y)
+    check_oracle(step, b[0], b[1])
