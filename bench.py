@@ -174,7 +174,8 @@ class StepRunner:
     """Enqueues one step (KV write + attention) on the current stream, calling
     the C ABI directly with pre-marshalled arguments."""
 
-    def __init__(self, step, dev, num_splits, pools=None, cascade=None, fused=False):
+    def __init__(self, step, dev, num_splits, pools=None, cascade=None, fused=False,
+                 unshared=False):
         import ctypes
 
         import torch
@@ -183,6 +184,9 @@ class StepRunner:
         from paged_attention_flat_amd import _lib
         self.pa, self.lib, self.ctypes, self.torch = pa, _lib.LIB, ctypes, torch
         self.step = step
+        # the caller's statement that no block is read by two requests
+        # (pa_set_unshared_blocks), in force for this runner's launches only
+        self.unshared = unshared
         g = {}
         for name in ("query", "key", "value"):
             g[name] = getattr(step, name).to(dev).contiguous()
@@ -259,6 +263,16 @@ class StepRunner:
             self.attn_fn = self.lib.pa_attention_fwd_cascade
 
     def __call__(self):
+        if self.unshared:
+            prev = self.lib.pa_set_unshared_blocks(1)
+            try:
+                self._launch()
+            finally:
+                self.lib.pa_set_unshared_blocks(prev)
+        else:
+            self._launch()
+
+    def _launch(self):
         s = self.ctypes.c_void_p(self.torch.cuda.current_stream().cuda_stream)
         if self.fused:
             st = self.step_fn(*self.step_args, s)
@@ -423,7 +437,8 @@ class RopeRunner:
 
 
 # every workload a report times, by the name of its profile summary
-WORKLOADS = ("long_context_decode", "large_batch_decode", "long_prefill",
+WORKLOADS = ("long_context_decode", "large_batch_decode", "large_batch_decode_unshared",
+             "long_prefill",
              "mixed_chunked_prefill_step", "mixed_chunked_prefill_step_shared_prefix",
              "long_context_decode_fp8", "large_batch_decode_fp8", "long_prefill_fp8",
              "rope_kv_write", "shared_prefix_plain", "shared_prefix_read_once")
@@ -439,6 +454,9 @@ def workload_runners(name, dev, args, pools=None):
     launch where it can and falls back to the two calls otherwise."""
     from workloads import config_step, fp8_cache, shared_prefix_step
     cfg_of = {v: k for k, v in PROFILE_NAMES.items()}
+    unshared = name.endswith("_unshared")
+    if unshared:
+        name = name[:-len("_unshared")]
     base = name[:-4] if name.endswith("_fp8") else name
     if name.startswith("shared_prefix"):
         step = shared_prefix_step(256, 16384, 0, 512, 11, device=dev, fill="zero")
@@ -462,7 +480,7 @@ def workload_runners(name, dev, args, pools=None):
         sharers = [b for b in range(step.num_seqs) if list(bt[b, :P]) == prefix]
         r = StepRunner(step, dev, 0, pools=pools, cascade=(sharers, prefix))
         return step, [r], 1, args.extra_steps, 3
-    first = StepRunner(step, dev, 0, pools=pools, fused=True)
+    first = StepRunner(step, dev, 0, pools=pools, fused=True, unshared=unshared)
     if cfg != 2:
         return step, [first], 1, args.extra_steps, 3
     runners = [first]
@@ -853,6 +871,25 @@ def bench_extra(cfg, args, log):
                                "roofline_frac": t_roof / (us * 1e-6),
                                "traffic": measured_traffic(PROFILE_NAMES[cfg],
                                                            "mixed_prefill_decode")}
+    if cfg == 3:
+        # the same step with the caller's statement that no block is shared
+        # (pa_set_unshared_blocks): V streamed non-temporally
+        _, (ru,), _, nu, wu = workload_runners(PROFILE_NAMES[cfg] + "_unshared", dev, args,
+                                               pools=(r.g["kc"], r.g["vc"]))
+        ums, umode = time_steps([ru], nu, wu, not args.eager, log)
+        ukt = kernel_times([ru], min(nu, 20), log)
+        kb, _ = decode_kernel_bytes(step)
+        ugbs = kb / (ukt["decode"]["avg_us"] * 1e-6) / 1e9 if "decode" in ukt else None
+        out["unshared_blocks_hint"] = {
+            "ms_per_step": ums, "launch": umode,
+            "step_GBps": wm["bytes"] / (ums * 1e-3) / 1e9,
+            "kernels_us": attributed_us(ukt, ums),
+            "kernels_us_eager_traced": {k: round(v["avg_us"], 2) for k, v in ukt.items()},
+            "decode_kernel": {"bytes": kb, "GBps": ugbs,
+                              "frac_hbm": None if ugbs is None else ugbs / PEAK_HBM_GBS,
+                              "traffic": measured_traffic(PROFILE_NAMES[cfg] + "_unshared",
+                                                          "decode")}}
+        del ru
     if cfg == 5:
         t_roof = max(wm["bytes"] / (PEAK_HBM_GBS * 1e9), wm["flops"] / (PEAK_BF16_TFLOPS * 1e12))
         out["step_roofline_frac"] = t_roof / (ms * 1e-3)
