@@ -53,13 +53,13 @@ __global__ __launch_bounds__(1024) void decode_order_kernel(const int32_t* __res
   decode_order_block(qsl, seq_lens, num_seqs, dq, shift, order, hist, part);
 }
 
-// NTP: the loads that take the non-temporal policy (bf16 cache).  The
-// long-context shape streams K and V that way (measured 9-10 % faster from
+// NTP: the loads that take the non-temporal policy.  The long-context shape
+// streams K and V that way with a bf16 cache (measured 9-10 % faster from
 // 16K keys on, equal below).  The many-work-group shape streams V only, and
-// only when the call's blocks are unshared: 8 % faster on 256 unshared
-// requests, 25 % slower where all of them re-read one long prefix, which
-// cached loads serve from L2/MALL; non-temporal K loads (64 bytes of 16
-// rows each) were slower there in either case.
+// only when the call's blocks are unshared: 8 % (bf16) and 9 % (E4M3) faster
+// on 256 unshared requests, 25 % slower where all of them re-read one long
+// prefix, which cached loads serve from L2/MALL; non-temporal K loads (64
+// bytes of 16 rows each) were slower there in either case.
 template <int D, int G, int NW, int PIPE, bool F8, int NTP>
 __global__ __launch_bounds__(64 * NW, (PIPE == 2 && NW < 8 ? 8 / NW : 1)) void decode_kernel(
     DecodeParams p) {
@@ -89,7 +89,7 @@ void launch_dg(const AttnArgs& a, hipStream_t stream) {
     constexpr int NW = PA_DECODE_WAVES_PIPE;
     hipLaunchKernelGGL((decode_kernel<D, G, NW, 2, F8, kNtK | kNtV>), grid, dim3(64 * NW), 0,
                        stream, p);
-  } else if (a.unshared && !F8) {
+  } else if (a.unshared) {
     constexpr int NW = PA_DECODE_WAVES_WIDE;
     hipLaunchKernelGGL((decode_kernel<D, G, NW, 1, F8, kNtV>), grid, dim3(64 * NW), 0, stream, p);
   } else {

@@ -169,13 +169,14 @@ struct DecodeSmem {
   int last;
 };
 
-// Cache policy of a decode unit's K/V loads (bf16 cache): non-temporal loads
+// Cache policy of a decode unit's K/V loads: non-temporal loads
 // are not kept in L2/MALL for other readers.  A stream of whole 128-byte lines
 // gains from them (V: each load covers 512 contiguous bytes of a block); K
 // loads cover 64 bytes of 16 rows, which gains only in the long single
 // decode.  Blocks read by several requests of a step are re-read from HBM
 // under this policy.
-constexpr int kNtK = 1;  // K loads non-temporal
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+constexpr int kNtK = 1;  // K loads non-temporal (bf16 cache)
 constexpr int kNtV = 2;  // V loads non-temporal
 
 // One decode work unit: (KV head, request rank) = bx (KV head fastest) and
@@ -422,8 +423,15 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& p, int bx, int b
       else return *reinterpret_cast<const RT*>(ptr);
     };
     auto ldv = [](const CT* ptr) -> RT {
-      if constexpr ((NTP & kNtV) && !F8) return load_stream16(reinterpret_cast<const uint4*>(ptr));
-      else return *reinterpret_cast<const RT*>(ptr);
+      if constexpr ((NTP & kNtV) && !F8) {
+        return load_stream16(reinterpret_cast<const uint4*>(ptr));
+      } else if constexpr ((NTP & kNtV) && F8) {
+        // 8 codes: 256 contiguous bytes per 16 lanes, whole lines as for bf16
+        const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(ptr));
+        return make_uint2(v.x, v.y);
+      } else {
+        return *reinterpret_cast<const RT*>(ptr);
+      }
     };
     if constexpr (F8) {
       // 16 codes per load: steps 2t and 2t+1 (kd(2t + 1) = kd(2t) + 8)

@@ -96,7 +96,7 @@ void launch_dg(const AttnArgs& a, hipStream_t stream) {
   trace_before(K_MIXED, stream);
   // V streamed non-temporally when the call's blocks are unshared (as in the
   // many-work-group decode kernel)
-  if (a.unshared && !F8)
+  if (a.unshared)
     hipLaunchKernelGGL((mixed_kernel<D, G, F8, kNtV>), dim3(wgs), dim3(64 * kMixedWaves), 0,
                        stream, pp, dp, a.claim, prefill_first, decode_x, decode_units);
   else

@@ -1,8 +1,9 @@
 """The unshared-blocks hint (pa_set_unshared_blocks) changes only the cache
 policy of the decode rows' V loads: every output, lse and pool byte must be
-the same as without it, on the many-work-group decode shape, on a mixed step
-(persistent launch) and through the one-call step; and both must match the
-fp64 oracle at the usual bars (output 2e-2, lse 1e-3)."""
+the same as without it, on the many-work-group decode shape (bf16 and E4M3
+caches), on a mixed step (persistent launch) and through the one-call step;
+and both must match the fp64 oracle at the usual bars (output 2e-2, lse
+1e-3)."""
 
 import numpy as np
 import pytest
@@ -79,3 +80,47 @@ def test_mixed_step_same_with_hint(fused):
         assert torch.equal(x.view(torch.uint8) if x.dtype == torch.bfloat16 else x,
                            y.view(torch.uint8) if y.dtype == torch.bfloat16 else y)
     check_oracle(step, b[0], b[1])
+
+
+def run_step_fp8(step, hint):
+    import paged_attention_flat_amd as pa
+    dev = "cuda"
+    g = {n: getattr(step, n).to(dev).contiguous()
+         for n in ("query", "key", "value", "k_pool", "v_pool", "k_scale", "v_scale")}
+    qsl = torch.as_tensor(step.query_start_loc).to(dev)
+    sl = torch.as_tensor(step.seq_lens).to(dev)
+    bt = torch.as_tensor(step.block_tables).to(dev)
+    sm = torch.as_tensor(step.slot_mapping).to(dev)
+    prev = pa.set_unshared_blocks(hint)
+    try:
+        out, lse = pa.decode_step_fp8(g["key"], g["value"], g["k_pool"], g["v_pool"], sm,
+                                      g["k_scale"], g["v_scale"], g["query"], qsl, sl, bt,
+                                      step.max_query_len, step.max_seq_len, step.scale)
+        torch.cuda.synchronize()
+    finally:
+        pa.set_unshared_blocks(prev)
+    n = int(step.query_start_loc[-1])
+    return out[:n].cpu(), lse[:n].cpu(), g["k_pool"].cpu(), g["v_pool"].cpu()
+
+
+def test_many_unit_decode_fp8_same_with_hint():
+    # E4M3 cache: the V codes streamed non-temporally give the same bytes
+    from workloads import fp8_cache
+    step = fp8_cache(config_step(3, scale_down={"batch": 96, "lo": 200, "hi": 1200}), 3)
+    a = run_step_fp8(step, False)
+    b = run_step_fp8(step, True)
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.uint8) if x.dtype == torch.bfloat16 else x,
+                           y.view(torch.uint8) if y.dtype == torch.bfloat16 else y)
+    kp, vp = oracle.kv_write_fp8(raw_numpy(step.key), raw_numpy(step.value),
+                                 raw_numpy(step.k_pool), raw_numpy(step.v_pool),
+                                 step.slot_mapping, step.k_scale.cpu().numpy(),
+                                 step.v_scale.cpu().numpy(), step.dtype)
+    ro, rl = oracle.attention_fp8(raw_numpy(step.query), kp, vp, step.k_scale.cpu().numpy(),
+                                  step.v_scale.cpu().numpy(), step.query_start_loc,
+                                  step.seq_lens, step.block_tables, step.scale,
+                                  step.num_kv_heads, query_dtype=step.dtype)
+    n = b[0].shape[0]
+    o = b[0].float().double().numpy()
+    assert float(np.abs(o - ro[:n]).max()) <= 2e-2
+    assert float(np.abs(b[1].double().numpy() - rl[:n]).max()) <= 1e-3
