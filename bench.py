@@ -438,7 +438,7 @@ class RopeRunner:
 
 # every workload a report times, by the name of its profile summary
 WORKLOADS = ("long_context_decode", "large_batch_decode", "large_batch_decode_unshared",
-             "long_prefill",
+             "large_batch_decode_fp8_unshared", "long_prefill",
              "mixed_chunked_prefill_step", "mixed_chunked_prefill_step_shared_prefix",
              "long_context_decode_fp8", "large_batch_decode_fp8", "long_prefill_fp8",
              "rope_kv_write", "shared_prefix_plain", "shared_prefix_read_once")
@@ -730,6 +730,23 @@ def bench_fp8(args, log):
                                      "frac_mfma": tf / PEAK_BF16_TFLOPS,
                                      "traffic": measured_traffic(PROFILE_NAMES[cfg] + "_fp8",
                                                                  "prefill_mfma")}
+        if cfg == 3:
+            # with the caller's statement that no block is shared
+            wname = PROFILE_NAMES[cfg] + "_fp8_unshared"
+            _, (ru,), _, nu, wu = workload_runners(wname, dev, args,
+                                                   pools=(runners[0].g["kc"], runners[0].g["vc"]))
+            ums, umode = time_steps([ru], nu, wu, not args.eager, log)
+            ukt = kernel_times([ru], min(nu, 20), log)
+            kb, _ = decode_kernel_bytes(step)
+            ugbs = kb / (ukt["decode"]["avg_us"] * 1e-6) / 1e9 if "decode" in ukt else None
+            rec["unshared_blocks_hint"] = {
+                "ms_per_step": ums, "launch": umode,
+                "kernels_us": attributed_us(ukt, ums),
+                "kernels_us_eager_traced": {k: round(v["avg_us"], 2) for k, v in ukt.items()},
+                "decode_kernel": {"bytes": kb, "GBps": ugbs,
+                                  "frac_hbm": None if ugbs is None else ugbs / PEAK_HBM_GBS,
+                                  "traffic": measured_traffic(wname, "decode")}}
+            del ru
         log(f"fp8 config{cfg}: {json.dumps(rec)}")
         out.append(rec)
         del runners, step
