@@ -443,8 +443,9 @@ int32_t pa_capture_size(int32_t num_tokens, int32_t max_size);
  * 256 decodes that all re-read one 16K-token prefix ~25 % slower).  Results
  * are the same either way, bit for bit.  pa_attention_fwd_cascade always
  * reads that way (its decode rows skip the shared prefix).  Default 0;
- * process-wide, takes effect for launches issued after the call.  Returns
- * the previous setting.
+ * process-wide, takes effect for launches issued after the call (a captured
+ * HIP graph keeps the loads it was captured with).  Returns the previous
+ * setting.
  */
 int32_t pa_set_unshared_blocks(int32_t on);
 
