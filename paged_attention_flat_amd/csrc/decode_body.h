@@ -175,7 +175,6 @@ struct DecodeSmem {
 // loads cover 64 bytes of 16 rows, which gains only in the long single
 // decode.  Blocks read by several requests of a step are re-read from HBM
 // under this policy.
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 constexpr int kNtK = 1;  // K loads non-temporal (bf16 cache)
 constexpr int kNtV = 2;  // V loads non-temporal
 
@@ -427,8 +426,7 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& p, int bx, int b
         return load_stream16(reinterpret_cast<const uint4*>(ptr));
       } else if constexpr ((NTP & kNtV) && F8) {
         // 8 codes: 256 contiguous bytes per 16 lanes, whole lines as for bf16
-        const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(ptr));
-        return make_uint2(v.x, v.y);
+        return load_stream8(reinterpret_cast<const uint2*>(ptr));
       } else {
         return *reinterpret_cast<const RT*>(ptr);
       }

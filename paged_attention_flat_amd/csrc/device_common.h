@@ -108,6 +108,12 @@ __device__ __forceinline__ uint4 load_stream16(const uint4* p) {
   const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+// the same for 8 bytes
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 load_stream8(const uint2* p) {
+  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return make_uint2(v.x, v.y);
+}
 
 // max / sum of v over lanes i and i ^ 32 with one VALU lane-half swap
 // (v_permlane32_swap exchanges the upper half of its first operand with the

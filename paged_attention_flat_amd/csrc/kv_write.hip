@@ -40,8 +40,10 @@ __device__ __forceinline__ void write_tokens(const E* __restrict__ key,
     int64_t s = slots[t0 + ti];
     if (s >= num_slots) s = -1;  // out of the pool: dropped like a padded token
     const size_t src = ((size_t)(t0 + ti) * hkv + h) * d;
-    const uint4 kv = reinterpret_cast<const uint4*>(key + src)[part];
-    const uint4 vv = reinterpret_cast<const uint4*>(value + src)[part];
+    // the new tokens are read once: non-temporal loads (the cache rows they
+    // are stored to stay cached for the attention that follows)
+    const uint4 kv = load_stream16(reinterpret_cast<const uint4*>(key + src) + part);
+    const uint4 vv = load_stream16(reinterpret_cast<const uint4*>(value + src) + part);
     if (part == 0) sslot[ti] = s;
     reinterpret_cast<uint4*>(&vrow[ti][0])[part] = vv;
     if (s < 0) continue;
@@ -189,6 +191,10 @@ struct Piece4;  // four elements of E as one load / store
 template <>
 struct Piece4<uint16_t> {
   typedef uint2 T;
+  // a read-once input row: non-temporal load
+  static __device__ __forceinline__ T load(const uint16_t* p) {
+    return load_stream8(reinterpret_cast<const uint2*>(p));
+  }
   static __device__ __forceinline__ void get(T v, float* f) {
     f[0] = __uint_as_float(v.x << 16);
     f[1] = __uint_as_float(v.x & 0xffff0000u);
@@ -202,6 +208,9 @@ struct Piece4<uint16_t> {
 template <>
 struct Piece4<uint32_t> {
   typedef uint4 T;
+  static __device__ __forceinline__ T load(const uint32_t* p) {
+    return load_stream16(reinterpret_cast<const uint4*>(p));
+  }
   static __device__ __forceinline__ void get(T v, float* f) {
     f[0] = __uint_as_float(v.x);
     f[1] = __uint_as_float(v.y);
@@ -274,8 +283,8 @@ __global__ __launch_bounds__(256) void rope_kv_write_kernel(
     if (ti >= ntok || p < 0) continue;
     const size_t src = ((size_t)(t0 + ti) * hkv + h) * d + 4 * pc;
     float lo[4], hi[4];
-    Piece4<E>::get(*reinterpret_cast<const P4*>(key + src), lo);
-    Piece4<E>::get(*reinterpret_cast<const P4*>(key + src + half), hi);
+    Piece4<E>::get(Piece4<E>::load(key + src), lo);
+    Piece4<E>::get(Piece4<E>::load(key + src + half), hi);
     const float* row = &scs[ti][4 * pc];
     rotate4(lo, hi, *reinterpret_cast<const float4*>(row),
             *reinterpret_cast<const float4*>(row + half));
@@ -293,8 +302,8 @@ __global__ __launch_bounds__(256) void rope_kv_write_kernel(
     if (ti >= ntok || p < 0) continue;
     E* qrow = query + ((size_t)(t0 + ti) * hq + h * G + g) * d + 4 * pc;
     float lo[4], hi[4];
-    Piece4<E>::get(*reinterpret_cast<const P4*>(qrow), lo);
-    Piece4<E>::get(*reinterpret_cast<const P4*>(qrow + half), hi);
+    Piece4<E>::get(Piece4<E>::load(qrow), lo);
+    Piece4<E>::get(Piece4<E>::load(qrow + half), hi);
     const float* row = &scs[ti][4 * pc];
     rotate4(lo, hi, *reinterpret_cast<const float4*>(row),
             *reinterpret_cast<const float4*>(row + half));
@@ -307,7 +316,8 @@ __global__ __launch_bounds__(256) void rope_kv_write_kernel(
     const int ti = c / cpr, part = c - ti * cpr;
     if (ti >= ntok) break;
     const size_t src = ((size_t)(t0 + ti) * hkv + h) * d;
-    reinterpret_cast<uint4*>(&vrow[ti][0])[part] = reinterpret_cast<const uint4*>(value + src)[part];
+    reinterpret_cast<uint4*>(&vrow[ti][0])[part] =
+        load_stream16(reinterpret_cast<const uint4*>(value + src) + part);
   }
   __syncthreads();
   for (int e = tid; e < kTok * d; e += 256) {
