@@ -60,8 +60,20 @@ __global__ __launch_bounds__(1024) void decode_order_kernel(const int32_t* __res
 // on 256 unshared requests, 25 % slower where all of them re-read one long
 // prefix, which cached loads serve from L2/MALL; non-temporal K loads (64
 // bytes of 16 rows each) were slower there in either case.
+//
+// Waves per SIMD the register allocation must allow: two for the two-
+// fragment-set shape at four waves; four for the bf16 one-pair shape at four
+// waves (118 VGPRs, four work-groups per CU; left free, the compiler takes
+// 115 VGPRs + 32 AGPRs and only three fit, which measured 1 % slower on 256
+// unshared requests and 3 % on the shared-prefix decode); one otherwise (the
+// E4M3 one-pair shape held to four waves measured 0.5 % slower than at three,
+// and five waves of either dtype spill).
+constexpr int decode_min_waves(int nw, int pipe, bool f8) {
+  return pipe == 2 ? (nw < 8 ? 8 / nw : 1) : (nw == 4 && !f8 ? 4 : 1);
+}
+
 template <int D, int G, int NW, int PIPE, bool F8, int NTP>
-__global__ __launch_bounds__(64 * NW, (PIPE == 2 && NW < 8 ? 8 / NW : 1)) void decode_kernel(
+__global__ __launch_bounds__(64 * NW, decode_min_waves(NW, PIPE, F8)) void decode_kernel(
     DecodeParams p) {
   __shared__ DecodeSmem<D, NW> sm;
   decode_unit<D, G, NW, PIPE, F8, NTP>(p, blockIdx.x, blockIdx.y, sm, threadIdx.x);
