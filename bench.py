@@ -231,7 +231,7 @@ class StepRunner:
                               step.num_blocks, ctypes.c_float(step.scale), self.splits,
                               P(g["out"]), P(g["lse"]), P(g["ws"]), ws, code]
             self.kv_fn, self.attn_fn = self.lib.pa_kv_write, self.lib.pa_attention_fwd
-        self.fused = fused and cascade is None
+        self.fused = fused
         if self.fused and self.fp8:
             # one call: quantising KV write + attention (pa_decode_step_fp8):
             # (key, value, caches, slots, scales, query) + attention's metadata on
@@ -261,6 +261,12 @@ class StepRunner:
                               P(g["sharers"]), g["sharers"].numel(), P(g["prefix"]),
                               g["prefix"].numel(), P(g["out"]), P(g["lse"]), P(g["ws"]), need]
             self.attn_fn = self.lib.pa_attention_fwd_cascade
+            if self.fused:
+                # one call: KV write + shared-prefix attention (pa_decode_step_cascade):
+                # (key, value, caches, slots) + the cascade's arguments without its caches
+                self.step_args = ([P(g["key"]), P(g["value"]), P(g["kc"]), P(g["vc"]),
+                                   P(g["sm"])] + self.attn_args[:1] + self.attn_args[3:])
+                self.step_fn = self.lib.pa_decode_step_cascade
 
     def __call__(self):
         if self.unshared:
@@ -463,7 +469,7 @@ def workload_runners(name, dev, args, pools=None):
         casc = None
         if name == "shared_prefix_read_once":
             casc = (list(range(step.num_seqs)), list(step.info["shared_blocks"]))
-        r = StepRunner(step, dev, 0, pools=pools, cascade=casc, fused=casc is None)
+        r = StepRunner(step, dev, 0, pools=pools, cascade=casc, fused=True)
         return step, [r], 1, args.extra_steps, 3
     if name == "rope_kv_write":
         step = config_step(4, device=dev, fill="zero")
@@ -478,7 +484,7 @@ def workload_runners(name, dev, args, pools=None):
         P = len(prefix)
         bt = step.block_tables
         sharers = [b for b in range(step.num_seqs) if list(bt[b, :P]) == prefix]
-        r = StepRunner(step, dev, 0, pools=pools, cascade=(sharers, prefix))
+        r = StepRunner(step, dev, 0, pools=pools, cascade=(sharers, prefix), fused=True)
         return step, [r], 1, args.extra_steps, 3
     first = StepRunner(step, dev, 0, pools=pools, fused=True, unshared=unshared)
     if cfg != 2:
@@ -815,8 +821,14 @@ def bench_shared_prefix(args, log):
         res[name] = {"ms_per_step": ms, "step_GBps_unique": wm["bytes"] / (ms * 1e-3) / 1e9,
                      "kernels_us": attributed_us(kt, ms),
                      "kernels_us_eager_traced": {k: round(v["avg_us"], 2) for k, v in kt.items()}}
+    # context: the same read-once step as two calls (pa_kv_write, then
+    # pa_attention_fwd_cascade with its own setup launch)
+    r2 = StepRunner(step, dev, 0, pools=(r.g["kc"], r.g["vc"]), cascade=(
+        list(range(step.num_seqs)), list(step.info["shared_blocks"])), fused=False)
+    ms2, _ = time_steps([r2], n, warm, not args.eager, log)
+    res["shared_prefix_read_once"]["two_calls_ms_per_step"] = ms2
     log(f"shared prefix: {json.dumps(res)}")
-    del r, rc, step
+    del r, rc, r2, step
     torch.cuda.empty_cache()
     return res
 
@@ -915,13 +927,21 @@ def bench_extra(cfg, args, log):
                                              pools=(r.g["kc"], r.g["vc"]))
         cms, _ = time_steps([rc], n, warm, not args.eager, log)
         ckt = kernel_times([rc], min(n, 20), log)
+        # context: the same step as two calls (pa_kv_write, pa_attention_fwd_cascade)
+        prefix = list(step.info["shared_blocks"])
+        sharers = [b for b in range(step.num_seqs)
+                   if list(step.block_tables[b, :len(prefix)]) == prefix]
+        r2 = StepRunner(step, dev, 0, pools=(r.g["kc"], r.g["vc"]), cascade=(sharers, prefix),
+                        fused=False)
+        ms2, _ = time_steps([r2], n, warm, not args.eager, log)
         out["shared_prefix_read_once"] = {
             "sharers": int(rc.g["sharers"].numel()), "prefix_blocks": int(rc.g["prefix"].numel()),
             "ms_per_step": cms,
             "step_GBps": wm["bytes"] / (cms * 1e-3) / 1e9,
             "kernels_us": attributed_us(ckt, cms),
-            "kernels_us_eager_traced": {k: round(v["avg_us"], 2) for k, v in ckt.items()}}
-        del rc
+            "kernels_us_eager_traced": {k: round(v["avg_us"], 2) for k, v in ckt.items()},
+            "two_calls_ms_per_step": ms2}
+        del rc, r2
     log(f"config{cfg}: {json.dumps(out)}")
     del r
     torch.cuda.empty_cache()

@@ -287,6 +287,35 @@ size_t pa_cascade_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t n
                                  int32_t num_prefix_blocks);
 
 /*
+ * pa_decode_step_cascade -- pa_kv_write followed by pa_attention_fwd_cascade,
+ * as one call (bf16; arguments as those two, workspace sized by
+ * pa_cascade_workspace_size).  The decode step of requests that share a
+ * cached prefix ("Anatomy of a serving engine", prefix caching; "Model
+ * execution", "Flattening a step": tables may point several requests at the
+ * same blocks, and every new token goes to its slot before attention).  The
+ * write of all num_tokens tokens (slot < 0 or past the pool: nothing
+ * written) shares its launch with the stage's setup, which reads only
+ * metadata, so the setup costs no launch of its own; the prefix stage and
+ * the rest of the step follow as in pa_attention_fwd_cascade and read the
+ * cache after the write.  Without sharers or prefix blocks (or requests) it
+ * is pa_decode_step with dtype PA_BF16.  Results (pool bytes, out, lse) are
+ * those of the two calls, bit for bit.  Errors as those two calls; nothing
+ * is enqueued when the arguments are rejected.
+ */
+pa_status pa_decode_step_cascade(const void* key, const void* value, void* key_cache,
+                                 void* value_cache, const int64_t* slot_mapping,
+                                 const void* query, const int32_t* query_start_loc,
+                                 const int32_t* seq_lens, const int32_t* block_tables,
+                                 int32_t num_seqs, int32_t num_tokens, int32_t max_query_len,
+                                 int32_t max_seq_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t block_table_stride,
+                                 int64_t num_blocks, float scale, int32_t num_splits,
+                                 const int32_t* sharers, int32_t num_sharers,
+                                 const int32_t* prefix_blocks, int32_t num_prefix_blocks,
+                                 void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/*
  * FP8 KV cache (E4M3).  The pages name an 8-bit cache as the way to halve the
  * bytes every decode step reads ("Anatomy of a serving engine", KV-cache
  * capacity; "Model execution", section "Attention backends") without fixing

@@ -24,7 +24,7 @@ from .validate import step_problems, validate_step  # noqa: F401
 __all__ = [
     "PaError", "kv_write", "attention", "split_combine", "workspace_size",
     "kv_write_fp8", "attention_fp8", "alloc_cache_fp8", "rope_kv_write", "attention_cascade",
-    "decode_step", "decode_step_fp8",
+    "decode_step", "decode_step_fp8", "decode_step_cascade",
     "decode_step_noalloc", "choose_num_splits", "capture_size", "alloc_cache", "workspace", "trace_begin", "trace_end",
     "trace_read",
     "kernel_name", "version", "set_unshared_blocks", "validate_step", "step_problems",
@@ -362,6 +362,46 @@ def attention_cascade(query, key_cache, value_cache, query_start_loc, seq_lens, 
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _stream(stream))
     _check(st, "pa_attention_fwd_cascade")
+    return out, lse
+
+
+def decode_step_cascade(key, value, key_cache, value_cache, slot_mapping, query,
+                        query_start_loc, seq_lens, block_tables, max_query_len: int,
+                        max_seq_len: int, scale: float, sharers, prefix_blocks,
+                        num_splits: int = 0, out=None, lse=None, want_lse: bool = True,
+                        workspace=None, stream=None):
+    """kv_write then attention_cascade as one call (bf16): the write shares
+    its launch with the shared-prefix setup.  Returns (out, lse)."""
+    nt, hq, d, nb, hkv, ns = _check_step_args(key, value, key_cache, value_cache, slot_mapping,
+                                              query, query_start_loc, seq_lens, block_tables)
+    if query.dtype != torch.bfloat16:
+        raise ValueError("the shared-prefix step is bf16")
+    for name, t in (("sharers", sharers), ("prefix_blocks", prefix_blocks)):
+        if t.dtype != torch.int32:
+            raise ValueError(f"{name} must be int32")
+    splits = num_splits
+    if splits == 0:
+        splits = choose_num_splits(ns, max_query_len, max_seq_len, hq, hkv)
+    if out is None:
+        out = torch.empty_like(query)
+    if lse is None and want_lse:
+        lse = torch.empty(nt, hq, dtype=torch.float32, device=query.device)
+    need = int(LIB.pa_cascade_workspace_size(ns, nt, hq, hkv, d, max(1, splits),
+                                             sharers.numel(), int(max_query_len),
+                                             prefix_blocks.numel()))
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=query.device)
+    st = LIB.pa_decode_step_cascade(
+        _dev(key, "key"), _dev(value, "value"), _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), _dev(slot_mapping, "slot_mapping"),
+        _dev(query, "query"), _dev(query_start_loc, "query_start_loc"),
+        _dev(seq_lens, "seq_lens"), _dev(block_tables, "block_tables"), ns, nt,
+        int(max_query_len), int(max_seq_len), hq, hkv, d, PA_BLOCK_SIZE, block_tables.shape[1],
+        nb, float(scale), splits, _dev(sharers, "sharers"), sharers.numel(),
+        _dev(prefix_blocks, "prefix_blocks"), prefix_blocks.numel(), _dev(out, "out"),
+        None if lse is None else _dev(lse, "lse"), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "pa_decode_step_cascade")
     return out, lse
 
 

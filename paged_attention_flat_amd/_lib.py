@@ -47,6 +47,9 @@ PROTOTYPES = {
                                         _i32, _i32, _i32, _i32, _i32, _i64, _f32, _i32, _vp,
                                         _i32, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
     "pa_cascade_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "pa_decode_step_cascade": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                                      _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i64, _f32,
+                                      _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
     "pa_rope_kv_write": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                 _i32, _i32, _i64, _i32, _vp]),
     "pa_kv_write_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64,

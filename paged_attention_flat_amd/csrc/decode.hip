@@ -49,7 +49,7 @@ __global__ __launch_bounds__(1024) void decode_order_kernel(const int32_t* __res
                                                             int32_t shift,
                                                             int32_t* __restrict__ order) {
   __shared__ int hist[kBuckets];
-  __shared__ int part[1024];
+  __shared__ int part[kScanParts];
   decode_order_block(qsl, seq_lens, num_seqs, dq, shift, order, hist, part);
 }
 

@@ -69,47 +69,41 @@ inline int decode_order_shift(int32_t max_seq_len) {
 
 // Counting sort of the decode requests (0 < q_len <= dq) by block count,
 // largest first, into order[0] = count, order[1 + rank] = request.  Called
-// by every thread of one 1024-thread work-group (it holds barriers); hist
-// [kBuckets] and part [1024] are the caller's shared memory.  Ties keep no
-// particular order (the order only schedules work, it never changes a
+// by every thread of one NT-thread work-group (it holds barriers); hist
+// [kBuckets] and part [kScanParts] are the caller's shared memory.  Ties keep
+// no particular order (the order only schedules work, it never changes a
 // result).
+template <int NT = 1024>
 __device__ __forceinline__ void decode_order_block(const int32_t* __restrict__ qsl,
                                                    const int32_t* __restrict__ seq_lens,
                                                    int32_t num_seqs, int32_t dq, int32_t shift,
                                                    int32_t* __restrict__ order, int* hist,
                                                    int* part) {
+  constexpr int kPer = kBuckets / NT;  // buckets per thread in the scan
   const int tid = threadIdx.x;
-  for (int i = tid; i < kBuckets; i += 1024) hist[i] = 0;
+  for (int i = tid; i < kBuckets; i += NT) hist[i] = 0;
   __syncthreads();
-  for (int b = tid; b < num_seqs; b += 1024) {
+  for (int b = tid; b < num_seqs; b += NT) {
     const int ql = qsl[b + 1] - qsl[b];
     if (ql <= 0 || ql > dq) continue;
     const int key = min(((seq_lens[b] + 15) >> 4) >> shift, kBuckets - 1);
     atomicAdd(&hist[kBuckets - 1 - key], 1);
   }
   __syncthreads();
-  // exclusive scan of hist: 4 buckets per thread, then a scan of the partials
-  int loc[4], s = 0;
+  // exclusive scan of hist: kPer buckets per thread, then a scan of the partials
+  int loc[kPer], s = 0;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < kPer; ++k) {
     loc[k] = s;
-    s += hist[tid * 4 + k];
+    s += hist[tid * kPer + k];
   }
-  part[tid] = s;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int v = tid >= off ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
-  }
-  const int base = part[tid] - s;
-  __syncthreads();
+  int total;
+  const int base = block_scan<NT>(s, part, total) - s;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) hist[tid * 4 + k] = base + loc[k];
-  if (tid == 1023) order[0] = part[1023];
+  for (int k = 0; k < kPer; ++k) hist[tid * kPer + k] = base + loc[k];
+  if (tid == 0) order[0] = total;
   __syncthreads();
-  for (int b = tid; b < num_seqs; b += 1024) {
+  for (int b = tid; b < num_seqs; b += NT) {
     const int ql = qsl[b + 1] - qsl[b];
     if (ql <= 0 || ql > dq) continue;
     const int key = min(((seq_lens[b] + 15) >> 4) >> shift, kBuckets - 1);

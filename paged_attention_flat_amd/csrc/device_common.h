@@ -162,4 +162,36 @@ __device__ __forceinline__ float fast_log2(float x) {
   return __builtin_amdgcn_logf(x);
 }
 
+// Most wave totals a work-group's scan passes through LDS (1024 threads).
+constexpr int kScanParts = 16;
+
+// Inclusive prefix sum of v over the NT threads of a work-group (NT a
+// multiple of 64, at most 1024), in thread order; `total` receives the
+// work-group's sum.  Shuffles inside each wave, then the wave totals through
+// `part` (kScanParts ints of LDS): two barriers, where a scan through LDS
+// alone takes 2 log2(NT).  Every thread of the work-group calls it; `part`
+// may be reused as soon as it returns.
+template <int NT>
+__device__ __forceinline__ int block_scan(int v, int* part, int& total) {
+  static_assert(NT % 64 == 0 && NT / 64 <= kScanParts, "one wave total per part");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int u = __shfl_up(v, off);
+    if (lane >= off) v += u;
+  }
+  if (lane == 63) part[wave] = v;
+  __syncthreads();
+  int base = 0, sum = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    const int p = part[i];
+    base += i < wave ? p : 0;
+    sum += p;
+  }
+  __syncthreads();
+  total = sum;
+  return v + base;
+}
+
 }  // namespace pa

@@ -2,66 +2,19 @@
 // slot_mapping ("Model execution", section "Flattening a step": the KV write
 // puts each new token's K and V at slot block_id * block_size + offset).
 //
-// One work-group handles 16 consecutive flat tokens of one KV head.  The K
-// row of a token is a contiguous run in the token-major K block, copied in
-// 16-byte pieces.  The V block is dim-major, so the 16 V rows are first staged
-// in LDS and then written column by column: lanes that differ in the token
-// index write neighbouring offsets of one dimension, which coalesce when the
-// tokens fill consecutive slots of a block (the usual case for a prefill
-// chunk).  The copy is a bit copy; the element type only fixes the width.
+// One work-group handles 16 consecutive flat tokens of one KV head
+// (write_tokens: K rows copied in 16-byte pieces, V rows staged in LDS and
+// written dim-major, so that they coalesce when the tokens fill consecutive
+// slots of a block, the usual case for a prefill chunk).  The copy is a bit
+// copy; the element type only fixes the width.
 #include <type_traits>
 
-#include "device_common.h"
-#include "pa_internal.h"
+#include "kv_write_body.h"
 
 namespace pa {
 namespace {
 
-constexpr int kTok = 16;
-
-// Writes the `ntok` (<= 16) tokens t0 .. t0 + ntok - 1 of KV head h.  Every
-// thread of the work-group calls it (it holds a barrier); `vrow` / `sslot`
-// are the caller's LDS staging.
-template <typename E>
-__device__ __forceinline__ void write_tokens(const E* __restrict__ key,
-                                             const E* __restrict__ value, E* __restrict__ kc,
-                                             E* __restrict__ vc,
-                                             const int64_t* __restrict__ slots, int t0,
-                                             int ntok, int h, int32_t hkv, int32_t d,
-                                             int64_t num_slots, E (*vrow)[128 + 16 / sizeof(E)],
-                                             int64_t* sslot) {
-  const int tid = threadIdx.x;
-  // The K/V loads do not depend on the slot, so they are issued together with
-  // the slot load (one memory round trip before the stores).
-  const int cpr = d * (int)sizeof(E) / 16;  // 16-byte pieces per row
-  for (int c = tid; c < kTok * cpr; c += 256) {
-    const int ti = c / cpr, part = c - ti * cpr;
-    if (ti >= ntok) break;
-    int64_t s = slots[t0 + ti];
-    if (s >= num_slots) s = -1;  // out of the pool: dropped like a padded token
-    const size_t src = ((size_t)(t0 + ti) * hkv + h) * d;
-    // the new tokens are read once: non-temporal loads (the cache rows they
-    // are stored to stay cached for the attention that follows)
-    const uint4 kv = load_stream16(reinterpret_cast<const uint4*>(key + src) + part);
-    const uint4 vv = load_stream16(reinterpret_cast<const uint4*>(value + src) + part);
-    if (part == 0) sslot[ti] = s;
-    reinterpret_cast<uint4*>(&vrow[ti][0])[part] = vv;
-    if (s < 0) continue;
-    const size_t blk = (size_t)(s >> 4), off = (size_t)(s & 15);
-    E* kdst = kc + ((blk * hkv + h) * kTok + off) * d;
-    reinterpret_cast<uint4*>(kdst)[part] = kv;
-  }
-  __syncthreads();
-
-  for (int e = tid; e < kTok * d; e += 256) {
-    const int ti = e & (kTok - 1), c = e >> 4;
-    if (ti >= ntok) continue;
-    const int64_t s = sslot[ti];
-    if (s < 0) continue;
-    const size_t blk = (size_t)(s >> 4), off = (size_t)(s & 15);
-    vc[((blk * hkv + h) * d + c) * kTok + off] = vrow[ti][c];
-  }
-}
+constexpr int kTok = kWriteTokens;
 
 template <typename E>
 __global__ __launch_bounds__(256) void kv_write_kernel(
@@ -72,7 +25,7 @@ __global__ __launch_bounds__(256) void kv_write_kernel(
   __shared__ int64_t sslot[kTok];
   const int t0 = blockIdx.x * kTok;
   write_tokens<E>(key, value, kc, vc, slots, t0, min(kTok, nt - t0), blockIdx.y, hkv, d,
-                  num_slots, vrow, sslot);
+                  num_slots, vrow, sslot, threadIdx.x);
 }
 
 // FP8 (E4M3) cache: the same geometry with one byte per element.  Each
@@ -174,7 +127,7 @@ __global__ __launch_bounds__(256) void kv_write_plan_kernel(
                           t0, min(kTok, t_end - t0), h, hkv, d, num_slots, vrow, sslot);
     else
       write_tokens<E>(key, value, (E*)kc, (E*)vc, slots, t0, min(kTok, t_end - t0), h, hkv, d,
-                      num_slots, vrow, sslot);
+                      num_slots, vrow, sslot, threadIdx.x);
     __syncthreads();  // the staging is reused by the next 16 tokens
   }
 }

@@ -205,6 +205,7 @@ const char* pa_kernel_name(int32_t id) {
     case K_CASCADE_SETUP: return "cascade_setup";
     case K_CASCADE_PREFIX: return "cascade_prefix";
     case K_MIXED: return "mixed_prefill_decode";
+    case K_CASCADE_WRITE_SETUP: return "cascade_write_setup";
   }
   return "unknown";
 }
@@ -483,8 +484,18 @@ pa_status attention_impl(const void* query, const void* key_cache, const void* v
     const bool prefill = max_query_len > dq;
     const bool has_decode_rows = (int64_t)num_seqs > (int64_t)num_tokens / (dq + 1);
     if (cascade) {
-      e = launch_cascade_prefix(a, s);
-      a.order_ready = 1;  // its setup kernel also ranked the decode requests
+      if (a.knew != nullptr) {
+        // one-call shared-prefix step: the setup's launch also writes every
+        // new token (before the stage reads the cache), so nothing later
+        // writes again
+        e = launch_cascade_write_setup(a, s);
+        a.casc_setup_ready = 1;
+        a.knew = nullptr;
+        a.vnew = nullptr;
+        a.slots = nullptr;
+      }
+      if (e == hipSuccess) e = launch_cascade_prefix(a, s);
+      a.order_ready = 1;  // its setup also ranked the decode requests
     }
     if (e == hipSuccess && prefill && has_decode_rows) {
       e = launch_mixed_bf16(a, s);
@@ -595,6 +606,37 @@ pa_status pa_attention_fwd_cascade(const void* query, const void* key_cache,
                         num_blocks, scale, num_splits, out, lse, workspace, workspace_bytes,
                         PA_BF16, false, stream, sharers, num_sharers, prefix_blocks,
                         num_prefix_blocks);
+}
+
+pa_status pa_decode_step_cascade(const void* key, const void* value, void* key_cache,
+                                 void* value_cache, const int64_t* slot_mapping,
+                                 const void* query, const int32_t* query_start_loc,
+                                 const int32_t* seq_lens, const int32_t* block_tables,
+                                 int32_t num_seqs, int32_t num_tokens, int32_t max_query_len,
+                                 int32_t max_seq_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t block_table_stride,
+                                 int64_t num_blocks, float scale, int32_t num_splits,
+                                 const int32_t* sharers, int32_t num_sharers,
+                                 const int32_t* prefix_blocks, int32_t num_prefix_blocks,
+                                 void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  if (num_sharers < 0 || num_prefix_blocks < 0) return PA_ERR_INVALID;
+  const bool cascade = num_sharers > 0 && num_prefix_blocks > 0;
+  if (cascade && (!sharers || !prefix_blocks)) return PA_ERR_NULL;
+  if (!cascade || num_seqs == 0)  // no shared prefix: the plain one-call step
+    return pa::decode_step_impl(key, value, key_cache, value_cache, slot_mapping, query,
+                                query_start_loc, seq_lens, block_tables, num_seqs, num_tokens,
+                                max_query_len, max_seq_len, num_q_heads, num_kv_heads, head_dim,
+                                block_size, block_table_stride, num_blocks, scale, num_splits,
+                                out, lse, workspace, workspace_bytes, PA_BF16, stream);
+  if (num_tokens > 0 && (!key || !value || !slot_mapping)) return PA_ERR_NULL;
+  if (!aligned16(key) || !aligned16(value)) return PA_ERR_INVALID;
+  return attention_impl(query, key_cache, value_cache, nullptr, nullptr, query_start_loc,
+                        seq_lens, block_tables, num_seqs, num_tokens, max_query_len, max_seq_len,
+                        num_q_heads, num_kv_heads, head_dim, block_size, block_table_stride,
+                        num_blocks, scale, num_splits, out, lse, workspace, workspace_bytes,
+                        PA_BF16, false, stream, sharers, num_sharers, prefix_blocks,
+                        num_prefix_blocks, key, value, slot_mapping);
 }
 
 pa_status pa_decode_step(const void* key, const void* value, void* key_cache, void* value_cache,

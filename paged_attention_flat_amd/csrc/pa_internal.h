@@ -26,7 +26,8 @@ enum KernelId : int32_t {
   K_CASCADE_SETUP = 12,
   K_CASCADE_PREFIX = 13,
   K_MIXED = 14,
-  K_COUNT = 15
+  K_CASCADE_WRITE_SETUP = 15,
+  K_COUNT = 16
 };
 
 // Tracing hooks (pa_api.cpp).  trace_before/after bracket one launch.
@@ -72,6 +73,7 @@ struct AttnArgs {
   int32_t* decode_order;  // nullable: count + ranked decode requests
   int32_t* claim;         // [2] work counters of the mixed kernel (prefill, decode)
   int32_t order_ready;    // 1: decode_order was already built this call
+  int32_t casc_setup_ready;  // 1: the shared-prefix setup already ran this call
   int32_t unshared;       // 1: no cache block is read by two requests of the step
                           //    (the many-unit decode then streams V non-temporally)
   int32_t num_cus;        // compute units of the current device
@@ -128,9 +130,13 @@ hipError_t launch_decode_bf16(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_prefill_plan(const AttnArgs& a, hipStream_t stream, bool with_order);
 hipError_t launch_mixed_bf16(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t stream);
-// shared-prefix stage: gather the sharers' decode rows, attend them to the
-// shared blocks (partials in pre_out / pre_lse); the decode kernel merges
+// shared-prefix stage: gather the sharers' decode rows (unless
+// a.casc_setup_ready), attend them to the shared blocks (partials in pre_out
+// / pre_lse); the decode kernel merges
 hipError_t launch_cascade_prefix(const AttnArgs& a, hipStream_t stream);
+// one launch: the shared-prefix setup (gathered rows and decode order) beside
+// the KV write of all a.num_tokens tokens (a.knew / a.vnew / a.slots, bf16)
+hipError_t launch_cascade_write_setup(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_zero(void* ptr, size_t bytes, hipStream_t stream);
 hipError_t launch_combine(const float* po, const float* pl, int32_t splits,

@@ -41,6 +41,7 @@
 // head) land on the same XCD (round-robin dispatch over 8 XCDs) and share its
 // L2 copy of that head's K/V.
 #include "decode_body.h"
+#include "kv_write_body.h"
 #include "prefill_body.h"
 
 namespace pa {
@@ -62,21 +63,21 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
                                                     int32_t* __restrict__ claim,
                                                     int32_t* __restrict__ order,
                                                     int32_t order_shift) {
-  __shared__ int s_scan[1024];
+  __shared__ int s_scan[kScanParts];
   __shared__ int hist[kPlanBuckets];
-  __shared__ int s_base;
   static_assert(kPlanBuckets == kBuckets, "the decode order shares the plan's histogram");
   if (blockIdx.x == 1) {
     decode_order_block(qsl, seq_lens, num_seqs, dq, order_shift, order, hist, s_scan);
     return;
   }
   const int tid = threadIdx.x;
-  if (tid == 0) s_base = 0;
   // the mixed kernel's work counters start from zero every call
   if (claim != nullptr && tid < 2) claim[tid] = 0;
   for (int i = tid; i < kPlanBuckets; i += 1024) hist[i] = 0;
   __syncthreads();
-  // 1. enumerate items (request, tile) into tmp, histogram of weights
+  // 1. enumerate items (request, tile) into tmp, histogram of weights; `run`
+  // (the same in every thread) counts the items of earlier chunks
+  int run = 0;
   for (int c0 = 0; c0 < num_seqs; c0 += 1024) {
     const int b = c0 + tid;
     int n = 0, ql = 0, ctx = 0;
@@ -85,15 +86,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
       ctx = seq_lens[b] - ql;
       if (ql > dq) n = (ql + tq - 1) / tq;
     }
-    s_scan[tid] = n;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-      const int v = tid >= off ? s_scan[tid - off] : 0;
-      __syncthreads();
-      s_scan[tid] += v;
-      __syncthreads();
-    }
-    const int base = s_base + s_scan[tid] - n;
+    int chunk_items;
+    const int base = run + block_scan<1024>(n, s_scan, chunk_items) - n;
     for (int k = 0; k < n; ++k) {
       const int idx = base + k;
       if (idx < cap) {
@@ -103,11 +97,10 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
         atomicAdd(&hist[kPlanBuckets - 1 - min(keys >> shift, kPlanBuckets - 1)], 1);
       }
     }
-    __syncthreads();
-    if (tid == 1023) s_base = s_base + s_scan[1023];
-    __syncthreads();
+    run += chunk_items;
   }
-  const int count = min(s_base, cap);
+  __syncthreads();  // the histogram is complete
+  const int count = min(run, cap);
   // 2. exclusive scan of the histogram (4 buckets per thread)
   int loc[4], s = 0;
 #pragma unroll
@@ -115,15 +108,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
     loc[k] = s;
     s += hist[tid * 4 + k];
   }
-  s_scan[tid] = s;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int v = tid >= off ? s_scan[tid - off] : 0;
-    __syncthreads();
-    s_scan[tid] += v;
-    __syncthreads();
-  }
-  const int base = s_scan[tid] - s;
+  int all_items;
+  const int base = block_scan<1024>(s, s_scan, all_items) - s;
 #pragma unroll
   for (int k = 0; k < 4; ++k) hist[tid * 4 + k] = base + loc[k];
   __syncthreads();
@@ -183,58 +169,131 @@ void launch_dg(const AttnArgs& a, hipStream_t stream) {
 // every gathered row, count in casc_count[0].  Requests whose rows the decode
 // kernel handles (0 < q_len <= dq, dq also bounded by the host's
 // max_query_len, which sized the gathered-row buffers) take part; others keep
-// pre_index = -1 and read the prefix themselves.  One work-group.
-__global__ __launch_bounds__(1024) void cascade_setup_kernel(
-    const int32_t* __restrict__ sharers, int32_t num_sharers, const int32_t* __restrict__ qsl,
-    const int32_t* __restrict__ seq_lens, int32_t num_seqs, int32_t dq,
-    int32_t* __restrict__ pre_index, int32_t* __restrict__ vtok, int32_t* __restrict__ vpos,
-    int32_t* __restrict__ count, int32_t* __restrict__ order, int32_t order_dq,
-    int32_t order_shift) {
-  __shared__ int s_scan[1024];
-  __shared__ int s_base;
-  __shared__ int hist[kBuckets];
+// pre_index = -1 and read the prefix themselves.  The decode order of the
+// step (order nullable) is built in the same launch by a second work-group:
+// one kernel boundary fewer on the step's serial path, and the two parts'
+// memory round trips overlap.  cascade_setup_block<NT>(part) is called by
+// every thread of an NT-thread work-group: part 0 gathers, part 1 ranks;
+// s_scan [kScanParts] and hist [kBuckets] are its LDS.
+struct CascadeSetupArgs {
+  const int32_t* sharers;
+  int32_t num_sharers;
+  const int32_t* qsl;
+  const int32_t* seq_lens;
+  int32_t num_seqs, dq;
+  int32_t* pre_index;
+  int32_t* vtok;
+  int32_t* vpos;
+  int32_t* count;
+  int32_t* order;
+  int32_t order_dq, order_shift;
+};
+
+struct CascadeSetupSmem {
+  int s_scan[kScanParts];
+  int hist[kBuckets];
+};
+
+template <int NT>
+__device__ __forceinline__ void cascade_setup_block(const CascadeSetupArgs& c,
+                                                    CascadeSetupSmem& sm, int part) {
+  if (part == 1) {
+    decode_order_block<NT>(c.qsl, c.seq_lens, c.num_seqs, c.order_dq, c.order_shift, c.order,
+                           sm.hist, sm.s_scan);
+    return;
+  }
   const int tid = threadIdx.x;
-  for (int b = tid; b < num_seqs; b += 1024) pre_index[b] = -1;
-  if (tid == 0) s_base = 0;
+  for (int b = tid; b < c.num_seqs; b += NT) c.pre_index[b] = -1;
+  // the sharers' pre_index entries are written after every -1 above
   __syncthreads();
-  for (int c0 = 0; c0 < num_sharers; c0 += 1024) {
+  int run = 0;  // gathered rows of earlier chunks (the same in every thread)
+  for (int c0 = 0; c0 < c.num_sharers; c0 += NT) {
     const int i = c0 + tid;
     int b = -1, ql = 0;
-    if (i < num_sharers) {
-      b = sharers[i];
-      if (b >= 0 && b < num_seqs) {
-        ql = qsl[b + 1] - qsl[b];
-        if (ql <= 0 || ql > dq) ql = 0;
+    if (i < c.num_sharers) {
+      b = c.sharers[i];
+      if (b >= 0 && b < c.num_seqs) {
+        ql = c.qsl[b + 1] - c.qsl[b];
+        if (ql <= 0 || ql > c.dq) ql = 0;
       }
     }
-    s_scan[tid] = ql;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-      const int v = tid >= off ? s_scan[tid - off] : 0;
-      __syncthreads();
-      s_scan[tid] += v;
-      __syncthreads();
-    }
-    const int v0 = s_base + s_scan[tid] - ql;
+    int chunk_rows;
+    const int v0 = run + block_scan<NT>(ql, sm.s_scan, chunk_rows) - ql;
     if (ql > 0) {
-      pre_index[b] = v0;
-      const int ctx = seq_lens[b] - ql;
+      c.pre_index[b] = v0;
+      const int ctx = c.seq_lens[b] - ql;
       for (int j = 0; j < ql; ++j) {
-        vtok[v0 + j] = qsl[b] + j;
-        vpos[v0 + j] = ctx + j;
+        c.vtok[v0 + j] = c.qsl[b] + j;
+        c.vpos[v0 + j] = ctx + j;
       }
     }
-    __syncthreads();
-    if (tid == 1023) s_base += s_scan[1023];
-    __syncthreads();
+    run += chunk_rows;
   }
-  if (tid == 0) count[0] = s_base;
-  // the decode order of this step, in the same launch (one kernel boundary
-  // fewer on the step's serial path)
-  if (order != nullptr) {
-    __syncthreads();
-    decode_order_block(qsl, seq_lens, num_seqs, order_dq, order_shift, order, hist, s_scan);
+  if (tid == 0) c.count[0] = run;
+}
+
+// work-groups of the setup: the gather, and the ranking when it is asked for
+inline int cascade_setup_groups(const CascadeSetupArgs& c) { return c.order != nullptr ? 2 : 1; }
+
+__global__ __launch_bounds__(1024) void cascade_setup_kernel(CascadeSetupArgs c) {
+  __shared__ CascadeSetupSmem sm;
+  cascade_setup_block<1024>(c, sm, blockIdx.x);
+}
+
+// The first launch of the one-call shared-prefix step: the first one or two
+// work-groups run the setup above (at 256 threads), the others write the
+// step's new tokens exactly as pa_kv_write does (16 flat tokens of one KV
+// head each).  The two are independent (the setup reads only metadata), so
+// the setup's latency hides under the write, and both are done before the
+// prefix stage reads the cache.
+__global__ __launch_bounds__(256) void cascade_write_setup_kernel(
+    CascadeSetupArgs c, const uint16_t* __restrict__ key, const uint16_t* __restrict__ value,
+    uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, const int64_t* __restrict__ slots,
+    int32_t nt, int32_t hkv, int32_t d, int64_t num_slots, int32_t setup_groups) {
+  __shared__ __align__(16) union {
+    CascadeSetupSmem setup;
+    WriteStage<uint16_t> write;
+  } sm;
+  if ((int)blockIdx.x < setup_groups) {
+    cascade_setup_block<256>(c, sm.setup, blockIdx.x);
+    return;
   }
+  const int w = blockIdx.x - setup_groups;
+  const int t0 = (w / hkv) * kWriteTokens;
+  write_tokens<uint16_t>(key, value, kc, vc, slots, t0, min(kWriteTokens, nt - t0), w % hkv, hkv,
+                         d, num_slots, sm.write.vrow, sm.write.slot, threadIdx.x);
+}
+
+template <int G>
+CascadeSetupArgs cascade_setup_args(const AttnArgs& a) {
+  CascadeSetupArgs c;
+  c.sharers = a.sharers;
+  c.num_sharers = a.num_sharers;
+  c.qsl = a.qsl;
+  c.seq_lens = a.seq_lens;
+  c.num_seqs = a.num_seqs;
+  c.dq = min(decode_max_q(G), a.max_query_len);
+  c.pre_index = a.pre_index;
+  c.vtok = a.vtok;
+  c.vpos = a.vpos;
+  c.count = a.casc_count;
+  c.order = a.decode_order;
+  c.order_dq = decode_max_q(G);
+  c.order_shift = decode_order_shift(a.max_seq_len);
+  return c;
+}
+
+template <int G>
+void cascade_write_setup_g(const AttnArgs& a, hipStream_t stream) {
+  const int64_t groups = ((int64_t)a.num_tokens + kWriteTokens - 1) / kWriteTokens;
+  const CascadeSetupArgs c = cascade_setup_args<G>(a);
+  const int setup_groups = cascade_setup_groups(c);
+  trace_before(K_CASCADE_WRITE_SETUP, stream);
+  hipLaunchKernelGGL(cascade_write_setup_kernel, dim3((unsigned)(setup_groups + groups * a.hkv)),
+                     dim3(256), 0, stream, c, (const uint16_t*)a.knew, (const uint16_t*)a.vnew,
+                     (uint16_t*)a.kc, (uint16_t*)a.vc, a.slots, a.num_tokens, a.hkv, a.d,
+                     a.num_blocks * kWriteTokens, setup_groups);
+  trace_after(stream);
 }
 
 template <int D, int G>
@@ -260,13 +319,13 @@ void launch_cascade_dg(const AttnArgs& a, hipStream_t stream) {
   p.pre_rows = a.casc_rows_max;
   p.pre_out = a.pre_out;
   p.pre_lse = a.pre_lse;
-  trace_before(K_CASCADE_SETUP, stream);
-  hipLaunchKernelGGL(cascade_setup_kernel, dim3(1), dim3(1024), 0, stream, a.sharers,
-                     a.num_sharers, a.qsl, a.seq_lens, a.num_seqs,
-                     min(decode_max_q(G), a.max_query_len), a.pre_index,
-                     a.vtok, a.vpos, a.casc_count, a.decode_order, decode_max_q(G),
-                     decode_order_shift(a.max_seq_len));
-  trace_after(stream);
+  if (!a.casc_setup_ready) {
+    trace_before(K_CASCADE_SETUP, stream);
+    const CascadeSetupArgs c = cascade_setup_args<G>(a);
+    hipLaunchKernelGGL(cascade_setup_kernel, dim3(cascade_setup_groups(c)), dim3(1024), 0,
+                       stream, c);
+    trace_after(stream);
+  }
   const int tiles = (a.casc_rows_max + TQ - 1) / TQ;
   trace_before(K_CASCADE_PREFIX, stream);
   hipLaunchKernelGGL((prefill_kernel<D, G, NW, RG, BK, false, true>),
@@ -304,6 +363,17 @@ hipError_t launch_cascade_prefix(const AttnArgs& a, hipStream_t stream) {
       case 8: launch_cascade_dg<128, 8>(a, stream); break;
       default: launch_cascade_dg<128, 16>(a, stream); break;
     }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_cascade_write_setup(const AttnArgs& a, hipStream_t stream) {
+  switch (a.hq / a.hkv) {
+    case 1: cascade_write_setup_g<1>(a, stream); break;
+    case 2: cascade_write_setup_g<2>(a, stream); break;
+    case 4: cascade_write_setup_g<4>(a, stream); break;
+    case 8: cascade_write_setup_g<8>(a, stream); break;
+    default: cascade_write_setup_g<16>(a, stream); break;
   }
   return hipGetLastError();
 }

@@ -216,6 +216,33 @@ def test_cascade_validation(lib):
     assert _cascade(lib, ns=0) == 0
 
 
+def _step_cascade(lib, **kw):
+    a = dict(k=P, v=P, kc=P, vc=P, sm=P, q=P, qsl=P, sl=P, bt=P, ns=2, nt=2, mq=1, ms=40, hq=8,
+             hkv=2, d=128, bs=16, stride=3, nb=10, scale=0.1, splits=1, sh=P, nsh=2, pb=P, npb=2,
+             out=P, lse=None, ws=P, wsb=1 << 20)
+    a.update(kw)
+    return lib.pa_decode_step_cascade(a["k"], a["v"], a["kc"], a["vc"], a["sm"], a["q"],
+                                      a["qsl"], a["sl"], a["bt"], a["ns"], a["nt"], a["mq"],
+                                      a["ms"], a["hq"], a["hkv"], a["d"], a["bs"], a["stride"],
+                                      a["nb"], a["scale"], a["splits"], a["sh"], a["nsh"],
+                                      a["pb"], a["npb"], a["out"], a["lse"], a["ws"], a["wsb"],
+                                      None)
+
+
+def test_decode_step_cascade_validation(lib):
+    assert _step_cascade(lib, nsh=-1) == 2
+    assert _step_cascade(lib, npb=-1) == 2
+    assert _step_cascade(lib, sh=None) == 1
+    assert _step_cascade(lib, pb=None) == 1
+    assert _step_cascade(lib, k=None) == 1                  # the write needs the new K
+    assert _step_cascade(lib, sm=None) == 1
+    assert _step_cascade(lib, v=ctypes.c_void_p(258)) == 2  # misaligned new V
+    assert _step_cascade(lib, d=96) == 3
+    assert _step_cascade(lib, hq=6, hkv=4) == 2
+    assert _step_cascade(lib, bs=32) == 3
+    assert _step_cascade(lib, nt=0) == 0                    # empty step
+
+
 def _step(lib, fp8=False, **kw):
     a = dict(k=P, v=P, kc=P, vc=P, sm=P, ks=P, vs=P, q=P, qsl=P, sl=P, bt=P, ns=2, nt=2, mq=1,
              ms=40, hq=8, hkv=2, d=128, bs=16, stride=3, nb=10, scale=0.1, splits=1, out=P,
