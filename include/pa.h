@@ -461,22 +461,32 @@ int32_t pa_choose_num_splits(int32_t num_seqs, int32_t max_query_len,
 int32_t pa_capture_size(int32_t num_tokens, int32_t max_size);
 
 /*
- * pa_set_unshared_blocks -- cache-read hint for later calls in this process.
- * Block tables may point several requests of a step at the same physical
- * blocks (prefix caching: "Anatomy of a serving engine"; "Model execution",
- * "Flattening a step").  on = 1 states that no cache block is read by two
- * requests of a step; the decode rows of pa_attention_fwd(_fp8) /
- * pa_decode_step(_fp8) then read V with the non-temporal policy, which
+ * pa_set_unshared_blocks -- cache-read policy of the decode rows for later
+ * calls in this process.  Block tables may point several requests of a step
+ * at the same physical blocks (prefix caching: "Anatomy of a serving
+ * engine"; "Model execution", "Flattening a step").  A request whose blocks
+ * no other request reads has its V read with the non-temporal policy, which
  * streams it without keeping it in L2/MALL (measured: 256 unshared decodes
- * ~8 % faster with a bf16 cache, ~9 % with E4M3;
- * 256 decodes that all re-read one 16K-token prefix ~25 % slower).  Results
- * are the same either way, bit for bit.  pa_attention_fwd_cascade always
- * reads that way (its decode rows skip the shared prefix).  Default 0;
- * process-wide, takes effect for launches issued after the call (a captured
- * HIP graph keeps the loads it was captured with).  Returns the previous
- * setting.
+ * ~8 % faster with a bf16 cache, ~9 % with E4M3); blocks that several
+ * requests read stay cached, since the non-temporal policy would re-read them
+ * from HBM (256 decodes that all re-read one 16K-token prefix: ~25 % slower).
+ * This applies to the decode rows of pa_attention_fwd(_fp8) /
+ * pa_decode_step(_fp8) when the step has more decode work units than two per
+ * compute unit or also has prefill rows.  mode:
+ *    0 (default) automatic: a request counts as unshared when its first
+ *      block is no other request's first block (sharing goes through common
+ *      prefixes); tested while the decode requests are ranked (steps of 64
+ *      to 8192 requests), otherwise every request counts as shared;
+ *    1 every request counts as unshared (the caller states that no block is
+ *      read by two requests of a step);
+ *   -1 every request counts as shared.
+ * Results are the same under every mode, bit for bit.
+ * pa_attention_fwd_cascade always reads the unshared way (its decode rows
+ * skip the shared prefix).  Process-wide, takes effect for launches issued
+ * after the call (a captured HIP graph keeps the loads it was captured
+ * with).  Returns the previous mode.
  */
-int32_t pa_set_unshared_blocks(int32_t on);
+int32_t pa_set_unshared_blocks(int32_t mode);
 
 /* pa_status_string -- static text for a status code (never NULL). */
 const char* pa_status_string(pa_status status);

@@ -70,11 +70,14 @@ def version() -> int:
     return int(LIB.pa_version())
 
 
-def set_unshared_blocks(on: bool) -> bool:
-    """pa_set_unshared_blocks: declare that no cache block is read by two
-    requests of a step (later decode reads of V then bypass L2/MALL
-    allocation).  Returns the previous setting."""
-    return bool(LIB.pa_set_unshared_blocks(1 if on else 0))
+def set_unshared_blocks(mode) -> int:
+    """pa_set_unshared_blocks: the decode rows' cache-read policy for V in
+    later calls.  1 (or True): every request's blocks are its own (V streamed
+    past L2/MALL); 0 (or False, the default): automatic, a request whose
+    first block is no other request's first block counts as unshared; -1:
+    every request's blocks count as shared.  Returns the previous mode."""
+    m = int(mode)
+    return int(LIB.pa_set_unshared_blocks(1 if m > 0 else (-1 if m < 0 else 0)))
 
 
 def alloc_cache(num_blocks: int, num_kv_heads: int, head_dim: int, dtype, device="cuda"):

@@ -42,15 +42,19 @@
 namespace pa {
 namespace {
 
-// Counting sort of the decode requests by block count (decode_order_block).
+// Counting sort of the decode requests by block count, with the sharing
+// test when `tables` is given (decode_order_block).
 __global__ __launch_bounds__(1024) void decode_order_kernel(const int32_t* __restrict__ qsl,
                                                             const int32_t* __restrict__ seq_lens,
+                                                            const int32_t* __restrict__ tables,
+                                                            int32_t table_stride,
                                                             int32_t num_seqs, int32_t dq,
                                                             int32_t shift,
                                                             int32_t* __restrict__ order) {
-  __shared__ int hist[kBuckets];
-  __shared__ int part[kScanParts];
-  decode_order_block(qsl, seq_lens, num_seqs, dq, shift, order, hist, part);
+  __shared__ OrderSmem sm;
+  __shared__ ShareSmem share;
+  decode_order_block(qsl, seq_lens, tables, table_stride, num_seqs, dq, shift, order, sm,
+                     &share);
 }
 
 // NTP: the loads that take the non-temporal policy.  The long-context shape
@@ -86,7 +90,8 @@ void order_dg(const AttnArgs& a, hipStream_t stream) {
   if (a.decode_order == nullptr || a.order_ready) return;
   trace_before(K_DECODE_ORDER, stream);
   hipLaunchKernelGGL(decode_order_kernel, dim3(1), dim3(1024), 0, stream, a.qsl, a.seq_lens,
-                     a.num_seqs, 16 / G, decode_order_shift(a.max_seq_len), a.decode_order);
+                     a.detect_sharing ? a.tables : nullptr, a.table_stride, a.num_seqs, 16 / G,
+                     decode_order_shift(a.max_seq_len), a.decode_order);
   trace_after(stream);
 }
 
@@ -104,6 +109,10 @@ void launch_dg(const AttnArgs& a, hipStream_t stream) {
   } else if (a.unshared) {
     constexpr int NW = PA_DECODE_WAVES_WIDE;
     hipLaunchKernelGGL((decode_kernel<D, G, NW, 1, F8, kNtV>), grid, dim3(64 * NW), 0, stream, p);
+  } else if (a.detect_sharing) {
+    constexpr int NW = PA_DECODE_WAVES_WIDE;
+    hipLaunchKernelGGL((decode_kernel<D, G, NW, 1, F8, kNtAuto>), grid, dim3(64 * NW), 0, stream,
+                       p);
   } else {
     constexpr int NW = PA_DECODE_WAVES_WIDE;
     hipLaunchKernelGGL((decode_kernel<D, G, NW, 1, F8, 0>), grid, dim3(64 * NW), 0, stream, p);

@@ -67,27 +67,85 @@ inline int decode_order_shift(int32_t max_seq_len) {
   return shift;
 }
 
+// Shared memory of decode_order_block: the sort's histogram and scan, and
+// (for the sharing test) an open-addressing set of first blocks (key = block
+// id + 1, 0 = empty) with a bit per slot that marks a first block met more
+// than once.
+constexpr int kShareSlots = 16384;
+struct OrderSmem {
+  int hist[kBuckets];
+  int part[kScanParts];
+};
+struct ShareSmem {
+  uint32_t keys[kShareSlots];
+  uint32_t multi[kShareSlots / 32];
+};
+
+// Requests whose first blocks the sharing test can hold (half the set).
+constexpr int kShareMaxSeqs = kShareSlots / 2;
+
+__device__ __forceinline__ int share_slot(uint32_t key) {
+  return (int)((key * 2654435761u) >> 18);  // 14 bits: kShareSlots
+}
+
+// Bit 31 of an order entry: the request's blocks are taken as read by it
+// alone (its V is streamed non-temporally by the decode units that read the
+// order with the automatic policy).
+constexpr uint32_t kOrderUnshared = 0x80000000u;
+
 // Counting sort of the decode requests (0 < q_len <= dq) by block count,
 // largest first, into order[0] = count, order[1 + rank] = request.  Called
-// by every thread of one NT-thread work-group (it holds barriers); hist
-// [kBuckets] and part [kScanParts] are the caller's shared memory.  Ties keep
-// no particular order (the order only schedules work, it never changes a
-// result).
+// by every thread of one NT-thread work-group (it holds barriers); sm is its
+// shared memory.  Ties keep no particular order (the order only schedules
+// work, it never changes a result).
+//
+// With `tables` and `share` (nullable, and num_seqs <= kShareMaxSeqs), each entry also
+// says whether the request shares blocks with another request of the step:
+// it does when its first block is the first block of another request (with
+// any new or cached token).  Blocks are shared through common prefixes (a
+// cached prefix, a forked sequence), so a request whose first block is its
+// own reads no block that another request reads; a step that shares blocks
+// any other way is only slower under the flag, never different.
 template <int NT = 1024>
 __device__ __forceinline__ void decode_order_block(const int32_t* __restrict__ qsl,
                                                    const int32_t* __restrict__ seq_lens,
-                                                   int32_t num_seqs, int32_t dq, int32_t shift,
-                                                   int32_t* __restrict__ order, int* hist,
-                                                   int* part) {
+                                                   const int32_t* __restrict__ tables,
+                                                   int32_t table_stride, int32_t num_seqs,
+                                                   int32_t dq, int32_t shift,
+                                                   int32_t* __restrict__ order, OrderSmem& sm,
+                                                   ShareSmem* share) {
   constexpr int kPer = kBuckets / NT;  // buckets per thread in the scan
   const int tid = threadIdx.x;
-  for (int i = tid; i < kBuckets; i += NT) hist[i] = 0;
+  const bool detect = tables != nullptr && share != nullptr && num_seqs <= kShareMaxSeqs;
+  for (int i = tid; i < kBuckets; i += NT) sm.hist[i] = 0;
+  if (detect) {
+    for (int i = tid; i < kShareSlots; i += NT) share->keys[i] = 0u;
+    for (int i = tid; i < kShareSlots / 32; i += NT) share->multi[i] = 0u;
+  }
   __syncthreads();
   for (int b = tid; b < num_seqs; b += NT) {
     const int ql = qsl[b + 1] - qsl[b];
+    const int sl = seq_lens[b];
+    if (detect && sl > 0) {
+      const int first = tables[(size_t)b * table_stride];
+      if (first >= 0) {
+        const uint32_t key = (uint32_t)first + 1u;
+        int h = share_slot(key);
+        // the set is at most half full, so a free slot or the key is found
+        for (int probe = 0; probe < kShareSlots; ++probe) {
+          const uint32_t prev = atomicCAS(&share->keys[h], 0u, key);
+          if (prev == 0u) break;
+          if (prev == key) {
+            atomicOr(&share->multi[h >> 5], 1u << (h & 31));
+            break;
+          }
+          h = (h + 1) & (kShareSlots - 1);
+        }
+      }
+    }
     if (ql <= 0 || ql > dq) continue;
-    const int key = min(((seq_lens[b] + 15) >> 4) >> shift, kBuckets - 1);
-    atomicAdd(&hist[kBuckets - 1 - key], 1);
+    const int key = min(((sl + 15) >> 4) >> shift, kBuckets - 1);
+    atomicAdd(&sm.hist[kBuckets - 1 - key], 1);
   }
   __syncthreads();
   // exclusive scan of hist: kPer buckets per thread, then a scan of the partials
@@ -95,20 +153,33 @@ __device__ __forceinline__ void decode_order_block(const int32_t* __restrict__ q
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
     loc[k] = s;
-    s += hist[tid * kPer + k];
+    s += sm.hist[tid * kPer + k];
   }
   int total;
-  const int base = block_scan<NT>(s, part, total) - s;
+  const int base = block_scan<NT>(s, sm.part, total) - s;
 #pragma unroll
-  for (int k = 0; k < kPer; ++k) hist[tid * kPer + k] = base + loc[k];
+  for (int k = 0; k < kPer; ++k) sm.hist[tid * kPer + k] = base + loc[k];
   if (tid == 0) order[0] = total;
   __syncthreads();
   for (int b = tid; b < num_seqs; b += NT) {
     const int ql = qsl[b + 1] - qsl[b];
     if (ql <= 0 || ql > dq) continue;
-    const int key = min(((seq_lens[b] + 15) >> 4) >> shift, kBuckets - 1);
-    const int pos = atomicAdd(&hist[kBuckets - 1 - key], 1);
-    order[1 + pos] = b;
+    const int sl = seq_lens[b];
+    uint32_t flag = 0u;
+    if (detect && sl > 0) {
+      // the first block was entered above
+      const int first = tables[(size_t)b * table_stride];
+      if (first >= 0) {
+        const uint32_t key = (uint32_t)first + 1u;
+        int h = share_slot(key);
+        for (int probe = 0; probe < kShareSlots && share->keys[h] != key; ++probe)
+          h = (h + 1) & (kShareSlots - 1);
+        if (!((share->multi[h >> 5] >> (h & 31)) & 1u)) flag = kOrderUnshared;
+      }
+    }
+    const int key = min(((sl + 15) >> 4) >> shift, kBuckets - 1);
+    const int pos = atomicAdd(&sm.hist[kBuckets - 1 - key], 1);
+    order[1 + pos] = (int32_t)((uint32_t)b | flag);
   }
 }
 
@@ -169,16 +240,20 @@ struct DecodeSmem {
 // loads cover 64 bytes of 16 rows, which gains only in the long single
 // decode.  Blocks read by several requests of a step are re-read from HBM
 // under this policy.
-constexpr int kNtK = 1;  // K loads non-temporal (bf16 cache)
-constexpr int kNtV = 2;  // V loads non-temporal
+constexpr int kNtK = 1;     // K loads non-temporal (bf16 cache)
+constexpr int kNtV = 2;     // V loads non-temporal
+constexpr int kNtAuto = 4;  // V loads non-temporal for requests the order marks unshared
 
 // One decode work unit: (KV head, request rank) = bx (KV head fastest) and
 // split = by, computed by the NW waves of the calling work-group (tidx: the
-// thread's index in it).  NTP: kNtK | kNtV, the loads that take the
-// non-temporal policy.  Every exit is work-group uniform.
+// thread's index in it) for request b (live = 0: a rank past the order's
+// count, whose work-group only takes part in the tail write).  NTP: kNtK |
+// kNtV, the loads that take the non-temporal policy.  Every exit is
+// work-group uniform.
 template <int D, int G, int NW, int PIPE, bool F8, int NTP>
-__device__ __forceinline__ void decode_unit(const DecodeParams& p, int bx, int by,
-                                            DecodeSmem<D, NW>& sm, const int tidx) {
+__device__ __forceinline__ void decode_unit_body(const DecodeParams& p, int bx, int by, int b,
+                                                 int live, DecodeSmem<D, NW>& sm,
+                                                 const int tidx) {
   typedef typename Frag8<F8>::elem CT;
   typedef typename Frag8<F8>::raw RT;
   constexpr int DQ = 16 / G;       // new tokens per request packed in the columns
@@ -190,23 +265,13 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& p, int bx, int b
   float (&s_x)[NW / 2][NREG][64] = sm.x;
 
   const int kvh = bx % p.hkv;
-  const int rank = bx / p.hkv;
   const int split = by;
   const int lane = tidx & 63, wave = tidx >> 6;
   const int col = lane & 15, kg = lane >> 4;
 
   CT* const kc_w = const_cast<CT*>(static_cast<const CT*>(p.kc));
   CT* const vc_w = const_cast<CT*>(static_cast<const CT*>(p.vc));
-  // First-level metadata, issued together (each serialised scalar round trip
-  // here delays every work-group's first K/V load).  order[1 + rank] is in
-  // bounds for every rank (rank < num_seqs).
   const bool tail_wg = p.knew != nullptr && bx == 0 && by == 0;
-  int b = rank;
-  int live = 1;
-  if (p.order != nullptr) {
-    live = rank < p.order[0];
-    b = p.order[1 + rank];
-  }
   if (tail_wg) {
     // fused KV write of tokens after the last request's rows (no row reads
     // them; written for the pool's sake, every KV head)
@@ -782,6 +847,34 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& p, int bx, int b
     }
   }
   if (tidx == 0) __hip_atomic_store(sem, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The work unit of decode_unit_body, its request read from the decode order
+// (one scalar round trip, before the request's own metadata).  NTP may add
+// kNtAuto: the unit then streams V non-temporally when the order marks its
+// request as reading no block another request reads.  order[1 + rank] is in
+// bounds for every rank (rank < num_seqs).
+template <int D, int G, int NW, int PIPE, bool F8, int NTP>
+__device__ __forceinline__ void decode_unit(const DecodeParams& p, int bx, int by,
+                                            DecodeSmem<D, NW>& sm, const int tidx) {
+  const int rank = bx / p.hkv;
+  int b = rank, live = 1;
+  bool unshared = false;
+  if (p.order != nullptr) {
+    live = rank < p.order[0];
+    const uint32_t v = (uint32_t)p.order[1 + rank];
+    b = (int)(v & ~kOrderUnshared);
+    unshared = (v & kOrderUnshared) != 0u;
+  }
+  if constexpr ((NTP & kNtAuto) != 0) {
+    constexpr int kBase = NTP & ~kNtAuto;
+    if (unshared)
+      decode_unit_body<D, G, NW, PIPE, F8, kBase | kNtV>(p, bx, by, b, live, sm, tidx);
+    else
+      decode_unit_body<D, G, NW, PIPE, F8, kBase>(p, bx, by, b, live, sm, tidx);
+  } else {
+    decode_unit_body<D, G, NW, PIPE, F8, NTP>(p, bx, by, b, live, sm, tidx);
+  }
 }
 
 }  // namespace pa

@@ -94,10 +94,14 @@ void launch_dg(const AttnArgs& a, hipStream_t stream) {
   const int32_t wgs = a.num_cus;
   const int32_t prefill_first = (wgs + PA_MIXED_PREFILL_SHARE - 1) / PA_MIXED_PREFILL_SHARE;
   trace_before(K_MIXED, stream);
-  // V streamed non-temporally when the call's blocks are unshared (as in the
-  // many-work-group decode kernel)
+  // V streamed non-temporally when the call's blocks are unshared, or per
+  // request as the decode order marks it (as in the many-work-group decode
+  // kernel)
   if (a.unshared)
     hipLaunchKernelGGL((mixed_kernel<D, G, F8, kNtV>), dim3(wgs), dim3(64 * kMixedWaves), 0,
+                       stream, pp, dp, a.claim, prefill_first, decode_x, decode_units);
+  else if (a.detect_sharing)
+    hipLaunchKernelGGL((mixed_kernel<D, G, F8, kNtAuto>), dim3(wgs), dim3(64 * kMixedWaves), 0,
                        stream, pp, dp, a.claim, prefill_first, decode_x, decode_units);
   else
     hipLaunchKernelGGL((mixed_kernel<D, G, F8, 0>), dim3(wgs), dim3(64 * kMixedWaves), 0,

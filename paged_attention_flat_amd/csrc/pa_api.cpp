@@ -183,10 +183,12 @@ const char* pa_status_string(pa_status s) {
 int32_t pa_version(void) { return 100; }  // 0.1.0
 
 namespace {
-std::atomic<int32_t> g_unshared{0};  // pa_set_unshared_blocks
+std::atomic<int32_t> g_unshared{0};  // pa_set_unshared_blocks: 1, 0 (automatic) or -1
 }  // namespace
 
-int32_t pa_set_unshared_blocks(int32_t on) { return g_unshared.exchange(on ? 1 : 0); }
+int32_t pa_set_unshared_blocks(int32_t mode) {
+  return g_unshared.exchange(mode > 0 ? 1 : (mode < 0 ? -1 : 0));
+}
 
 const char* pa_kernel_name(int32_t id) {
   switch (id) {
@@ -445,7 +447,15 @@ pa_status attention_impl(const void* query, const void* key_cache, const void* v
   }
   // the decode rows' blocks are unshared when the caller says so, and in a
   // shared-prefix call once the prefix is read by its own stage
-  a.unshared = (cascade || g_unshared.load(std::memory_order_relaxed)) ? 1 : 0;
+  const int32_t share_mode = g_unshared.load(std::memory_order_relaxed);
+  a.unshared = (cascade || share_mode > 0) ? 1 : 0;
+  // otherwise, by default, the decode order marks the requests that share no
+  // block when the many-work-group shape or the persistent launch reads them
+  const int32_t dq_group = decode_max_q(group);
+  const bool many_units = (int64_t)num_seqs * num_kv_heads * splits > 2 * (int64_t)a.num_cus ||
+                          max_query_len > dq_group;
+  a.detect_sharing =
+      (!a.unshared && share_mode == 0 && a.decode_order != nullptr && many_units) ? 1 : 0;
   a.sharers = cascade ? sharers : nullptr;
   a.num_sharers = cascade ? num_sharers : 0;
   a.pre_blocks = pre_blocks;

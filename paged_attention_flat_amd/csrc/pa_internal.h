@@ -76,6 +76,9 @@ struct AttnArgs {
   int32_t casc_setup_ready;  // 1: the shared-prefix setup already ran this call
   int32_t unshared;       // 1: no cache block is read by two requests of the step
                           //    (the many-unit decode then streams V non-temporally)
+  int32_t detect_sharing; // 1: the decode order marks the requests whose first block
+                          //    no other request has, and the many-unit decode streams
+                          //    their V non-temporally
   int32_t num_cus;        // compute units of the current device
   int32_t* sem;           // nullable: zeroed arrival counters, one per (request, KV head)
   int32_t cache_fp8;      // 1: kc / vc hold E4M3 codes (query and out bf16)

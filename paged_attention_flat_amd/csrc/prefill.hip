@@ -62,14 +62,19 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
                                                     int32_t* __restrict__ tmp, int32_t cap,
                                                     int32_t* __restrict__ claim,
                                                     int32_t* __restrict__ order,
-                                                    int32_t order_shift) {
-  __shared__ int s_scan[kScanParts];
-  __shared__ int hist[kPlanBuckets];
-  static_assert(kPlanBuckets == kBuckets, "the decode order shares the plan's histogram");
+                                                    int32_t order_shift,
+                                                    const int32_t* __restrict__ tables,
+                                                    int32_t table_stride) {
+  __shared__ OrderSmem osm;
+  __shared__ ShareSmem share;
+  static_assert(kPlanBuckets == kBuckets, "the plan uses the decode order's histogram");
   if (blockIdx.x == 1) {
-    decode_order_block(qsl, seq_lens, num_seqs, dq, order_shift, order, hist, s_scan);
+    decode_order_block(qsl, seq_lens, tables, table_stride, num_seqs, dq, order_shift, order,
+                       osm, &share);
     return;
   }
+  int* const s_scan = osm.part;
+  int* const hist = osm.hist;
   const int tid = threadIdx.x;
   // the mixed kernel's work counters start from zero every call
   if (claim != nullptr && tid < 2) claim[tid] = 0;
@@ -144,7 +149,8 @@ hipError_t plan_dg(const AttnArgs& a, hipStream_t stream, bool with_order) {
   hipLaunchKernelGGL(plan_kernel, dim3(order ? 2 : 1), dim3(1024), 0, stream, a.qsl, a.seq_lens,
                      a.num_seqs, decode_max_q(G), prefill_tile_tokens(G), shift, a.plan,
                      a.plan_tmp, a.plan_cap, a.claim, order ? a.decode_order : nullptr,
-                     decode_order_shift(a.max_seq_len));
+                     decode_order_shift(a.max_seq_len), a.detect_sharing ? a.tables : nullptr,
+                     a.table_stride);
   trace_after(stream);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && a.knew != nullptr) e = launch_kv_write_plan(a, prefill_tile_tokens(G), stream);
@@ -174,7 +180,7 @@ void launch_dg(const AttnArgs& a, hipStream_t stream) {
 // one kernel boundary fewer on the step's serial path, and the two parts'
 // memory round trips overlap.  cascade_setup_block<NT>(part) is called by
 // every thread of an NT-thread work-group: part 0 gathers, part 1 ranks;
-// s_scan [kScanParts] and hist [kBuckets] are its LDS.
+// sm is its LDS.
 struct CascadeSetupArgs {
   const int32_t* sharers;
   int32_t num_sharers;
@@ -189,17 +195,15 @@ struct CascadeSetupArgs {
   int32_t order_dq, order_shift;
 };
 
-struct CascadeSetupSmem {
-  int s_scan[kScanParts];
-  int hist[kBuckets];
-};
+typedef OrderSmem CascadeSetupSmem;
 
 template <int NT>
 __device__ __forceinline__ void cascade_setup_block(const CascadeSetupArgs& c,
                                                     CascadeSetupSmem& sm, int part) {
   if (part == 1) {
-    decode_order_block<NT>(c.qsl, c.seq_lens, c.num_seqs, c.order_dq, c.order_shift, c.order,
-                           sm.hist, sm.s_scan);
+    // (no sharing test: the shared-prefix call streams every decode unit's V)
+    decode_order_block<NT>(c.qsl, c.seq_lens, nullptr, 0, c.num_seqs, c.order_dq,
+                           c.order_shift, c.order, sm, nullptr);
     return;
   }
   const int tid = threadIdx.x;
@@ -218,7 +222,7 @@ __device__ __forceinline__ void cascade_setup_block(const CascadeSetupArgs& c,
       }
     }
     int chunk_rows;
-    const int v0 = run + block_scan<NT>(ql, sm.s_scan, chunk_rows) - ql;
+    const int v0 = run + block_scan<NT>(ql, sm.part, chunk_rows) - ql;
     if (ql > 0) {
       c.pre_index[b] = v0;
       const int ctx = c.seq_lens[b] - ql;

@@ -277,12 +277,14 @@ def test_workspace_init_validation(lib):
 
 
 def test_unshared_blocks_hint(lib):
-    # a host-side setting: returns the previous value, any nonzero means on
+    # a host-side setting: returns the previous mode; positive means 1,
+    # negative -1, zero the automatic default
     before = lib.pa_set_unshared_blocks(0)
     try:
         assert lib.pa_set_unshared_blocks(1) == 0
         assert lib.pa_set_unshared_blocks(7) == 1
-        assert lib.pa_set_unshared_blocks(0) == 1
+        assert lib.pa_set_unshared_blocks(-5) == 1
+        assert lib.pa_set_unshared_blocks(0) == -1
         assert lib.pa_set_unshared_blocks(0) == 0
     finally:
         lib.pa_set_unshared_blocks(before)

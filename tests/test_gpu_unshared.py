@@ -1,9 +1,11 @@
-"""The unshared-blocks hint (pa_set_unshared_blocks) changes only the cache
-policy of the decode rows' V loads: every output, lse and pool byte must be
-the same as without it, on the many-work-group decode shape (bf16 and E4M3
-caches), on a mixed step (persistent launch) and through the one-call step;
-and both must match the fp64 oracle at the usual bars (output 2e-2, lse
-1e-3)."""
+"""The decode rows' cache-read policy (pa_set_unshared_blocks: -1 every
+request shared, 0 automatic from the requests' first blocks, 1 every request
+unshared) changes only how V is loaded: every output, lse and pool byte must
+be the same under the three modes, on the many-work-group decode shape (bf16
+and E4M3 caches), on a mixed step whose sharers of a prefix and private
+requests take different policies in one persistent launch, and through the
+one-call step; and the results must match the fp64 oracle at the usual bars
+(output 2e-2, lse 1e-3)."""
 
 import numpy as np
 import pytest
@@ -13,6 +15,15 @@ import oracle
 from workloads import config_step, raw_numpy
 
 pytestmark = pytest.mark.gpu
+
+
+MODES = (-1, 0, 1)
+
+
+def same(a, b):
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.uint8) if x.dtype == torch.bfloat16 else x,
+                           y.view(torch.uint8) if y.dtype == torch.bfloat16 else y)
 
 
 def run_step(step, hint, fused):
@@ -56,30 +67,26 @@ def check_oracle(step, out, lse):
 
 
 @pytest.mark.parametrize("fused", [False, True])
-def test_many_unit_decode_same_with_hint(fused):
+def test_many_unit_decode_same_under_every_mode(fused):
     # 96 decodes x 8 KV heads = 768 work units: the many-work-group shape
     step = config_step(3, scale_down={"batch": 96, "lo": 200, "hi": 1200})
-    a = run_step(step, False, fused)
-    b = run_step(step, True, fused)
-    for x, y in zip(a, b):
-        assert torch.equal(x.view(torch.uint8) if x.dtype == torch.bfloat16 else x,
-                           y.view(torch.uint8) if y.dtype == torch.bfloat16 else y)
-    check_oracle(step, b[0], b[1])
+    runs = [run_step(step, m, fused) for m in MODES]
+    for r in runs[1:]:
+        same(runs[0], r)
+    check_oracle(step, runs[1][0], runs[1][1])
 
 
 @pytest.mark.parametrize("fused", [False, True])
-def test_mixed_step_same_with_hint(fused):
+def test_mixed_step_same_under_every_mode(fused):
     # two prefill chunks and 120 decodes: the persistent mixed launch
     step = config_step(5, scale_down={"chunk": 90, "priors": (70, 300), "decodes": 120,
                                       "lo": 20, "hi": 900, "prefix": 64, "sharers": 30,
                                       "stride": 64})
     assert step.num_seqs > step.num_tokens // 5
-    a = run_step(step, False, fused)
-    b = run_step(step, True, fused)
-    for x, y in zip(a, b):
-        assert torch.equal(x.view(torch.uint8) if x.dtype == torch.bfloat16 else x,
-                           y.view(torch.uint8) if y.dtype == torch.bfloat16 else y)
-    check_oracle(step, b[0], b[1])
+    runs = [run_step(step, m, fused) for m in MODES]
+    for r in runs[1:]:
+        same(runs[0], r)
+    check_oracle(step, runs[1][0], runs[1][1])
 
 
 def run_step_fp8(step, hint):
@@ -103,15 +110,14 @@ def run_step_fp8(step, hint):
     return out[:n].cpu(), lse[:n].cpu(), g["k_pool"].cpu(), g["v_pool"].cpu()
 
 
-def test_many_unit_decode_fp8_same_with_hint():
+def test_many_unit_decode_fp8_same_under_every_mode():
     # E4M3 cache: the V codes streamed non-temporally give the same bytes
     from workloads import fp8_cache
     step = fp8_cache(config_step(3, scale_down={"batch": 96, "lo": 200, "hi": 1200}), 3)
-    a = run_step_fp8(step, False)
-    b = run_step_fp8(step, True)
-    for x, y in zip(a, b):
-        assert torch.equal(x.view(torch.uint8) if x.dtype == torch.bfloat16 else x,
-                           y.view(torch.uint8) if y.dtype == torch.bfloat16 else y)
+    runs = [run_step_fp8(step, m) for m in MODES]
+    for r in runs[1:]:
+        same(runs[0], r)
+    b = runs[1]
     kp, vp = oracle.kv_write_fp8(raw_numpy(step.key), raw_numpy(step.value),
                                  raw_numpy(step.k_pool), raw_numpy(step.v_pool),
                                  step.slot_mapping, step.k_scale.cpu().numpy(),
