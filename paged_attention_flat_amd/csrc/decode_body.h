@@ -99,7 +99,7 @@ constexpr uint32_t kOrderUnshared = 0x80000000u;
 // shared memory.  Ties keep no particular order (the order only schedules
 // work, it never changes a result).
 //
-// With `tables` and `share` (nullable, and num_seqs <= kShareMaxSeqs), each entry also
+// With `tables` and `share` (nullable; num_seqs <= kShareMaxSeqs and 8 NT), each entry also
 // says whether the request shares blocks with another request of the step:
 // it does when its first block is the first block of another request (with
 // any new or cached token).  Blocks are shared through common prefixes (a
@@ -115,21 +115,42 @@ __device__ __forceinline__ void decode_order_block(const int32_t* __restrict__ q
                                                    int32_t* __restrict__ order, OrderSmem& sm,
                                                    ShareSmem* share) {
   constexpr int kPer = kBuckets / NT;  // buckets per thread in the scan
+  constexpr int kIt = 8;               // requests per thread held in registers
   const int tid = threadIdx.x;
-  const bool detect = tables != nullptr && share != nullptr && num_seqs <= kShareMaxSeqs;
+  const bool in_regs = num_seqs <= kIt * NT;
+  const bool detect = tables != nullptr && share != nullptr && in_regs &&
+                      num_seqs <= kShareMaxSeqs;
+  auto bucket = [&](int sl) {
+    return kBuckets - 1 - min(((sl + 15) >> 4) >> shift, kBuckets - 1);
+  };
   for (int i = tid; i < kBuckets; i += NT) sm.hist[i] = 0;
   if (detect) {
     for (int i = tid; i < kShareSlots; i += NT) share->keys[i] = 0u;
     for (int i = tid; i < kShareSlots / 32; i += NT) share->multi[i] = 0u;
   }
+  int ql[kIt], sl[kIt], first[kIt];
+  if (in_regs) {
+    // every request's metadata loaded at once (one round trip), kept for
+    // both passes
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int b = tid + it * NT;
+      ql[it] = 0;
+      sl[it] = 0;
+      first[it] = -1;
+      if (b < num_seqs) {
+        ql[it] = qsl[b + 1] - qsl[b];
+        sl[it] = seq_lens[b];
+        if (detect) first[it] = tables[(size_t)b * table_stride];
+      }
+    }
+  }
   __syncthreads();
-  for (int b = tid; b < num_seqs; b += NT) {
-    const int ql = qsl[b + 1] - qsl[b];
-    const int sl = seq_lens[b];
-    if (detect && sl > 0) {
-      const int first = tables[(size_t)b * table_stride];
-      if (first >= 0) {
-        const uint32_t key = (uint32_t)first + 1u;
+  if (in_regs) {
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      if (detect && sl[it] > 0 && first[it] >= 0) {
+        const uint32_t key = (uint32_t)first[it] + 1u;
         int h = share_slot(key);
         // the set is at most half full, so a free slot or the key is found
         for (int probe = 0; probe < kShareSlots; ++probe) {
@@ -142,10 +163,13 @@ __device__ __forceinline__ void decode_order_block(const int32_t* __restrict__ q
           h = (h + 1) & (kShareSlots - 1);
         }
       }
+      if (ql[it] > 0 && ql[it] <= dq) atomicAdd(&sm.hist[bucket(sl[it])], 1);
     }
-    if (ql <= 0 || ql > dq) continue;
-    const int key = min(((sl + 15) >> 4) >> shift, kBuckets - 1);
-    atomicAdd(&sm.hist[kBuckets - 1 - key], 1);
+  } else {
+    for (int b = tid; b < num_seqs; b += NT) {
+      const int q = qsl[b + 1] - qsl[b];
+      if (q > 0 && q <= dq) atomicAdd(&sm.hist[bucket(seq_lens[b])], 1);
+    }
   }
   __syncthreads();
   // exclusive scan of hist: kPer buckets per thread, then a scan of the partials
@@ -161,25 +185,29 @@ __device__ __forceinline__ void decode_order_block(const int32_t* __restrict__ q
   for (int k = 0; k < kPer; ++k) sm.hist[tid * kPer + k] = base + loc[k];
   if (tid == 0) order[0] = total;
   __syncthreads();
-  for (int b = tid; b < num_seqs; b += NT) {
-    const int ql = qsl[b + 1] - qsl[b];
-    if (ql <= 0 || ql > dq) continue;
-    const int sl = seq_lens[b];
-    uint32_t flag = 0u;
-    if (detect && sl > 0) {
-      // the first block was entered above
-      const int first = tables[(size_t)b * table_stride];
-      if (first >= 0) {
-        const uint32_t key = (uint32_t)first + 1u;
+  if (in_regs) {
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      if (ql[it] <= 0 || ql[it] > dq) continue;  // (also every b past num_seqs)
+      uint32_t flag = 0u;
+      if (detect && sl[it] > 0 && first[it] >= 0) {
+        // the first block was entered above
+        const uint32_t key = (uint32_t)first[it] + 1u;
         int h = share_slot(key);
         for (int probe = 0; probe < kShareSlots && share->keys[h] != key; ++probe)
           h = (h + 1) & (kShareSlots - 1);
         if (!((share->multi[h >> 5] >> (h & 31)) & 1u)) flag = kOrderUnshared;
       }
+      const int pos = atomicAdd(&sm.hist[bucket(sl[it])], 1);
+      order[1 + pos] = (int32_t)((uint32_t)(tid + it * NT) | flag);
     }
-    const int key = min(((sl + 15) >> 4) >> shift, kBuckets - 1);
-    const int pos = atomicAdd(&sm.hist[kBuckets - 1 - key], 1);
-    order[1 + pos] = (int32_t)((uint32_t)b | flag);
+  } else {
+    for (int b = tid; b < num_seqs; b += NT) {
+      const int q = qsl[b + 1] - qsl[b];
+      if (q <= 0 || q > dq) continue;
+      const int pos = atomicAdd(&sm.hist[bucket(seq_lens[b])], 1);
+      order[1 + pos] = b;
+    }
   }
 }
 
