@@ -184,3 +184,67 @@ def test_step_cascade_without_sharers_is_decode_step():
     torch.cuda.synchronize()
     for n in ("k_pool", "v_pool", "out", "lse"):
         assert torch.equal(_bits(a[n]), _bits(g[n])), n
+
+
+def _check_sampled(step, out, lse, kc, vc, pick, what, sub=None):
+    """Rows of the requests `pick` (or the rows `sub` of them) against the
+    oracle on a compact copy of those requests, and their new tokens' cache
+    entries against the inputs (the write is a bit copy)."""
+    from workloads import extract_requests
+    small, rows = extract_requests(step, pick)
+    rows = np.asarray(rows)
+    kp, vp = oracle.kv_write(raw_numpy(small.key), raw_numpy(small.value),
+                             raw_numpy(small.k_pool), raw_numpy(small.v_pool), small.slot_mapping)
+    idx = np.arange(len(rows)) if sub is None else np.asarray(sub)
+    ro, rl = oracle.attention(raw_numpy(small.query), kp, vp, small.query_start_loc,
+                              small.seq_lens, small.block_tables, small.scale,
+                              small.num_kv_heads, small.dtype, rows=idx)
+    ro, rl = ro[idx], rl[idx]
+    o = out.float().cpu().double().numpy()[rows[idx]]
+    assert np.isfinite(o).all(), what
+    assert float(np.abs(o - ro).max()) <= 2e-2, what
+    assert float(np.linalg.norm(o - ro) / np.linalg.norm(ro)) <= 2e-2, what
+    assert float(np.abs(lse.cpu().double().numpy()[rows[idx]] - rl).max()) <= 1e-3, what
+    kin = raw_numpy(step.key).view(np.uint16)
+    vin = raw_numpy(step.value).view(np.uint16)
+    for t in rows:
+        s = int(step.slot_mapping[t])
+        blk, off = s // 16, s % 16
+        kk = kc[blk, :, off, :].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        vv = vc[blk, :, :, off].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(kk, kin[t]), f"{what}: K entry of token {t}"
+        assert np.array_equal(vv, vin[t]), f"{what}: V entry of token {t}"
+
+
+def test_step_cascade_full_mixed_step_sampled():
+    # the full mixed chunked-prefill step (4096 decodes, 1024 sharers of a
+    # 64-block prefix, two 2048-token chunks) through the one call, as timed
+    step = config_step(5)
+    prefix = list(step.info["shared_blocks"])
+    sharers = _sharers_of(step, prefix)
+    assert len(sharers) == step.info["num_sharers"]
+    g = run_one_call(step, sharers, prefix, 0)
+    rng = np.random.default_rng(5)
+    ql = np.diff(step.query_start_loc)
+    non = [b for b in range(step.num_seqs) if b not in set(sharers) and ql[b] == 1]
+    chunks = [b for b in range(step.num_seqs) if ql[b] > 1]
+    pick = list(rng.choice(sharers, 4, replace=False)) + list(rng.choice(non, 2, replace=False))
+    _check_sampled(step, g["out"], g["lse"], g["k_pool"], g["v_pool"], pick,
+                   "one-call cascade, full mixed step (decode rows)")
+    # 24 seeded rows of each prefill chunk (2048 rows over a 4096- and a
+    # 16384-token prior context); every chunk token's cache entries
+    for c in chunks:
+        sub = sorted(int(x) for x in rng.choice(int(ql[c]), 24, replace=False))
+        _check_sampled(step, g["out"], g["lse"], g["k_pool"], g["v_pool"], [c],
+                       f"one-call cascade, full mixed step (chunk {c})", sub=sub)
+
+
+def test_step_cascade_full_shared_prefix_sampled():
+    # 256 decodes sharing a 16384-token prefix, 0..512 private tokens, as timed
+    step = shared_prefix_step(256, 16384, 0, 512, 11, fill="nan")
+    prefix = list(step.info["shared_blocks"])
+    g = run_one_call(step, list(range(step.num_seqs)), prefix, 0)
+    rng = np.random.default_rng(11)
+    pick = [int(x) for x in rng.choice(step.num_seqs, 5, replace=False)]
+    _check_sampled(step, g["out"], g["lse"], g["k_pool"], g["v_pool"], pick,
+                   "one-call cascade, 256 x 16384 shared prefix")
