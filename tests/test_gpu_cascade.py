@@ -133,7 +133,7 @@ def test_cascade_edge_cases(hq, hkv):
 
 
 def test_cascade_full_mixed_step_sampled():
-    step = config_step(5)
+    step = config_step(5, device="cuda")
     prefix = list(step.info["shared_blocks"])
     sharers = sharers_of(step, prefix)
     assert len(sharers) == step.info["num_sharers"]

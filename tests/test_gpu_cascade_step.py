@@ -219,7 +219,8 @@ def _check_sampled(step, out, lse, kc, vc, pick, what, sub=None):
 def test_step_cascade_full_mixed_step_sampled():
     # the full mixed chunked-prefill step (4096 decodes, 1024 sharers of a
     # 64-block prefix, two 2048-token chunks) through the one call, as timed
-    step = config_step(5)
+    # (drawn on the device; the pools are written in place)
+    step = config_step(5, device="cuda")
     prefix = list(step.info["shared_blocks"])
     sharers = _sharers_of(step, prefix)
     assert len(sharers) == step.info["num_sharers"]
