@@ -161,6 +161,74 @@ def test_full_config5_decode_step_pools():
     del k_before
 
 
+def check_sampled_rows(step, out, lse, pick, what, sub=None, seed=0):
+    # rows of the requests `pick` (or `sub` of them) against the oracle on a
+    # compact copy of those requests; the step's pools were written in place,
+    # which the oracle's own write repeats bit for bit
+    from workloads import extract_requests
+    small, rows = extract_requests(step, pick)
+    idx = np.arange(len(rows)) if sub is None else np.asarray(sub)
+    kp, vp = oracle.kv_write(raw_numpy(small.key), raw_numpy(small.value),
+                             raw_numpy(small.k_pool), raw_numpy(small.v_pool), small.slot_mapping)
+    ro, rl = oracle.attention(raw_numpy(small.query), kp, vp, small.query_start_loc,
+                              small.seq_lens, small.block_tables, small.scale,
+                              small.num_kv_heads, small.dtype, rows=idx)
+    o = out.float().cpu().double().numpy()[rows[idx]]
+    assert np.isfinite(o).all(), what
+    assert float(np.abs(o - ro[idx]).max()) <= 2e-2, what
+    assert float(np.linalg.norm(o - ro[idx]) / np.linalg.norm(ro[idx])) <= 2e-2, what
+    assert float(np.abs(lse.cpu().double().numpy()[rows[idx]] - rl[idx]).max()) <= 1e-3, what
+
+
+def test_full_config3_decode_step():
+    # the large-batch decode in the launch the benchmark times: one call (the
+    # new tokens written inside the decode launch), no split, the automatic V
+    # read policy (every request's first block is its own).  Every written
+    # block byte-compared with the oracle's write, nine requests' rows (the
+    # shortest, the longest and three seeded ones) against the oracle.
+    step = config_step(3, device="cuda")
+    sm = step.slot_mapping
+    blocks = np.unique(sm[sm >= 0] // 16)
+    bidx = torch.as_tensor(blocks).to("cuda")
+    k_sel = {n: raw_numpy(getattr(step, n)[bidx]) for n in ("k_pool", "v_pool")}
+    out, lse, g = run_step(step, 0)
+    remap = {int(b): i for i, b in enumerate(blocks)}
+    local = np.array([remap[int(s) // 16] * 16 + int(s) % 16 if s >= 0 else -1 for s in sm])
+    kp, vp = oracle.kv_write(raw_numpy(step.key), raw_numpy(step.value), k_sel["k_pool"],
+                             k_sel["v_pool"], local)
+    for name, ref in (("k_pool", kp), ("v_pool", vp)):
+        got = raw_numpy(g[name][bidx])
+        assert np.array_equal(np.ascontiguousarray(got).view(np.uint8),
+                              np.ascontiguousarray(ref).view(np.uint8)), name
+    order = np.argsort(step.seq_lens)
+    rng = np.random.default_rng(33)
+    pick = sorted(set(order[:3].tolist() + order[-3:].tolist() +
+                      rng.choice(step.num_seqs, 3, replace=False).tolist()))
+    check_sampled_rows(step, out, lse, pick, "full config3 decode step")
+
+
+def test_full_config5_decode_step_rows():
+    # the mixed step through the one call the benchmark times (persistent
+    # launch, automatic V read policy: sharers of the prefix cached, the
+    # others streamed): sampled decode rows of sharers and non-sharers and
+    # seeded rows of both chunks against the oracle
+    step = config_step(5, device="cuda")
+    out, lse, g = run_step(step, 0)
+    ql = np.diff(step.query_start_loc)
+    shared = set(step.info["shared_blocks"])
+    dec = np.nonzero(ql == 1)[0]
+    sharers = [int(b) for b in dec if int(step.block_tables[b, 0]) in shared]
+    non = [int(b) for b in dec if int(step.block_tables[b, 0]) not in shared]
+    rng = np.random.default_rng(55)
+    pick = sorted(rng.choice(sharers, 4, replace=False).tolist() +
+                  rng.choice(non, 4, replace=False).tolist())
+    check_sampled_rows(step, out, lse, pick, "full config5 decode step (decode rows)")
+    for c in np.nonzero(ql > 1)[0]:
+        sub = sorted(int(x) for x in rng.choice(int(ql[c]), 24, replace=False))
+        check_sampled_rows(step, out, lse, [int(c)], f"full config5 decode step (chunk {c})",
+                           sub=sub)
+
+
 def check_pools(step, g, before, what):
     kp, vp = oracle.kv_write(raw_numpy(step.key), raw_numpy(step.value), before[0], before[1],
                              step.slot_mapping)
