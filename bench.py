@@ -184,8 +184,9 @@ class StepRunner:
         from paged_attention_flat_amd import _lib
         self.pa, self.lib, self.ctypes, self.torch = pa, _lib.LIB, ctypes, torch
         self.step = step
-        # the caller's statement that no block is read by two requests
-        # (pa_set_unshared_blocks), in force for this runner's launches only
+        # pa_set_unshared_blocks(1) (every request taken as reading blocks
+        # of its own, without the first-block test), in force for this
+        # runner's launches only
         self.unshared = unshared
         g = {}
         for name in ("query", "key", "value"):
@@ -737,7 +738,7 @@ def bench_fp8(args, log):
                                      "traffic": measured_traffic(PROFILE_NAMES[cfg] + "_fp8",
                                                                  "prefill_mfma")}
         if cfg == 3:
-            # with the caller's statement that no block is shared
+            # under pa_set_unshared_blocks(1) (no first-block test)
             wname = PROFILE_NAMES[cfg] + "_fp8_unshared"
             _, (ru,), _, nu, wu = workload_runners(wname, dev, args,
                                                    pools=(runners[0].g["kc"], runners[0].g["vc"]))
@@ -745,7 +746,7 @@ def bench_fp8(args, log):
             ukt = kernel_times([ru], min(nu, 20), log)
             kb, _ = decode_kernel_bytes(step)
             ugbs = kb / (ukt["decode"]["avg_us"] * 1e-6) / 1e9 if "decode" in ukt else None
-            rec["unshared_blocks_hint"] = {
+            rec["all_unshared_mode"] = {
                 "ms_per_step": ums, "launch": umode,
                 "kernels_us": attributed_us(ukt, ums),
                 "kernels_us_eager_traced": {k: round(v["avg_us"], 2) for k, v in ukt.items()},
@@ -901,15 +902,16 @@ def bench_extra(cfg, args, log):
                                "traffic": measured_traffic(PROFILE_NAMES[cfg],
                                                            "mixed_prefill_decode")}
     if cfg == 3:
-        # the same step with the caller's statement that no block is shared
-        # (pa_set_unshared_blocks): V streamed non-temporally
+        # the same step under pa_set_unshared_blocks(1): every request's V
+        # streamed non-temporally without the first-block test (the default,
+        # automatic policy marks all 256 requests unshared here as well)
         _, (ru,), _, nu, wu = workload_runners(PROFILE_NAMES[cfg] + "_unshared", dev, args,
                                                pools=(r.g["kc"], r.g["vc"]))
         ums, umode = time_steps([ru], nu, wu, not args.eager, log)
         ukt = kernel_times([ru], min(nu, 20), log)
         kb, _ = decode_kernel_bytes(step)
         ugbs = kb / (ukt["decode"]["avg_us"] * 1e-6) / 1e9 if "decode" in ukt else None
-        out["unshared_blocks_hint"] = {
+        out["all_unshared_mode"] = {
             "ms_per_step": ums, "launch": umode,
             "step_GBps": wm["bytes"] / (ums * 1e-3) / 1e9,
             "kernels_us": attributed_us(ukt, ums),
