@@ -1131,7 +1131,7 @@ def cpu_baseline(args, log):
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}): this build has no "
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): the library has no "
               "multi-GPU path (attention shards by KV head or by request with no exchange "
               "inside the step)", file=sys.stderr)
         sys.exit(2)
