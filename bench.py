@@ -964,7 +964,8 @@ def _cpu_model():
 
 def _cpu_workers():
     """Worker processes for the oracle: the host cores this process may run
-    on, at most 16 (a GPU machine's host share per GPU)."""
+    on, at most 16 (the host cores a machine with one MI355X per 16 cores
+    gives each GPU)."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
@@ -1029,7 +1030,8 @@ def _run_oracle_pool(d, workers, seconds):
 
 
 def cpu_baseline(args, log):
-    """The fp64 oracle (as it stands) on the GPU machine's host cores: N worker
+    """The fp64 oracle (as it stands) on the host cores of the machine the GPU
+    sits in: N worker
     processes (one BLAS thread each, N = the cores this process may use, at
     most 16) repeat whole steps of the headline workload for about
     args.cpu_seconds, and bounded samples of the large-batch decode (16
