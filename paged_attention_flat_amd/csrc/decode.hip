@@ -79,7 +79,7 @@ constexpr int decode_min_waves(int nw, int pipe, bool f8) {
 template <int D, int G, int NW, int PIPE, bool F8, int NTP>
 __global__ __launch_bounds__(64 * NW, decode_min_waves(NW, PIPE, F8)) void decode_kernel(
     DecodeParams p) {
-  __shared__ DecodeSmem<D, NW> sm;
+  __shared__ DecodeSmem<D, NW, PIPE> sm;
   decode_unit<D, G, NW, PIPE, F8, NTP>(p, blockIdx.x, blockIdx.y, sm, threadIdx.x);
 }
 

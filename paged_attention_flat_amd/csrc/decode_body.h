@@ -254,11 +254,12 @@ inline DecodeParams make_decode_params(const AttnArgs& a) {
 }
 
 // Shared memory of one decode work-group: the lane-local exchange buffer of
-// the waves' tree merge (also the staging of the split merge) and the flag
-// that elects the merging work-group.
-template <int D, int NW>
+// the waves' merge (a slot per wave in the two-fragment-set shape, per pair
+// of waves in the tree merge of the many-work-group shape; also the staging
+// of the split merge) and the flag that elects the merging work-group.
+template <int D, int NW, int PIPE>
 struct DecodeSmem {
-  float x[NW / 2][4 * (D / 16) + 2][64];
+  float x[PIPE == 2 ? NW : NW / 2][4 * (D / 16) + 2][64];
   int last;
 };
 
@@ -280,7 +281,7 @@ constexpr int kNtAuto = 4;  // V loads non-temporal for requests the order marks
 // work-group uniform.
 template <int D, int G, int NW, int PIPE, bool F8, int NTP>
 __device__ __forceinline__ void decode_unit_body(const DecodeParams& p, int bx, int by, int b,
-                                                 int live, DecodeSmem<D, NW>& sm,
+                                                 int live, DecodeSmem<D, NW, PIPE>& sm,
                                                  const int tidx) {
   typedef typename Frag8<F8>::elem CT;
   typedef typename Frag8<F8>::raw RT;
@@ -290,7 +291,8 @@ __device__ __forceinline__ void decode_unit_body(const DecodeParams& p, int bx, 
   constexpr int NREG = 4 * DB + 2; // per-lane state: acc, m, l
 
   // lane-local exchange buffer for the tree merge of the waves' states
-  float (&s_x)[NW / 2][NREG][64] = sm.x;
+  constexpr int kSlots = PIPE == 2 ? NW : NW / 2;
+  float (&s_x)[kSlots][NREG][64] = sm.x;
 
   const int kvh = bx % p.hkv;
   const int split = by;
@@ -649,12 +651,26 @@ __device__ __forceinline__ void decode_unit_body(const DecodeParams& p, int bx, 
   // per-column denominator: sum the four key groups of the wave
   l = sum_xor32(sum_xor16(l));
 
-  // tree merge of the waves; every wave holds the same (column, dim) layout,
-  // so the merge is lane-local
-#pragma unroll
-  for (int half = NW / 2; half >= 1; half >>= 1) {
-    if (wave >= half && wave < 2 * half) {
-      float* x = &s_x[wave - half][0][lane];
+  // Merge of the waves' states.  Each wave ends up with the merged result
+  // for its share of the head dimension (dim blocks db0 .. db1 - 1, in
+  // mac[0 .. db1 - db0)) and the merged (m, l) of its columns.
+  //  - two-fragment-set shape: one exchange.  Every wave writes its (acc, m,
+  //    l) to LDS, then wave w combines the NW states for its share.  Every
+  //    wave holds the same (column, dim) layout, so the merge is lane-local.
+  //    Against a tree merge (one pair of waves per level: two LDS rounds and
+  //    four barriers at four waves) it takes 1.5 % off the long single decode
+  //    and the mixed step;
+  //  - many-work-group shape: the tree merge, wave 0 keeping every dim (twice
+  //    the LDS per work-group for the one exchange cost the short units of the
+  //    shared-prefix decode 10 %).
+  constexpr int DPW = PIPE == 2 ? (DB + NW - 1) / NW : DB;  // dim blocks per wave
+  int db0 = 0, db1 = 0;
+  f32x4 mac[DPW];
+  if constexpr (PIPE == 2) {
+    db0 = min(DB, wave * DPW);
+    db1 = min(DB, db0 + DPW);
+    {
+      float* x = &s_x[wave][0][lane];
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -663,36 +679,82 @@ __device__ __forceinline__ void decode_unit_body(const DecodeParams& p, int bx, 
       x[(4 * DB + 1) * 64] = l;
     }
     __syncthreads();
-    if (wave < half) {
-      const float* x = &s_x[wave][0][lane];
-      const float mo = x[(4 * DB) * 64], lo = x[(4 * DB + 1) * 64];
-      const float M = fmaxf(m, mo);
-      const float wa = (m == -INFINITY) ? 0.f : fast_exp2(m - M);
-      const float wb = (mo == -INFINITY) ? 0.f : fast_exp2(mo - M);
+    float wgt[NW];
+    {
+      float M = -INFINITY;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int w2 = 0; w2 < NW; ++w2) M = fmaxf(M, s_x[w2][4 * DB][lane]);
+      float L = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[db][i] = acc[db][i] * wa + x[(4 * db + i) * 64] * wb;
-      l = l * wa + lo * wb;
+      for (int w2 = 0; w2 < NW; ++w2) {
+        const float mo = s_x[w2][4 * DB][lane];
+        wgt[w2] = (mo == -INFINITY) ? 0.f : fast_exp2(mo - M);
+        L += wgt[w2] * s_x[w2][4 * DB + 1][lane];
+      }
       m = M;
+      l = L;
     }
-    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < DPW; ++k) {
+      mac[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int db = db0 + k;
+      if (db < db1) {
+#pragma unroll
+        for (int w2 = 0; w2 < NW; ++w2)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mac[k][i] += wgt[w2] * s_x[w2][4 * db + i][lane];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int half = NW / 2; half >= 1; half >>= 1) {
+      if (wave >= half && wave < 2 * half) {
+        float* x = &s_x[wave - half][0][lane];
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[(4 * db + i) * 64] = acc[db][i];
+        x[(4 * DB) * 64] = m;
+        x[(4 * DB + 1) * 64] = l;
+      }
+      __syncthreads();
+      if (wave < half) {
+        const float* x = &s_x[wave][0][lane];
+        const float mo = x[(4 * DB) * 64], lo = x[(4 * DB + 1) * 64];
+        const float M = fmaxf(m, mo);
+        const float wa = (m == -INFINITY) ? 0.f : fast_exp2(m - M);
+        const float wb = (mo == -INFINITY) ? 0.f : fast_exp2(mo - M);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[db][i] = acc[db][i] * wa + x[(4 * db + i) * 64] * wb;
+        l = l * wa + lo * wb;
+        m = M;
+      }
+      __syncthreads();
+    }
+    if (wave == 0) db1 = DB;
+#pragma unroll
+    for (int k = 0; k < DPW; ++k) mac[k] = acc[k];
   }
-  // wave 0, lane (col, kg) holds dims 16*db + 4*kg .. +4 of column col
   const int t = q0 + qi;
   const int h = kvh * G + g;
   // a sharer always merges (its splits and the prefix partial)
   const bool merged = p.splits > 1 || pv0 >= 0;
-  if (wave == 0 && col_valid) {
+  if (col_valid && db0 < db1) {
     if (!merged) {
       const float inv = v_scale / l;
       uint16_t* dst = p.out + ((size_t)t * p.hq + h) * D + 4 * kg;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-        *reinterpret_cast<uint2*>(dst + 16 * db) =
-            make_uint2(pack_bf16x2(acc[db][0] * inv, acc[db][1] * inv),
-                       pack_bf16x2(acc[db][2] * inv, acc[db][3] * inv));
-      if (p.lse != nullptr && kg == 0) p.lse[(size_t)t * p.hq + h] = (m + fast_log2(l)) * kLn2;
+      for (int k = 0; k < DPW; ++k) {
+        const int db = db0 + k;
+        if (db < db1)
+          *reinterpret_cast<uint2*>(dst + 16 * db) =
+              make_uint2(pack_bf16x2(mac[k][0] * inv, mac[k][1] * inv),
+                         pack_bf16x2(mac[k][2] * inv, mac[k][3] * inv));
+      }
+      if (p.lse != nullptr && wave == 0 && kg == 0)
+        p.lse[(size_t)t * p.hq + h] = (m + fast_log2(l)) * kLn2;
     } else if (p.splits == 1) {
       // a sharer without a split: merge the prefix partials (written by the
       // previous launch on this stream) with this work-group's own result
@@ -703,31 +765,37 @@ __device__ __forceinline__ void decode_unit_body(const DecodeParams& p, int bx, 
       for (int ks = 0; ks < p.pre_splits; ++ks) M = fmaxf(M, p.pre_lse[ks * kstride + prer]);
       const float wb = (lb == -INFINITY) ? 0.f : fast_exp2((lb - M) * kLog2e);
       float den = wb;
-      float4 o[DB];
+      float4 o[DPW];
+      const float cb = (l == 0.f) ? 0.f : wb * v_scale / l;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const float cb = (l == 0.f) ? 0.f : wb * v_scale / l;
-        o[db] = make_float4(cb * acc[db][0], cb * acc[db][1], cb * acc[db][2], cb * acc[db][3]);
-      }
+      for (int k = 0; k < DPW; ++k)
+        o[k] = make_float4(cb * mac[k][0], cb * mac[k][1], cb * mac[k][2], cb * mac[k][3]);
       for (int ks = 0; ks < p.pre_splits; ++ks) {
         const float la = p.pre_lse[ks * kstride + prer];
         const float wa = (la == -INFINITY) ? 0.f : fast_exp2((la - M) * kLog2e);
         den += wa;
         const float* src = p.pre_out + (ks * kstride + prer) * D + 4 * kg;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const float4 oa = *reinterpret_cast<const float4*>(src + 16 * db);
-          o[db].x += wa * oa.x; o[db].y += wa * oa.y; o[db].z += wa * oa.z; o[db].w += wa * oa.w;
+        for (int k = 0; k < DPW; ++k) {
+          const int db = db0 + k;
+          if (db < db1) {
+            const float4 oa = *reinterpret_cast<const float4*>(src + 16 * db);
+            o[k].x += wa * oa.x; o[k].y += wa * oa.y; o[k].z += wa * oa.z; o[k].w += wa * oa.w;
+          }
         }
       }
       const float inv = 1.f / den;
       uint16_t* dst = p.out + ((size_t)t * p.hq + h) * D + 4 * kg;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-        *reinterpret_cast<uint2*>(dst + 16 * db) =
-            make_uint2(pack_bf16x2(o[db].x * inv, o[db].y * inv),
-                       pack_bf16x2(o[db].z * inv, o[db].w * inv));
-      if (p.lse != nullptr && kg == 0) p.lse[(size_t)t * p.hq + h] = M + fast_log2(den) * kLn2;
+      for (int k = 0; k < DPW; ++k) {
+        const int db = db0 + k;
+        if (db < db1)
+          *reinterpret_cast<uint2*>(dst + 16 * db) =
+              make_uint2(pack_bf16x2(o[k].x * inv, o[k].y * inv),
+                         pack_bf16x2(o[k].z * inv, o[k].w * inv));
+      }
+      if (p.lse != nullptr && wave == 0 && kg == 0)
+        p.lse[(size_t)t * p.hq + h] = M + fast_log2(den) * kLn2;
     } else {
       const bool empty = (l == 0.f);
       const float inv = empty ? 0.f : v_scale / l;
@@ -736,12 +804,16 @@ __device__ __forceinline__ void decode_unit_body(const DecodeParams& p, int bx, 
       // merging work-group (possibly on another XCD) reads them from memory
       // without an L2 write-back here
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int k = 0; k < DPW; ++k) {
+        const int db = db0 + k;
+        if (db < db1) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          __hip_atomic_store(dst + 16 * db + i, acc[db][i] * inv, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-      if (kg == 0)
+          for (int i = 0; i < 4; ++i)
+            __hip_atomic_store(dst + 16 * db + i, mac[k][i] * inv, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      if (wave == 0 && kg == 0)
         __hip_atomic_store(p.part_lse + ((size_t)split * p.nt + t) * p.hq + h,
                            empty ? -INFINITY : (m + fast_log2(l)) * kLn2, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
@@ -754,20 +826,21 @@ __device__ __forceinline__ void decode_unit_body(const DecodeParams& p, int bx, 
   // "Inside the engine: kernels, CUDA graphs and the life of a request",
   // section "Prefill has a full grid; decode at batch 1 has almost none";
   // here that pass is done by whichever work-group of this (request, KV head)
-  // completes last, so the step needs no second launch).  Only wave 0 stored partials, all of them device-scope
-  // atomic stores: once the wave's store counter has drained they are visible
-  // device-wide, and its lane 0 then counts the arrival.  (A release fence
-  // would also write back this XCD's whole L2, which costs microseconds per
-  // work-group; nothing else here needs publishing.)  The last arrival
-  // acquires, which drops stale L2 lines, before reading the other splits'
-  // partials.  The counter is returned to zero for the next call.
+  // completes last, so the step needs no second launch).  Every wave stored
+  // its share of the partial with device-scope atomic stores: once each
+  // wave's store counter has drained they are visible device-wide, and after
+  // a barrier thread 0 counts the arrival.  (A release fence would also write
+  // back this XCD's whole L2, which costs microseconds per work-group;
+  // nothing else here needs publishing.)  The last arrival acquires, which
+  // drops stale L2 lines, before reading the other splits' partials.  The
+  // counter is returned to zero for the next call.
   int& s_last = sm.last;
   int* sem = p.sem + (size_t)b * p.hkv + kvh;
-  if (tidx == 0) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tidx == 0)
     s_last = __hip_atomic_fetch_add(sem, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
              p.splits - 1;
-  }
   __syncthreads();
   if (!s_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
@@ -884,7 +957,7 @@ __device__ __forceinline__ void decode_unit_body(const DecodeParams& p, int bx, 
 // bounds for every rank (rank < num_seqs).
 template <int D, int G, int NW, int PIPE, bool F8, int NTP>
 __device__ __forceinline__ void decode_unit(const DecodeParams& p, int bx, int by,
-                                            DecodeSmem<D, NW>& sm, const int tidx) {
+                                            DecodeSmem<D, NW, PIPE>& sm, const int tidx) {
   const int rank = bx / p.hkv;
   int b = rank, live = 1;
   bool unshared = false;

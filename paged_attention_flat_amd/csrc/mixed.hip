@@ -39,7 +39,7 @@ static_assert(PA_PREFILL_WAVES == kMixedWaves && PA_PREFILL_ROW_GROUPS == 1,
 template <int D>
 union MixedSmem {
   PrefillSmem<D, PA_PREFILL_KEYS> p;
-  DecodeSmem<D, kMixedWaves> d;
+  DecodeSmem<D, kMixedWaves, 2> d;
 };
 
 template <int D, int G, bool F8, int NTP>
