@@ -28,10 +28,11 @@
 // of the two S^T products are assigned to keys so that each lane's P values
 // are 8 consecutive keys of one block, matching one 16-byte V load.  Block
 // ids come 64 at a time from one coalesced table load and are picked with
-// readlane.  Sixteen waves per CU (four 4-wave work-groups at 118 VGPRs, or
-// two-fragment-set waves when there are few units) keep enough loads in
-// flight to cover HBM latency.  Row maxima use two cross-lane
-// exchanges; exponentials are base 2 on log2(e)-prescaled scores.
+// readlane.  With many units, sixteen waves per CU (four 4-wave work-groups
+// at 118 VGPRs) keep enough loads in flight to cover HBM latency; with few,
+// eight waves per CU each keep the next pair's loads in flight while they
+// compute the current one (two fragment sets).  Row maxima use two
+// cross-lane exchanges; exponentials are base 2 on log2(e)-prescaled scores.
 //
 // Work order: work-group index = KV head fastest, then request rank.  For
 // batches with more work than compute units the ranks come from a device-side
@@ -60,10 +61,12 @@ __global__ __launch_bounds__(1024) void decode_order_kernel(const int32_t* __res
 // NTP: the loads that take the non-temporal policy.  The long-context shape
 // streams K and V that way with a bf16 cache (measured 9-10 % faster from
 // 16K keys on, equal below).  The many-work-group shape streams V only, and
-// only when the call's blocks are unshared: 8 % (bf16) and 9 % (E4M3) faster
-// on 256 unshared requests, 25 % slower where all of them re-read one long
-// prefix, which cached loads serve from L2/MALL; non-temporal K loads (64
-// bytes of 16 rows each) were slower there in either case.
+// only for requests whose blocks are their own (kNtV for every request when
+// the call says so, kNtAuto per request as the decode order marks it): 8 %
+// (bf16) and 9 % (E4M3) faster on 256 unshared requests, 25 % slower where
+// all of them re-read one long prefix, which cached loads serve from
+// L2/MALL; non-temporal K loads (64 bytes of 16 rows each) were slower there
+// in either case.
 //
 // Waves per SIMD the register allocation must allow: two for the two-
 // fragment-set shape at four waves; four for the bf16 one-pair shape at four
